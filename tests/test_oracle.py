@@ -1,0 +1,337 @@
+"""Pins of the fp64 CPU oracle against what mathematics fixes.
+
+Every check here is independent of the oracle's own code: closed forms,
+library routines (scipy, scikit-learn), invariances, a hand-derived worked
+example and a separately written brute-force N x K path. Each is chosen so a
+plausible slip in the oracle (a dropped log-det or 2 pi term, a wrong sign, a
+transposed operand, the variance about the old instead of the new mean, a
+mishandled empty component) fails at least one of them.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
+from scipy.special import logsumexp
+from scipy.stats import norm
+
+from gmm_em_amd import datagen as dg
+from oracle import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rand_params(rng, k, d, spread=3.0):
+    w = rng.dirichlet(np.ones(k))
+    mu = rng.normal(0, spread, size=(k, d))
+    var = rng.uniform(0.3, 3.0, size=(k, d))
+    return w, mu, var
+
+
+def test_logdensity_matches_scipy_norm_logpdf():
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 2, size=(40, 7)).astype(np.float32)
+    w, mu, var = _rand_params(rng, 5, 7)
+    got = oracle.logdensity(x, w, mu, var)
+    want = np.log(w)[None, :] + norm.logpdf(
+        x.astype(np.float64)[:, None, :], loc=mu[None], scale=np.sqrt(var)[None]).sum(axis=2)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_logdensity_one_dim_one_component_by_hand():
+    # D=1, K=1, x=3, mu=1, v=4: log N = -1/2 log(2 pi 4) - (3-1)^2/(2*4)
+    x = np.array([[3.0]], dtype=np.float32)
+    got = oracle.logdensity(x, [1.0], [[1.0]], [[4.0]])[0, 0]
+    assert got == pytest.approx(-0.5 * np.log(8 * np.pi) - 0.5, rel=1e-15)
+
+
+def test_per_row_loglik_matches_scipy_logsumexp():
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 3, size=(300, 6)).astype(np.float32)
+    w, mu, var = _rand_params(rng, 9, 6)
+    total, rows = oracle.loglik(x, w, mu, var, per_row=True)
+    ell = oracle.logdensity(x, w, mu, var)
+    np.testing.assert_allclose(rows, logsumexp(ell, axis=1), rtol=1e-13)
+    assert total == pytest.approx(rows.sum(), rel=1e-13)
+
+
+def test_golden_symmetric_pair():
+    import mpmath as mp
+
+    mp.mp.dps = 30
+    g = json.load(open(os.path.join(HERE, "golden", "symmetric_pair.json")))
+    vals = {k: float(v) for k, v in g["expected_values"].items()}
+    # the stored numbers are the stated closed forms
+    assert vals["mean_plus"] == float(mp.tanh(1))
+    assert vals["variance"] == float(1 - mp.tanh(1) ** 2)
+    assert vals["loglik"] == float(2 * mp.log((1 + mp.e ** -2) / 2) - mp.log(2 * mp.pi))
+    x = np.array(g["x"], dtype=np.float32)
+    w2, mu2, v2, L, nk = oracle.em_step(x, g["weights"], g["means"], g["variances"], 0.0)
+    np.testing.assert_allclose(w2, [0.5, 0.5], rtol=1e-15)
+    np.testing.assert_allclose(mu2[:, 0], [-vals["mean_plus"], vals["mean_plus"]], rtol=1e-15)
+    np.testing.assert_allclose(v2[:, 0], [vals["variance"]] * 2, rtol=1e-14)
+    assert L == pytest.approx(vals["loglik"], rel=1e-15)
+    _, resp, _ = oracle.topm(x, g["weights"], g["means"], g["variances"], 1)
+    assert resp[1, 0] == pytest.approx(vals["responsibility_own"], rel=1e-15)
+
+
+def test_single_component_closed_form_and_fixed_point():
+    rng = np.random.default_rng(13)
+    x = (rng.normal(2.0, 1.5, size=(5000, 4)) * [1, 3, 0.5, 2]).astype(np.float32)
+    X = x.astype(np.float64)
+    mean, popvar = X.mean(axis=0), X.var(axis=0)  # numpy's own mean and population variance
+    w1, mu1, v1, L0, nk = oracle.em_step(x, [1.0], [[9.0, -4.0, 0.0, 1.0]], [[2.0, 0.1, 7.0, 1.0]])
+    assert w1[0] == 1.0 and nk[0] == pytest.approx(5000.0, rel=1e-14)
+    np.testing.assert_allclose(mu1[0], mean, rtol=1e-12)
+    np.testing.assert_allclose(v1[0], popvar, rtol=1e-11)
+    # second step: fixed point, and L is the Gaussian max log-likelihood
+    w2, mu2, v2, L1, _ = oracle.em_step(x, w1, mu1, v1)
+    np.testing.assert_allclose(mu2, mu1, rtol=1e-12)
+    np.testing.assert_allclose(v2, v1, rtol=1e-11)
+    want = -0.5 * 5000 * np.sum(np.log(2 * np.pi * popvar) + 1)
+    assert L1 == pytest.approx(want, rel=1e-12)
+
+
+def test_identical_components_reduce_to_single_component():
+    rng = np.random.default_rng(14)
+    x = rng.normal(0, 2, size=(3000, 5)).astype(np.float32)
+    X = x.astype(np.float64)
+    k = 4
+    w = np.array([0.1, 0.2, 0.3, 0.4])
+    mu = np.tile(rng.normal(size=5), (k, 1))
+    var = np.tile(rng.uniform(0.5, 2, size=5), (k, 1))
+    w1, mu1, v1, L, _ = oracle.em_step(x, w, mu, var)
+    np.testing.assert_allclose(w1, w, rtol=1e-12)
+    for j in range(k):
+        np.testing.assert_allclose(mu1[j], X.mean(axis=0), rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(v1[j], X.var(axis=0), rtol=1e-11)
+    L1 = oracle.loglik(x, [1.0], mu[:1], var[:1])
+    assert L == pytest.approx(L1, rel=1e-13)
+
+
+def test_responsibilities_sum_to_one_and_weights_to_one():
+    rng = np.random.default_rng(15)
+    x = rng.normal(0, 3, size=(400, 3)).astype(np.float32)
+    w, mu, var = _rand_params(rng, 6, 3)
+    *_, r = oracle.brute_em_step(x, w, mu, var)
+    np.testing.assert_allclose(r.sum(axis=1), 1.0, atol=1e-14)
+    w2, *_ = oracle.em_step(x, w, mu, var)
+    assert abs(w2.sum() - 1.0) < 1e-14
+
+
+def test_brute_force_matches_streaming():
+    x, pl, _ = dg.custom(6000, 6, 5, seed=16)  # > one 4096-row block
+    rng = np.random.default_rng(16)
+    w, mu, var = _rand_params(rng, 5, 6)
+    a = oracle.em_step(x, w, mu, var, 1e-6)
+    b = oracle.brute_em_step(x, w, mu, var, 1e-6)
+    for i in range(3):
+        np.testing.assert_allclose(a[i], b[i], rtol=1e-12, atol=1e-14)
+    assert a[3] == pytest.approx(b[3], rel=1e-13)
+    np.testing.assert_allclose(a[4], b[4], rtol=1e-12)
+
+
+@settings(max_examples=25, deadline=None)
+@given(n=st.integers(1, 60), d=st.integers(1, 5), k=st.integers(1, 6), seed=st.integers(0, 10_000))
+def test_brute_force_matches_streaming_random_shapes(n, d, k, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 2, size=(n, d)).astype(np.float32)
+    w, mu, var = _rand_params(rng, k, d, spread=2.0)
+    a = oracle.em_step(x, w, mu, var, 1e-6)
+    b = oracle.brute_em_step(x, w, mu, var, 1e-6)
+    live = b[4] > 1e-200
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-11, atol=1e-300)
+    np.testing.assert_allclose(a[1][live], b[1][live], rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(a[2][live], b[2][live], rtol=1e-8, atol=1e-11)
+    assert a[3] == pytest.approx(b[3], rel=1e-12, abs=1e-12)
+
+
+def test_loglik_never_decreases():
+    W = dg.WORKLOADS["tiny"]
+    x = dg.rows(W)
+    w0, m0, v0 = dg.init_params(W, x)
+    *_, hist = oracle.fit(x, w0, m0, v0, W.var_floor, W.iters)
+    assert len(hist) == W.iters
+    assert np.all(np.diff(hist) >= -1e-12 * np.abs(hist[1:]))
+
+
+def test_planted_recovery_well_separated():
+    # 6 planted components 40 sd apart in D=8: posteriors are one-hot in fp64,
+    # so one step from one seeded member per component gives exactly the
+    # label-grouped sample statistics, and these estimate the planted values.
+    k, d, n = 6, 8, 30000
+    rng = np.random.default_rng(17)
+    means = rng.normal(0, 1, size=(k, d))
+    means = 40.0 * np.arange(k)[:, None] * np.ones(d)[None, :] + means
+    sds = rng.uniform(0.5, 1.0, size=(k, d))
+    wts = np.array([0.05, 0.1, 0.15, 0.2, 0.2, 0.3])
+    z = rng.choice(k, size=n, p=wts)
+    x = (means[z] + sds[z] * rng.standard_normal((n, d))).astype(np.float32)
+    seeds = np.array([np.nonzero(z == j)[0][0] for j in range(k)])
+    w1, mu1, v1, L, _ = oracle.em_step(x, np.full(k, 1 / k), x[seeds].astype(np.float64),
+                                       np.ones((k, d)))
+    X = x.astype(np.float64)
+    for j in range(k):
+        g = X[z == j]
+        assert w1[j] == pytest.approx(len(g) / n, rel=1e-12)
+        np.testing.assert_allclose(mu1[j], g.mean(axis=0), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(v1[j], g.var(axis=0), rtol=1e-10)
+        cnt = len(g)
+        assert np.all(np.abs(mu1[j] - means[j]) < 6 * sds[j] / np.sqrt(cnt))
+        assert np.all(np.abs(v1[j] / sds[j] ** 2 - 1) < 6 * np.sqrt(2 / cnt))
+        assert abs(w1[j] - wts[j]) < 6 * np.sqrt(wts[j] * (1 - wts[j]) / n)
+
+
+def test_component_permutation_equivariance():
+    rng = np.random.default_rng(18)
+    x = rng.normal(0, 3, size=(2000, 4)).astype(np.float32)
+    w, mu, var = _rand_params(rng, 7, 4)
+    perm = rng.permutation(7)
+    a = oracle.em_step(x, w, mu, var)
+    b = oracle.em_step(x, w[perm], mu[perm], var[perm])
+    np.testing.assert_allclose(b[0], a[0][perm], rtol=1e-13)
+    np.testing.assert_allclose(b[1], a[1][perm], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(b[2], a[2][perm], rtol=1e-12)
+    assert b[3] == pytest.approx(a[3], rel=1e-14)
+
+
+def test_row_permutation_invariance():
+    rng = np.random.default_rng(19)
+    x = rng.normal(0, 3, size=(9000, 4)).astype(np.float32)
+    w, mu, var = _rand_params(rng, 5, 4)
+    a = oracle.em_step(x, w, mu, var)
+    b = oracle.em_step(x[rng.permutation(len(x))], w, mu, var)
+    for i in range(3):
+        np.testing.assert_allclose(b[i], a[i], rtol=1e-12, atol=1e-14)
+    assert b[3] == pytest.approx(a[3], rel=1e-13)
+
+
+def test_affine_equivariance():
+    # x -> a x + b per dim, with a a power of two and integer data so the
+    # transformed fp32 rows are exact
+    rng = np.random.default_rng(20)
+    x = np.rint(rng.normal(0, 20, size=(4000, 3))).astype(np.float32)
+    a = np.array([2.0, 0.5, 4.0])
+    b = np.array([3.0, -7.0, 1.0])
+    xt = (x * a + b).astype(np.float32)
+    assert np.array_equal(xt.astype(np.float64), x.astype(np.float64) * a + b)
+    w, mu, var = _rand_params(rng, 4, 3, spread=20.0)
+    var = var * 50
+    f = 1e-6
+    r0 = oracle.em_step(x, w, mu, var, f)
+    r1 = oracle.em_step(xt, w, mu * a + b, var * a * a, f)  # floor inactive here
+    np.testing.assert_allclose(r1[0], r0[0], rtol=1e-12)
+    np.testing.assert_allclose(r1[1], r0[1] * a + b, rtol=1e-12, atol=1e-10)
+    np.testing.assert_allclose(r1[2], r0[2] * a * a, rtol=1e-11)
+    assert r1[3] == pytest.approx(r0[3] - len(x) * np.log(np.abs(a)).sum(), rel=1e-13)
+
+
+def test_zero_weight_component_is_frozen():
+    rng = np.random.default_rng(21)
+    x = rng.normal(0, 1, size=(500, 3)).astype(np.float32)
+    w = np.array([0.5, 0.0, 0.5])
+    mu = rng.normal(size=(3, 3))
+    var = rng.uniform(0.5, 2, size=(3, 3))
+    w1, mu1, v1, L, nk = oracle.em_step(x, w, mu, var)
+    assert nk[1] == 0.0 and w1[1] == 0.0
+    assert np.array_equal(mu1[1], mu[1]) and np.array_equal(v1[1], var[1])
+    assert abs(w1.sum() - 1) < 1e-14
+
+
+def test_far_component_gets_exact_zero_mass():
+    # a component 1e4 sd away underflows to r == 0.0 exactly for every row
+    rng = np.random.default_rng(22)
+    x = rng.normal(0, 1, size=(800, 2)).astype(np.float32)
+    mu = np.array([[0.0, 0.0], [1e4, 1e4]])
+    w1, mu1, v1, L, nk = oracle.em_step(x, [0.5, 0.5], mu, np.ones((2, 2)))
+    assert nk[1] == 0.0 and w1[1] == 0.0 and w1[0] == 1.0
+    assert np.array_equal(mu1[1], mu[1])
+
+
+def test_variance_floor_clamps_constant_dimension():
+    rng = np.random.default_rng(23)
+    x = rng.normal(0, 1, size=(300, 3)).astype(np.float32)
+    x[:, 1] = 5.0
+    w1, mu1, v1, *_ = oracle.em_step(x, [1.0], [[0.0, 4.0, 0.0]], np.ones((1, 3)), 1e-3)
+    assert v1[0, 1] == 1e-3 and mu1[0, 1] == 5.0
+    assert v1[0, 0] > 1e-3
+
+
+def test_topm_order_ties_and_values():
+    rng = np.random.default_rng(24)
+    x = rng.normal(0, 2, size=(200, 3)).astype(np.float32)
+    w, mu, var = _rand_params(rng, 6, 3)
+    # components 2 and 4 identical: equal log-densities, the smaller index wins
+    mu[4], var[4], w[4] = mu[2], var[2], w[2]
+    idx, resp, gap = oracle.topm(x, w, mu, var, 3)
+    ell = oracle.logdensity(x, w, mu, var)
+    lse = logsumexp(ell, axis=1)
+    order = np.lexsort((np.tile(np.arange(6), (200, 1)), -ell), axis=1)  # by -l, then k
+    np.testing.assert_array_equal(idx, order[:, :3])
+    np.testing.assert_allclose(resp, np.exp(np.take_along_axis(ell, order[:, :3], 1) - lse[:, None]),
+                               rtol=1e-13)
+    srt = np.take_along_axis(ell, order, 1)
+    np.testing.assert_allclose(gap, srt[:, 2] - srt[:, 3], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(ell[:, 2], ell[:, 4])  # the tie really is exact
+    has4 = np.any(idx == 4, axis=1)
+    assert np.all(np.any(idx == 2, axis=1)[has4])  # 4 is never chosen before 2
+
+
+def test_empty_and_invalid_inputs():
+    x0 = np.zeros((0, 3), dtype=np.float32)
+    assert oracle.loglik(x0, [1.0], [[0, 0, 0]], [[1, 1, 1]]) == 0.0
+    with pytest.raises(oracle.OracleError):
+        oracle.em_step(x0, [1.0], [[0, 0, 0]], [[1, 1, 1]])
+    x = np.zeros((4, 3), dtype=np.float32)
+    with pytest.raises(oracle.OracleError):
+        oracle.em_step(x, [1.0], [[0, 0, 0]], [[1, 0, 1]])  # zero variance
+    with pytest.raises(oracle.OracleError):
+        oracle.em_step(x, [0.0], [[0, 0, 0]], [[1, 1, 1]])  # no positive weight
+    with pytest.raises(oracle.OracleError):
+        oracle.topm(x, [1.0], [[0, 0, 0]], [[1, 1, 1]], 2)  # m > K
+
+
+def test_sklearn_gaussian_mixture_cross_check():
+    from sklearn.mixture import GaussianMixture
+
+    W = dg.WORKLOADS["tiny"]
+    x = dg.rows(W)
+    w0, m0, v0 = dg.init_params(W, x)
+    w1, mu1, v1, L0, _ = oracle.em_step(x, w0, m0, v0, 0.0)
+    gm = GaussianMixture(n_components=W.k, covariance_type="diag", weights_init=w0.astype(np.float64),
+                         means_init=m0.astype(np.float64), precisions_init=1.0 / v0.astype(np.float64),
+                         reg_covar=0.0, max_iter=1, tol=0.0, init_params="random")
+    import warnings
+
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        gm.fit(x.astype(np.float64))
+    np.testing.assert_allclose(gm.weights_, w1, rtol=1e-9)
+    np.testing.assert_allclose(gm.means_, mu1, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(gm.covariances_, v1, rtol=1e-8)
+    # sklearn's score is the mean per-row log-likelihood
+    assert gm.score(x.astype(np.float64)) == pytest.approx(
+        oracle.loglik(x, gm.weights_, gm.means_, gm.covariances_) / len(x), rel=1e-12)
+
+
+def test_thread_count_independence():
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import numpy as np\n"
+        "from gmm_em_amd import datagen as dg\n"
+        "from oracle import oracle\n"
+        "x, pl, _ = dg.custom(20000, 5, 7, seed=25)\n"
+        "w = np.full(7, 1/7); mu = x[:7].astype(np.float64); v = np.ones((7, 5))\n"
+        "r = oracle.em_step(x, w, mu, v)\n"
+        "sys.stdout.buffer.write(b''.join(np.asarray(a, dtype=np.float64).tobytes() for a in r))\n"
+    ) % os.path.dirname(HERE)
+    outs = []
+    for t in ("1", "3", "8"):
+        env = dict(os.environ, OMP_NUM_THREADS=t)
+        outs.append(subprocess.run([sys.executable, "-c", code], env=env, check=True,
+                                   capture_output=True).stdout)
+    assert outs[0] == outs[1] == outs[2]
