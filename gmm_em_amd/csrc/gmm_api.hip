@@ -1,0 +1,298 @@
+// gmm_api.hip - the C ABI declared in include/gmm_em.h: argument checks,
+// workspace planning and the launch sequence of each entry point.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <new>
+
+#include "gmm_em.h"
+#include "gmm_internal.h"
+
+namespace gmm {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool make_plan(int d, int k, void* ws, Plan* pl) {
+    if (d < 1 || k < 1 || k > (1 << 22)) return false;
+    Plan p;
+    p.d = d;
+    p.dp = (d + 15) / 16 * 16;
+    if (p.dp > MAX_DP) return false;
+    p.k = k;
+    p.kp = (k + 63) / 64 * 64;
+    p.ntiles = p.kp / 16;
+    const int kgroups = p.ntiles / 4;
+    int g = (1024 + kgroups - 1) / kgroups;
+    p.ngroups = g < 1 ? 1 : (g > 512 ? 512 : g);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t o_status = take(16 * sizeof(int));
+    const size_t o_tshift = take((size_t)p.ntiles * p.dp * sizeof(float));
+    const size_t o_pg = take((size_t)p.kp * 2 * p.dp * sizeof(float));
+    const size_t o_c = take((size_t)p.kp * sizeof(float));
+    const size_t o_perm = take((size_t)p.kp * sizeof(int));
+    const size_t o_lse = take((size_t)CHUNK_ROWS * sizeof(float));
+    const size_t o_ll = take((size_t)(CHUNK_ROWS / 128) * sizeof(double));
+    const size_t o_np = take((size_t)p.ngroups * p.kp * sizeof(double));
+    const size_t o_part = take((size_t)p.ngroups * p.kp * 2 * p.dp * sizeof(double));
+    const size_t o_lt = take(sizeof(double));
+    p.bytes = off;
+    if (ws) {
+        char* b = (char*)ws;
+        p.status = (int*)(b + o_status);
+        p.tshift = (float*)(b + o_tshift);
+        p.Pg = (float*)(b + o_pg);
+        p.cvec = (float*)(b + o_c);
+        p.perm = (int*)(b + o_perm);
+        p.lse = (float*)(b + o_lse);
+        p.llpart = (double*)(b + o_ll);
+        p.npart = (double*)(b + o_np);
+        p.part = (double*)(b + o_part);
+        p.ll_tmp = (double*)(b + o_lt);
+    }
+    *pl = p;
+    return true;
+}
+
+}  // namespace gmm
+
+using namespace gmm;
+
+static int check_common(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                        const void* w, const void* mu, const void* var, int32_t k, void* ws,
+                        size_t ws_bytes, Plan* pl) {
+    if (n < 0 || d < 1 || k < 1 || ldx < d) return GMM_E_INVALID;
+    if (n > 0 && !x) return GMM_E_INVALID;
+    if (!w || !mu || !var) return GMM_E_INVALID;
+    if (x_dtype != GMM_F32 && x_dtype != GMM_BF16) return GMM_E_DTYPE;
+    if (!make_plan(d, k, nullptr, pl)) return GMM_E_UNSUPPORTED;
+    if (!ws || ws_bytes < pl->bytes) return GMM_E_WORKSPACE;
+    if ((uintptr_t)ws % 256 != 0) return GMM_E_WORKSPACE;
+    make_plan(d, k, ws, pl);
+    return GMM_OK;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? GMM_OK : GMM_E_HIP; }
+
+// E-step over all rows: per-row normalisers (to lse_rows + offset when given,
+// else to the chunk scratch) and the log-likelihood partials. When `stats`
+// is set, each chunk's statistics pass follows its normaliser pass.
+// Optional event recording around the two passes (gmm_profile_begin/end).
+struct Prof {
+    bool on = false;
+    int cap = 0;
+    int n1 = 0, n2 = 0;
+    hipEvent_t* ev1 = nullptr;  // [2*cap] start/stop pairs, pass 1
+    hipEvent_t* ev2 = nullptr;  // [2*cap] pass 2
+};
+static Prof g_prof;
+
+static void prof_mark(int pass, bool start, hipStream_t st) {
+    if (!g_prof.on) return;
+    int& cnt = pass == 1 ? g_prof.n1 : g_prof.n2;
+    hipEvent_t* ev = pass == 1 ? g_prof.ev1 : g_prof.ev2;
+    if (cnt >= g_prof.cap) return;
+    (void)hipEventRecord(ev[2 * cnt + (start ? 0 : 1)], st);
+    if (!start) ++cnt;
+}
+
+static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                             float* lse_rows, bool stats, hipStream_t st, int m = 0,
+                             int32_t* idx = nullptr, float* resp = nullptr) {
+    const size_t esz = dtype == GMM_BF16 ? 2 : 4;
+    for (int64_t c0 = 0, ci = 0; c0 < n; c0 += CHUNK_ROWS, ++ci) {
+        const int64_t cn = n - c0 < CHUNK_ROWS ? n - c0 : CHUNK_ROWS;
+        const void* xc = (const char*)x + (size_t)c0 * (size_t)ldx * esz;
+        float* lse = (lse_rows && lse_rows != pl.lse) ? lse_rows + c0 : pl.lse;
+        prof_mark(1, true, st);
+        hipError_t e = launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m,
+                                  m > 0 ? idx + c0 * m : nullptr, m > 0 ? resp + c0 * m : nullptr, st);
+        prof_mark(1, false, st);
+        if (e != hipSuccess) return e;
+        if (stats) {
+            prof_mark(2, true, st);
+            e = launch_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+            prof_mark(2, false, st);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+static int ll_parts(int64_t n) {
+    const int64_t first = n < CHUNK_ROWS ? n : CHUNK_ROWS;
+    return (int)((first + 127) / 128);
+}
+
+extern "C" {
+
+size_t gmm_workspace_bytes(int32_t d, int32_t k) {
+    Plan p;
+    return make_plan(d, k, nullptr, &p) ? p.bytes : 0;
+}
+
+int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype, float* weights,
+                float* means, float* variances, int32_t k, float var_floor, double* loglik_dev,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    int rc = check_common(x, n, d, ldx, x_dtype, weights, means, variances, k, workspace,
+                          workspace_bytes, &pl);
+    if (rc) return rc;
+    if (n < 1 || !(var_floor >= 0.0f) || !isfinite(var_floor)) return GMM_E_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_prologue(pl, weights, means, variances, st);
+    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, nullptr, true, st);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(n), loglik_dev ? loglik_dev : pl.ll_tmp, st);
+    if (e == hipSuccess) e = launch_finalize(pl, n, var_floor, weights, means, variances, st);
+    return hip_status(e);
+}
+
+int gmm_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype, float* weights,
+            float* means, float* variances, int32_t k, float var_floor, int32_t max_iter,
+            double tol, double* loglik_hist_dev, int32_t* iters_done, void* workspace,
+            size_t workspace_bytes, void* stream) {
+    if (max_iter < 0 || !(tol >= 0.0) || !isfinite(tol)) return GMM_E_INVALID;
+    Plan pl;
+    int rc = check_common(x, n, d, ldx, x_dtype, weights, means, variances, k, workspace,
+                          workspace_bytes, &pl);
+    if (rc) return rc;
+    if (n < 1 || !(var_floor >= 0.0f) || !isfinite(var_floor)) return GMM_E_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    double prev = 0.0;
+    int done = 0;
+    for (int it = 0; it < max_iter; ++it) {
+        double* ll = loglik_hist_dev ? loglik_hist_dev + it : pl.ll_tmp;
+        rc = gmm_em_step(x, n, d, ldx, x_dtype, weights, means, variances, k, var_floor, ll,
+                         workspace, workspace_bytes, stream);
+        if (rc) break;
+        ++done;
+        if (tol > 0.0) {
+            double cur = 0.0;
+            if (hipMemcpyAsync(&cur, ll, sizeof(double), hipMemcpyDeviceToHost, st) != hipSuccess ||
+                hipStreamSynchronize(st) != hipSuccess) {
+                rc = GMM_E_HIP;
+                break;
+            }
+            if (it > 0 && cur - prev < tol * fabs(cur)) break;
+            prev = cur;
+        }
+    }
+    if (iters_done) *iters_done = done;
+    return rc;
+}
+
+int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+               const float* weights, const float* means, const float* variances, int32_t k,
+               double* total_dev, float* per_row_dev, void* workspace, size_t workspace_bytes,
+               void* stream) {
+    Plan pl;
+    int rc = check_common(x, n, d, ldx, x_dtype, weights, means, variances, k, workspace,
+                          workspace_bytes, &pl);
+    if (rc) return rc;
+    if (!total_dev) return GMM_E_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_prologue(pl, weights, means, variances, st);
+    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, per_row_dev, false, st);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(n), total_dev, st);
+    return hip_status(e);
+}
+
+int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                    const float* weights, const float* means, const float* variances, int32_t k,
+                    int32_t m, int32_t* idx_dev, float* resp_dev, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (m < 1 || m > 4 || m > k || ((!idx_dev || !resp_dev) && n > 0)) return GMM_E_INVALID;
+    Plan pl;
+    int rc = check_common(x, n, d, ldx, x_dtype, weights, means, variances, k, workspace,
+                          workspace_bytes, &pl);
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_prologue(pl, weights, means, variances, st);
+    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, pl.lse, false, st, m, idx_dev, resp_dev);
+    return hip_status(e);
+}
+
+int gmm_device_status(const void* workspace, void* stream) {
+    if (!workspace) return GMM_E_INVALID;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GMM_E_HIP;
+    int st[2] = {0, 0};
+    if (hipMemcpy(st, workspace, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return GMM_E_HIP;
+    return (st[0] != 0 || st[1] == 0) ? GMM_E_PARAMS : GMM_OK;
+}
+
+const char* gmm_status_string(int status) {
+    switch (status) {
+        case GMM_OK: return "ok";
+        case GMM_E_INVALID: return "invalid argument";
+        case GMM_E_DTYPE: return "unsupported data type";
+        case GMM_E_WORKSPACE: return "workspace missing, misaligned or too small";
+        case GMM_E_PARAMS: return "invalid parameter values";
+        case GMM_E_HIP: return "HIP runtime error";
+        case GMM_E_UNSUPPORTED: return "shape not supported by this build";
+        default: return "unknown status";
+    }
+}
+
+int gmm_profile_begin(int32_t max_launches) {
+    if (max_launches < 1 || max_launches > (1 << 16)) return GMM_E_INVALID;
+    if (g_prof.cap < max_launches) {
+        hipEvent_t* e1 = new (std::nothrow) hipEvent_t[2 * max_launches];
+        hipEvent_t* e2 = new (std::nothrow) hipEvent_t[2 * max_launches];
+        if (!e1 || !e2) {
+            delete[] e1;
+            delete[] e2;
+            return GMM_E_INVALID;
+        }
+        for (int i = 0; i < 2 * g_prof.cap; ++i) {
+            (void)hipEventDestroy(g_prof.ev1[i]);
+            (void)hipEventDestroy(g_prof.ev2[i]);
+        }
+        delete[] g_prof.ev1;
+        delete[] g_prof.ev2;
+        g_prof.ev1 = e1;
+        g_prof.ev2 = e2;
+        for (int i = 0; i < 2 * max_launches; ++i) {
+            if (hipEventCreate(&e1[i]) != hipSuccess || hipEventCreate(&e2[i]) != hipSuccess) {
+                g_prof.cap = 0;
+                return GMM_E_HIP;
+            }
+        }
+        g_prof.cap = max_launches;
+    }
+    g_prof.n1 = g_prof.n2 = 0;
+    g_prof.on = true;
+    return GMM_OK;
+}
+
+int gmm_profile_end(double* ms1, int32_t* n1, double* ms2, int32_t* n2) {
+    g_prof.on = false;
+    double t1 = 0.0, t2 = 0.0;
+    for (int i = 0; i < g_prof.n1; ++i) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(g_prof.ev1[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, g_prof.ev1[2 * i], g_prof.ev1[2 * i + 1]) != hipSuccess)
+            return GMM_E_HIP;
+        t1 += ms;
+    }
+    for (int i = 0; i < g_prof.n2; ++i) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(g_prof.ev2[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, g_prof.ev2[2 * i], g_prof.ev2[2 * i + 1]) != hipSuccess)
+            return GMM_E_HIP;
+        t2 += ms;
+    }
+    if (ms1) *ms1 = t1;
+    if (n1) *n1 = g_prof.n1;
+    if (ms2) *ms2 = t2;
+    if (n2) *n2 = g_prof.n2;
+    return GMM_OK;
+}
+
+int32_t gmm_version(void) { return 100; }
+
+}  // extern "C"

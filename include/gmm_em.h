@@ -1,0 +1,138 @@
+/*
+ * gmm_em.h - C ABI of the fused diagonal-covariance GMM EM library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is one expectation-maximization (EM) iteration of a Gaussian
+ * mixture with diagonal covariances, fused so that the N x K responsibility
+ * matrix is never written to device memory: statistics are formed per data
+ * tile and accumulated globally into O(K*D) buffers ("Flash-GMM: A
+ * Memory-Efficient Kernel for Scalable Soft Clustering", section 1 for the
+ * responsibility matrix, section 3 for the tiled EM with globally accumulated
+ * per-tile statistics; the abstract for the use of responsibilities to assign
+ * border vectors to several clusters).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Data X: device pointer, row-major, n rows of d values with a leading
+ *   dimension ldx >= d (in elements), fp32 or bf16 (x_dtype).
+ * Parameters: device pointers, fp32, row-major:
+ *   weights[k] (mixture weights, >= 0, not all 0),
+ *   means[k*d], variances[k*d] (> 0).
+ * Workspace: a device buffer of at least gmm_workspace_bytes(d, k) bytes,
+ *   owned by the caller. Its size does not depend on n. Calls that share a
+ *   workspace must not overlap in time (use one stream, or separate
+ *   workspaces).
+ * Stream: a hipStream_t passed as void* (NULL = the null stream). All work is
+ *   enqueued asynchronously on it; results are valid once the stream has
+ *   reached them. Nothing synchronises except gmm_device_status and
+ *   gmm_fit with tol > 0.
+ * Errors: every function returns a gmm_status. Argument errors found on the
+ *   host are returned before anything is enqueued (buffers are untouched).
+ *   Invalid parameter values (non-finite, variance <= 0, negative weight,
+ *   all weights zero) are detected on the device: the call still returns
+ *   GMM_OK, outputs are NaN, and gmm_device_status reports GMM_E_PARAMS.
+ *   No function throws or aborts.
+ * Determinism: for a given device, inputs and (d, k) every output is
+ *   bitwise reproducible; no floating-point atomics are used.
+ * Ownership: the library allocates no device memory and keeps no state
+ *   between calls besides cached device properties.
+ */
+#ifndef GMM_EM_H
+#define GMM_EM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GMM_OK = 0,
+    GMM_E_INVALID = 1,   /* bad size, pointer, stride or option */
+    GMM_E_DTYPE = 2,     /* unsupported data type */
+    GMM_E_WORKSPACE = 3, /* workspace missing or too small */
+    GMM_E_PARAMS = 4,    /* invalid parameter values (reported by gmm_device_status) */
+    GMM_E_HIP = 5,       /* a HIP runtime call failed */
+    GMM_E_UNSUPPORTED = 6 /* shape outside what this build supports */
+} gmm_status;
+
+typedef enum { GMM_F32 = 0, GMM_BF16 = 1 } gmm_dtype;
+
+/* Bytes of device workspace needed for data of dimension d and k components.
+ * Independent of the number of rows. Returns 0 for unsupported shapes. */
+size_t gmm_workspace_bytes(int32_t d, int32_t k);
+
+/* One EM iteration (E-step, responsibilities, M-step) in place.
+ *
+ * Computes, for the input parameters theta = (weights, means, variances):
+ *   l[n][k]  = log w[k] + log N(x_n | mu_k, diag(var_k))      (log-density)
+ *   lse[n]   = log sum_k exp(l[n][k])                          (normaliser)
+ *   r[n][k]  = exp(l[n][k] - lse[n])                          (responsibility)
+ *   N[k] = sum_n r[n][k], S1[k] = sum_n r[n][k] x_n, S2 = sum_n r[n][k] x_n^2
+ * and overwrites theta with the M-step update
+ *   w'[k] = N[k]/n, mu'[k] = S1[k]/N[k], var'[k] = max(S2[k]/N[k] - mu'[k]^2, var_floor)
+ * (a component with N[k] == 0 keeps its mean and variance and gets weight 0).
+ * r is never stored: it lives in registers between the two contractions.
+ * loglik_dev (device, 1 double, may be NULL) receives sum_n lse[n] for the
+ * INPUT parameters. var_floor must be finite and >= 0. n >= 1. */
+int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                float* weights, float* means, float* variances, int32_t k, float var_floor,
+                double* loglik_dev, void* workspace, size_t workspace_bytes, void* stream);
+
+/* max_iter EM iterations (gmm_em_step repeated). loglik_hist_dev (device,
+ * max_iter doubles, may be NULL) receives L(theta_t) for t = 0, 1, ...
+ * When tol > 0 the host reads each L after its step (one synchronisation per
+ * iteration) and stops once L_t - L_{t-1} < tol * |L_t|. iters_done (host
+ * pointer, may be NULL) receives the number of steps taken. */
+int gmm_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+            float* weights, float* means, float* variances, int32_t k, float var_floor,
+            int32_t max_iter, double tol, double* loglik_hist_dev, int32_t* iters_done,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Log-likelihood of the data under the parameters (the E-step half only).
+ * total_dev (device, 1 double) receives sum_n lse[n]; per_row_dev (device,
+ * n floats, may be NULL) receives lse[n]. n may be 0 (total = 0). */
+int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+               const float* weights, const float* means, const float* variances, int32_t k,
+               double* total_dev, float* per_row_dev, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Soft multi-assignment: the m components of highest responsibility for each
+ * row, most responsible first (ties: smaller component index first), with
+ * their responsibilities r[n][k]. idx_dev (device, n*m int32) and resp_dev
+ * (device, n*m floats) are row-major n x m. 1 <= m <= min(k, 4). n may be 0.
+ * Parameter errors are reported by gmm_device_status; the outputs are then
+ * unspecified. */
+int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                    const float* weights, const float* means, const float* variances, int32_t k,
+                    int32_t m, int32_t* idx_dev, float* resp_dev, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Synchronises the stream and returns GMM_E_PARAMS if the last call that used
+ * this workspace found invalid parameter values, GMM_OK otherwise, or
+ * GMM_E_HIP if the synchronisation failed. */
+int gmm_device_status(const void* workspace, void* stream);
+
+/* Static description of a status code. */
+const char* gmm_status_string(int status);
+
+/* Measurement hook. gmm_profile_begin(max_launches) starts recording HIP
+ * events on the caller's stream around every normaliser-pass (pass 1) and
+ * statistics-pass (pass 2) kernel launch of the following calls, up to
+ * max_launches of each (events are created on first use; no device memory is
+ * allocated). gmm_profile_end() synchronises those events and returns the
+ * summed milliseconds and launch counts of each pass, then stops recording.
+ * Not thread-safe; meant for benchmarks. */
+int gmm_profile_begin(int32_t max_launches);
+int gmm_profile_end(double* ms_pass1, int32_t* launches_pass1, double* ms_pass2,
+                    int32_t* launches_pass2);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t gmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMM_EM_H */

@@ -1,0 +1,86 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gmm_em.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gmm_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from gmm_em_amd import ops as o
+
+    return o
+
+
+def test_library_exports_every_declared_symbol(ops):
+    names = _declared()
+    assert {"gmm_em_step", "gmm_fit", "gmm_loglik", "gmm_assign_topm"} <= set(names)
+    for nm in names:
+        assert hasattr(ops.lib, nm), nm
+    assert ops.lib.gmm_version() >= 100
+
+
+def test_workspace_size_rules(ops):
+    a = ops.workspace_bytes(96, 1024)
+    assert a > 0 and a % 256 == 0
+    assert ops.workspace_bytes(96, 1024) == a  # no dependence on rows by construction
+    assert ops.workspace_bytes(0, 8) == 0 and ops.workspace_bytes(16, 0) == 0
+    assert ops.workspace_bytes(100000, 8) == 0  # unsupported dimension
+    assert ops.workspace_bytes(5, 3) == ops.workspace_bytes(16, 64)  # padded shapes share a plan
+
+
+def test_status_strings(ops):
+    for c in range(7):
+        assert ops.lib.gmm_status_string(c).decode()
+    assert ops.lib.gmm_status_string(99).decode() == "unknown status"
+
+
+def _em(ops, **kw):
+    a = dict(x=1, n=10, d=4, ldx=4, dt=0, w=1, mu=1, var=1, k=2, floor=1e-6, ll=None, ws=1, wsb=0,
+             st=None)
+    a.update(kw)
+    return ops.lib.gmm_em_step(a["x"], a["n"], a["d"], a["ldx"], a["dt"], a["w"], a["mu"], a["var"],
+                               a["k"], a["floor"], a["ll"], a["ws"], a["wsb"], a["st"])
+
+
+def test_bad_arguments_rejected_before_any_launch(ops):
+    # every case is decided on the host: no device pointer is dereferenced
+    assert _em(ops, n=0) == ops.GMM_E_WORKSPACE or _em(ops, n=0) == ops.GMM_E_INVALID
+    assert _em(ops, n=-1) == ops.GMM_E_INVALID
+    assert _em(ops, d=0) == ops.GMM_E_INVALID
+    assert _em(ops, ldx=3) == ops.GMM_E_INVALID
+    assert _em(ops, k=0) == ops.GMM_E_INVALID
+    assert _em(ops, x=None) == ops.GMM_E_INVALID
+    assert _em(ops, mu=None) == ops.GMM_E_INVALID
+    assert _em(ops, dt=7) == ops.GMM_E_DTYPE
+    assert _em(ops, d=4000, ldx=4000) == ops.GMM_E_UNSUPPORTED
+    assert _em(ops, ws=None) == ops.GMM_E_WORKSPACE
+    assert _em(ops, wsb=16) == ops.GMM_E_WORKSPACE
+    need = ops.workspace_bytes(4, 2)
+    assert _em(ops, ws=256 + 1, wsb=need) == ops.GMM_E_WORKSPACE  # misaligned
+    # n == 0 and a bad floor are invalid for an EM step once the workspace is fine
+    assert _em(ops, n=0, ws=256, wsb=need) == ops.GMM_E_INVALID
+    assert _em(ops, floor=float("nan"), ws=256, wsb=need) == ops.GMM_E_INVALID
+    assert _em(ops, floor=-1.0, ws=256, wsb=need) == ops.GMM_E_INVALID
+
+
+def test_fit_and_topm_argument_checks(ops):
+    f = ops.lib.gmm_fit
+    need = ops.workspace_bytes(4, 2)
+    assert f(1, 10, 4, 4, 0, 1, 1, 1, 2, 1e-6, -1, 0.0, None, None, 256, need, None) == ops.GMM_E_INVALID
+    assert f(1, 10, 4, 4, 0, 1, 1, 1, 2, 1e-6, 3, -1.0, None, None, 256, need, None) == ops.GMM_E_INVALID
+    t = ops.lib.gmm_assign_topm
+    assert t(1, 10, 4, 4, 0, 1, 1, 1, 2, 0, 1, 1, 256, need, None) == ops.GMM_E_INVALID
+    assert t(1, 10, 4, 4, 0, 1, 1, 1, 2, 3, 1, 1, 256, need, None) == ops.GMM_E_INVALID
+    assert t(1, 10, 4, 4, 0, 1, 1, 1, 2, 1, None, 1, 256, need, None) == ops.GMM_E_INVALID

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Every case uses the same seeded inputs on both sides. Per-step comparisons
+feed the GPU's fp32 parameters (converted exactly) to the oracle, so they
+measure one step's kernel error; end-to-end comparisons run both sides from
+the same initial parameters.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gmm_em_amd import datagen as dg  # noqa: E402
+from oracle import oracle  # noqa: E402
+from tests.parity import assert_params_close, param_errors, rel  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from gmm_em_amd import ops as o
+
+    return o
+
+
+def _to_dev(*arrays):
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in arrays]
+
+
+def _host(*ts):
+    return [t.detach().cpu().numpy() for t in ts]
+
+
+def _gpu_step(ops, xt, w, mu, var, floor=1e-6, ws=None):
+    L = ops.em_step(xt, w, mu, var, floor, ws=ws)
+    torch.cuda.synchronize()
+    return L.item()
+
+
+def _per_step(ops, x, w0, m0, v0, steps, floor=1e-6, tol=1e-4, ltol=1e-5, label=""):
+    xt, w, mu, var = _to_dev(x, w0, m0, v0)
+    ws = ops.workspace(x.shape[1], len(w0), DEV)
+    worst = {}
+    for t in range(steps):
+        th = _host(w, mu, var)
+        Lg = _gpu_step(ops, xt, w, mu, var, floor, ws)
+        rw, rmu, rv, rL, nk = oracle.em_step(x, *th, floor)
+        assert rel(Lg, rL) <= ltol, f"{label} step {t}: loglik {Lg} vs {rL}"
+        e = assert_params_close(_host(w, mu, var), (rw, rmu, rv), nk, len(x), tol, f"{label} step {t}")
+        for kk in ("mu", "var", "w"):
+            worst[kk] = max(worst.get(kk, 0.0), e[kk])
+    assert ops.device_status(ws, DEV) == ops.GMM_OK
+    return worst
+
+
+def test_tiny_per_step_20_iterations(ops):
+    W = dg.WORKLOADS["tiny"]
+    x = dg.rows(W)
+    w0, m0, v0 = dg.init_params(W, x)
+    worst = _per_step(ops, x, w0, m0, v0, W.iters, W.var_floor, label="tiny")
+    print("tiny per-step worst", worst)
+
+
+def test_tiny_end_to_end_fit(ops):
+    W = dg.WORKLOADS["tiny"]
+    x = dg.rows(W)
+    w0, m0, v0 = dg.init_params(W, x)
+    xt, w, mu, var = _to_dev(x, w0, m0, v0)
+    hist, done = ops.fit(xt, w, mu, var, W.var_floor, W.iters)
+    torch.cuda.synchronize()
+    assert done == W.iters
+    rw, rmu, rv, rhist = oracle.fit(x, w0, m0, v0, W.var_floor, W.iters)
+    h = hist.cpu().numpy()
+    assert np.all(np.abs(h - rhist) / np.abs(rhist) <= 1e-5), (h, rhist)
+    nk = rw * len(x)
+    e = assert_params_close(_host(w, mu, var), (rw, rmu, rv), nk, len(x), 1e-4, "tiny fit")
+    print("tiny end-to-end", e)
+    assert np.all(np.diff(h) >= -1e-6 * np.abs(h[1:]))  # monotone within fp32 noise
+
+
+@pytest.mark.parametrize("n,d,k,seed", [(1007, 5, 3, 1), (3001, 20, 70, 2), (130, 16, 64, 3),
+                                         (64 * 7 + 5, 33, 17, 4), (5000, 128, 100, 5)])
+def test_ragged_shapes(ops, n, d, k, seed):
+    x, pl, _ = dg.custom(n, d, k, seed=seed)
+    rng = np.random.default_rng(seed)
+    w0 = rng.dirichlet(np.ones(k)).astype(np.float32)
+    m0 = x[rng.choice(n, k, replace=False)].copy()
+    v0 = rng.uniform(0.5, 2.0, size=(k, d)).astype(np.float32)
+    _per_step(ops, x, w0, m0, v0, 3, label=f"ragged n={n} d={d} k={k}")
+
+
+def test_single_component_closed_form(ops):
+    rng = np.random.default_rng(7)
+    x = (rng.normal(3.0, 2.0, size=(20000, 12))).astype(np.float32)
+    xt, w, mu, var = _to_dev(x, np.ones(1, np.float32), np.zeros((1, 12), np.float32),
+                             np.ones((1, 12), np.float32))
+    _gpu_step(ops, xt, w, mu, var)
+    X = x.astype(np.float64)
+    gw, gmu, gv = _host(w, mu, var)
+    assert gw[0] == 1.0
+    np.testing.assert_allclose(gmu[0], X.mean(0), rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(gv[0], X.var(0), rtol=1e-4)
+
+
+def test_loglik_total_and_rows(ops):
+    W = dg.WORKLOADS["embed"]
+    x = dg.rows(W, 50_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    rw, rmu, rv, *_ = oracle.em_step(x, w0, m0, v0)  # a fitted-ish parameter set
+    th = [a.astype(np.float32) for a in (rw, rmu, rv)]
+    xt, w, mu, var = _to_dev(x, *th)
+    tot, rows = ops.loglik(xt, w, mu, var, per_row=True)
+    torch.cuda.synchronize()
+    rL, rrows = oracle.loglik(x, *th, per_row=True)
+    assert rel(tot.item(), rL) <= 1e-5
+    g = rows.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(g - rrows) / np.maximum(np.abs(rrows), 1.0)) <= 1e-4
+
+
+def test_loglik_empty_input(ops):
+    xt = torch.zeros((0, 8), dtype=torch.float32, device=DEV)
+    w, mu, var = _to_dev(np.full(4, 0.25, np.float32), np.zeros((4, 8), np.float32),
+                         np.ones((4, 8), np.float32))
+    tot = ops.loglik(xt, w, mu, var)
+    torch.cuda.synchronize()
+    assert tot.item() == 0.0
+
+
+def _check_topm(idx, resp, ridx, rresp, gap, ell_scale):
+    same = np.all(idx == ridx, axis=1)
+    # a different choice is only allowed where the oracle's own margin is tiny
+    near_tie = gap < 1e-3 * np.maximum(1.0, ell_scale)
+    assert np.all(same | near_tie), f"{np.sum(~same & ~near_tie)} rows differ"
+    ok = same
+    np.testing.assert_allclose(resp[ok], rresp[ok], rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("wl,n,m", [("tiny", 10_000, 2), ("embed", 20_000, 2), ("tiny", 3001, 3)])
+def test_assign_topm(ops, wl, n, m):
+    W = dg.WORKLOADS[wl]
+    x = dg.rows(W, n)
+    w0, m0, v0 = dg.init_params(W, x)
+    rw, rmu, rv, *_ = oracle.em_step(x, w0, m0, v0)
+    th = [a.astype(np.float32) for a in (rw, rmu, rv)]
+    xt, w, mu, var = _to_dev(x, *th)
+    idx, resp = ops.assign_topm(xt, w, mu, var, m)
+    torch.cuda.synchronize()
+    ridx, rresp, gap = oracle.topm(x, *th, m)
+    ell_top = np.abs(np.log(np.maximum(rresp[:, 0], 1e-300)))
+    _check_topm(idx.cpu().numpy(), resp.cpu().numpy(), ridx, rresp, gap, ell_top)
+
+
+def test_embed_prefix_per_step(ops):
+    W = dg.WORKLOADS["embed"]
+    x = dg.rows(W, 100_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    worst = _per_step(ops, x, w0, m0, v0, 3, label="embed prefix")
+    print("embed per-step worst", worst)
+
+
+def test_descriptor_prefix_first_step(ops):
+    W = dg.WORKLOADS["descriptor"]
+    x = dg.rows(W, 200_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    xt, w, mu, var = _to_dev(x, w0, m0, v0)
+    Lg = _gpu_step(ops, xt, w, mu, var)
+    rw, rmu, rv, rL, nk = oracle.em_step(x, w0, m0, v0)
+    e = param_errors(_host(w, mu, var), (rw, rmu, rv), nk, len(x))
+    print("descriptor prefix step 0:", e, "loglik rel", rel(Lg, rL))
+    assert rel(Lg, rL) <= 1e-5
+    assert e["mu"] <= 1e-4 and e["var"] <= 1e-4 and e["w"] <= 1e-4, e
+
+
+def test_bitwise_determinism(ops):
+    W = dg.WORKLOADS["embed"]
+    x = dg.rows(W, 30_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    outs = []
+    for _ in range(2):
+        xt, w, mu, var = _to_dev(x, w0, m0, v0)
+        L = _gpu_step(ops, xt, w, mu, var)
+        outs.append((L, *_host(w, mu, var)))
+    assert outs[0][0] == outs[1][0]
+    for a, b in zip(outs[0][1:], outs[1][1:]):
+        assert np.array_equal(a, b)
+
+
+def test_invalid_parameters_reported(ops):
+    x = np.random.default_rng(3).normal(size=(500, 4)).astype(np.float32)
+    v0 = np.ones((2, 4), np.float32)
+    v0[1, 2] = 0.0
+    xt, w, mu, var = _to_dev(x, np.array([0.5, 0.5], np.float32), x[:2].copy(), v0)
+    ws = ops.workspace(4, 2, DEV)
+    ops.em_step(xt, w, mu, var, ws=ws)
+    assert ops.device_status(ws, DEV) == ops.GMM_E_PARAMS
+    assert np.all(np.isnan(w.cpu().numpy()))
+    # a valid call on the same workspace clears the status
+    xt, w, mu, var = _to_dev(x, np.array([0.5, 0.5], np.float32), x[:2].copy(), np.ones((2, 4), np.float32))
+    ops.em_step(xt, w, mu, var, ws=ws)
+    assert ops.device_status(ws, DEV) == ops.GMM_OK
+
+
+def test_rows_beyond_one_chunk(ops):
+    # more rows than one 2^22-row chunk: normalisers and partials carry over
+    n = (1 << 22) + 1234
+    x, pl, _ = dg.custom(n, 8, 4, seed=9)
+    rng = np.random.default_rng(9)
+    w0 = np.full(4, 0.25, np.float32)
+    m0 = x[rng.choice(n, 4, replace=False)].copy()
+    v0 = np.ones((4, 8), np.float32)
+    _per_step(ops, x, w0, m0, v0, 1, label="two chunks")
+
+
+def test_bf16_input(ops):
+    x, pl, _ = dg.custom(20_000, 32, 12, seed=11, dtype="bf16")
+    rng = np.random.default_rng(11)
+    w0 = np.full(12, 1 / 12, np.float32)
+    m0 = dg.bf16_bits_to_f32(x[rng.choice(len(x), 12, replace=False)]).copy()
+    v0 = np.ones((12, 32), np.float32)
+    xt = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    w, mu, var = _to_dev(w0, m0, v0)
+    Lg = _gpu_step(ops, xt, w, mu, var)
+    rw, rmu, rv, rL, nk = oracle.em_step(x, w0, m0, v0)
+    assert rel(Lg, rL) <= 1e-5
+    assert_params_close(_host(w, mu, var), (rw, rmu, rv), nk, len(x), 5e-3, "bf16")
