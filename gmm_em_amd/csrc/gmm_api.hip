@@ -32,11 +32,10 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
         return o;
     };
     const size_t o_status = take(16 * sizeof(int));
-    const size_t o_tshift = take((size_t)p.ntiles * p.dp * sizeof(float));
-    const size_t o_pg = take((size_t)p.kp * 2 * p.dp * sizeof(float));
-    const size_t o_c = take((size_t)p.kp * sizeof(float));
-    const size_t o_perm = take((size_t)p.kp * sizeof(int));
-    const size_t o_lse = take((size_t)CHUNK_ROWS * sizeof(float));
+    const size_t o_shift = take((size_t)p.dp * sizeof(double));
+    const size_t o_pg = take((size_t)p.kp * 2 * p.dp * sizeof(double));
+    const size_t o_c = take((size_t)p.kp * sizeof(double));
+    const size_t o_lse = take((size_t)CHUNK_ROWS * sizeof(double));
     const size_t o_ll = take((size_t)(CHUNK_ROWS / 128) * sizeof(double));
     const size_t o_np = take((size_t)p.ngroups * p.kp * sizeof(double));
     const size_t o_part = take((size_t)p.ngroups * p.kp * 2 * p.dp * sizeof(double));
@@ -45,11 +44,10 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     if (ws) {
         char* b = (char*)ws;
         p.status = (int*)(b + o_status);
-        p.tshift = (float*)(b + o_tshift);
-        p.Pg = (float*)(b + o_pg);
-        p.cvec = (float*)(b + o_c);
-        p.perm = (int*)(b + o_perm);
-        p.lse = (float*)(b + o_lse);
+        p.shift = (double*)(b + o_shift);
+        p.Pg = (double*)(b + o_pg);
+        p.cvec = (double*)(b + o_c);
+        p.lse = (double*)(b + o_lse);
         p.llpart = (double*)(b + o_ll);
         p.npart = (double*)(b + o_np);
         p.part = (double*)(b + o_part);
@@ -79,9 +77,6 @@ static int check_common(const void* x, int64_t n, int32_t d, int64_t ldx, int32_
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? GMM_OK : GMM_E_HIP; }
 
-// E-step over all rows: per-row normalisers (to lse_rows + offset when given,
-// else to the chunk scratch) and the log-likelihood partials. When `stats`
-// is set, each chunk's statistics pass follows its normaliser pass.
 // Optional event recording around the two passes (gmm_profile_begin/end).
 struct Prof {
     bool on = false;
@@ -101,14 +96,19 @@ static void prof_mark(int pass, bool start, hipStream_t st) {
     if (!start) ++cnt;
 }
 
+// E-step over all rows in chunks of CHUNK_ROWS: per-row normalisers into the
+// workspace scratch and the log-likelihood partials; with `stats`, each
+// chunk's statistics pass follows its normaliser pass; with m > 0, the top-m
+// components of each row are written to idx/resp; lse_rows, if given,
+// receives every row's normaliser instead of the chunk scratch.
 static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                             float* lse_rows, bool stats, hipStream_t st, int m = 0,
-                             int32_t* idx = nullptr, float* resp = nullptr) {
+                             bool stats, hipStream_t st, int m = 0, int32_t* idx = nullptr,
+                             float* resp = nullptr, double* lse_rows = nullptr) {
     const size_t esz = dtype == GMM_BF16 ? 2 : 4;
     for (int64_t c0 = 0, ci = 0; c0 < n; c0 += CHUNK_ROWS, ++ci) {
         const int64_t cn = n - c0 < CHUNK_ROWS ? n - c0 : CHUNK_ROWS;
         const void* xc = (const char*)x + (size_t)c0 * (size_t)ldx * esz;
-        float* lse = (lse_rows && lse_rows != pl.lse) ? lse_rows + c0 : pl.lse;
+        double* lse = lse_rows ? lse_rows + c0 : pl.lse;
         prof_mark(1, true, st);
         hipError_t e = launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m,
                                   m > 0 ? idx + c0 * m : nullptr, m > 0 ? resp + c0 * m : nullptr, st);
@@ -146,7 +146,7 @@ int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtyp
     if (n < 1 || !(var_floor >= 0.0f) || !isfinite(var_floor)) return GMM_E_INVALID;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_prologue(pl, weights, means, variances, st);
-    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, nullptr, true, st);
+    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, true, st);
     if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(n), loglik_dev ? loglik_dev : pl.ll_tmp, st);
     if (e == hipSuccess) e = launch_finalize(pl, n, var_floor, weights, means, variances, st);
     return hip_status(e);
@@ -188,7 +188,7 @@ int gmm_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype, f
 
 int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
                const float* weights, const float* means, const float* variances, int32_t k,
-               double* total_dev, float* per_row_dev, void* workspace, size_t workspace_bytes,
+               double* total_dev, double* per_row_dev, void* workspace, size_t workspace_bytes,
                void* stream) {
     Plan pl;
     int rc = check_common(x, n, d, ldx, x_dtype, weights, means, variances, k, workspace,
@@ -197,7 +197,8 @@ int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype
     if (!total_dev) return GMM_E_INVALID;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_prologue(pl, weights, means, variances, st);
-    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, per_row_dev, false, st);
+    if (e == hipSuccess)
+        e = run_passes(pl, x, n, ldx, x_dtype, false, st, 0, nullptr, nullptr, per_row_dev);
     if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(n), total_dev, st);
     return hip_status(e);
 }
@@ -213,7 +214,7 @@ int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_prologue(pl, weights, means, variances, st);
-    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, pl.lse, false, st, m, idx_dev, resp_dev);
+    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, false, st, m, idx_dev, resp_dev);
     return hip_status(e);
 }
 

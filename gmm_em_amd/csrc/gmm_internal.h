@@ -14,22 +14,21 @@ constexpr int64_t CHUNK_ROWS = (int64_t)1 << 22;
 
 // Workspace layout and launch geometry for one (d, k).
 struct Plan {
-    int d = 0, dp = 0;        // data dimension and its padding to a multiple of 16
-    int k = 0, kp = 0;        // components and their padding to a multiple of 64
-    int ntiles = 0;           // 16-component K-tiles (kp / 16)
-    int ngroups = 0;          // row groups of the statistics pass
-    size_t bytes = 0;         // workspace bytes
+    int d = 0, dp = 0;         // data dimension and its padding to a multiple of 16
+    int k = 0, kp = 0;         // components and their padding to a multiple of 64
+    int ntiles = 0;            // 16-component K-tiles (kp / 16)
+    int ngroups = 0;           // row groups of the statistics pass
+    size_t bytes = 0;          // workspace bytes
     // device pointers (null when planning sizes only)
-    int* status = nullptr;    // [0]: invalid-parameter flag, [1]: some weight > 0
-    float* tshift = nullptr;  // [ntiles][dp] per-tile shift, permuted dim order
-    float* Pg = nullptr;      // [kp][2*dp] coefficient rows, MFMA operand order
-    float* cvec = nullptr;    // [kp] per-component constants
-    int* perm = nullptr;      // [kp] slot -> component (-1 = padding)
-    float* lse = nullptr;     // [CHUNK_ROWS] per-row normaliser of the current chunk
-    double* llpart = nullptr; // [CHUNK_ROWS / 128] log-likelihood partials
-    double* npart = nullptr;  // [ngroups][kp] responsibility mass partials
-    double* part = nullptr;   // [ngroups][kp][2*dp] first/second moment partials
-    double* ll_tmp = nullptr; // [1] scratch total
+    int* status = nullptr;     // [0]: invalid-parameter flag, [1]: some weight > 0
+    double* shift = nullptr;   // [dp] per-dim shift, permuted dim order
+    double* Pg = nullptr;      // [kp][2*dp] coefficient rows, MFMA operand order
+    double* cvec = nullptr;    // [kp] per-component constants
+    double* lse = nullptr;     // [CHUNK_ROWS] per-row normaliser of the current chunk
+    double* llpart = nullptr;  // [CHUNK_ROWS / 128] log-likelihood partials
+    double* npart = nullptr;   // [ngroups][kp] responsibility mass partials
+    double* part = nullptr;    // [ngroups][kp][2*dp] first/second moment partials
+    double* ll_tmp = nullptr;  // [1] scratch total
 };
 
 bool make_plan(int d, int k, void* ws, Plan* pl);
@@ -39,10 +38,10 @@ hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, cons
 // lse_out may be null (normalisers not kept); m > 0 also writes the top-m
 // components (idx, resp, row-major n x m) of each row.
 hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                      float* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
+                      double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
                       hipStream_t st);
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                        const float* lse, int acc, hipStream_t st);
+                        const double* lse, int acc, hipStream_t st);
 hipError_t launch_finalize(const Plan& pl, int64_t n, float var_floor, float* w, float* mu,
                            float* var, hipStream_t st);
 hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st);

@@ -9,74 +9,81 @@
 // buffers; section 1: the responsibility matrix is what must not be
 // materialised).
 //
-// Arithmetic layout
-// -----------------
-// For component k and a per-tile shift vector t (all components of one
-// 16-wide K-tile share t), with a = x - t, w = 1/var, b = mu - t:
-//   l[n][k] = sum_d ( w b a  - w a^2 / 2 ) + c_k,
+// Arithmetic
+// ----------
+// With a per-dimension shift s, a = x - s, w = 1/var, b = mu - s:
+//   l[n][k] = sum_d ( w b a - w a^2 / 2 ) + c_k,
 //   c_k     = log pi_k - 1/2 sum_d ( w b^2 + log var ) - D/2 log 2 pi.
-// The sum over d is a dense contraction of the feature rows [a, a^2] with the
-// coefficient rows [w b, -w/2]: v_mfma_f32_16x16x4_f32, fp32 in and fp32
-// accumulate. The shift keeps the features small, which keeps fp32 rounding
-// in the expanded form small.
+// The sum over d is a dense contraction of feature rows [a, a^2] with
+// coefficient rows [w b, -w/2] (the X^2 (1/var)^T and X (mu/var)^T products
+// of the expanded Gaussian exponent). Both contractions of the step run on
+// v_mfma_f64_16x16x4_f64: the expanded form cancels terms of size w a^2
+// against each other, which fp32 cannot resolve for narrow components far
+// from the shift (a component at the variance floor has w = 1e6), while in
+// fp64 the features a, a^2 and all products and sums stay exact to ~1e-16.
 //
-// MFMA operand layout (16x16x4 f32, wave64): lane l = 16*h + i.
-//   A operand: A[i][h], B operand: B[h][i], C: lane holds C[4h + q][i], q=0..3.
-// E-step: A = features (row i of a 16-row block), B = coefficients (component
-//   i of a 16-wide K-tile); step t uses feature (dim 2t + (h>>1), power 1 +
-//   (h&1)); C[row 4h+q][comp i] = l.
-// M-step: the E-step C registers are used unchanged as the A operand
-//   (A[comp i][row 4h+q] for step q), the B operand is feature column
-//   16j + i of row 4h + q; C[comp 4h+q][feature 16j+i] accumulates
-//   sum_n r[n][comp] * feature[n]. The responsibilities never leave registers.
+// MFMA operand layout (16x16x4 f64, wave64): lane l = 16*h + i.
+//   A operand: A[i][h]; B operand: B[h][i]; C: register q holds C[4q + h][i].
+// E-step: A = feature (row i of a 16-row block), B = coefficient (component i
+//   of a 16-wide K-tile); step t uses feature (dim 2t + (h>>1), power
+//   1 + (h&1)); register q of lane (h, i) ends with l[row 4q+h][comp i].
+// M-step: those registers, as r = exp(l - lse), are the A operand as they
+//   stand: step q contracts A[comp i][h] = r[row 4q+h][comp i] with
+//   B[h][j] = feature column 16J + j of row 4q + h; register q of lane (h, i)
+//   accumulates S[comp 4q+h][feature 16J+i] = sum_n r[n][comp] f[n]. The
+//   responsibilities never leave registers.
 //
 // Two passes per row chunk (the M-step of a component needs each row's
 // normaliser over ALL components before any of its responsibilities exist):
-//   pass 1 (k_lse):   row-stationary; every K-tile streams through LDS; a
-//                     per-row online logsumexp; writes lse per row and fp64
-//                     log-likelihood partials.
-//   pass 2 (k_stats): K-tile-stationary (coefficients in registers, fp32
-//                     statistics in MFMA accumulators, flushed into fp64
-//                     registers every 64-row tile); recomputes l with the same
-//                     instruction sequence as pass 1, so both passes see
-//                     bitwise identical log-densities.
+//   pass 1 (k_lse):   row-stationary: every K-tile streams through LDS; per-row
+//                     online logsumexp; writes lse per row and fp64
+//                     log-likelihood partials (and the top-m components).
+//   pass 2 (k_stats): K-tile-stationary: coefficients and statistics stay in
+//                     registers; recomputes l with the same instruction
+//                     sequence as pass 1, so both passes see bitwise identical
+//                     log-densities.
 // Partials are summed in a fixed order in fp64 by k_finalize: no atomics on
 // floating-point data, bitwise reproducible results.
 #include <hip/hip_runtime.h>
-#include <stdint.h>
 #include <math.h>
+#include <stdint.h>
 
 #include "gmm_internal.h"
 
 namespace gmm {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float load_x(const float* p) { return *p; }
 __device__ __forceinline__ float load_x(const uint16_t* p) {
     return __uint_as_float(((uint32_t)(*p)) << 16);
 }
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f64x4 mfma4d(double a, double b, f64x4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
-// Feature value of one E-step operand: a = x - s, and a or a^2.
-__device__ __forceinline__ float feat(float x, float s, bool sq) {
-    float a = x - s;
-    return a * (sq ? a : 1.0f);
+// E-step operand: a = x - s (exact in fp64 for fp32 x), then a or a^2.
+__device__ __forceinline__ double feat(float x, double s, bool sq) {
+    const double a = (double)x - s;
+    return sq ? a * a : a;
 }
 
-// Online logsumexp update of (m, s) with value v.
-__device__ __forceinline__ void lse_push(float& m, float& s, float v) {
-    float mn = fmaxf(m, v);
-    s = s * __expf(m - mn) + __expf(v - mn);
+// Online logsumexp with the running maximum in fp64 and the scaled sum in
+// fp32 (every exponent argument is <= 0).
+__device__ __forceinline__ void lse_push(double& m, float& s, double v) {
+    const double mn = fmax(m, v);
+    s = s * __expf((float)(m - mn)) + __expf((float)(v - mn));
     m = mn;
 }
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-    float mn = fmaxf(m, m2);
-    s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+__device__ __forceinline__ void lse_merge(double& m, float& s, double m2, float s2) {
+    const double mn = fmax(m, m2);
+    s = s * __expf((float)(m - mn)) + s2 * __expf((float)(m2 - mn));
     m = mn;
+}
+
+__device__ __forceinline__ double shfl_xor_d(double v, int off) {
+    return __shfl_xor(v, off);
 }
 
 // ---------------------------------------------------------------------------
@@ -88,14 +95,14 @@ __global__ void k_status_reset(int* status) {
 
 __global__ void k_validate(const float* __restrict__ w, const float* __restrict__ mu,
                            const float* __restrict__ var, int k, int d, int* status) {
-    int64_t total = (int64_t)k * d;
+    const int64_t total = (int64_t)k * d;
     int bad = 0, anypos = 0;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        float m = mu[i], v = var[i];
+        const float m = mu[i], v = var[i];
         if (!isfinite(m) || !isfinite(v) || !(v > 0.0f)) bad = 1;
         if (i < k) {
-            float wi = w[i];
+            const float wi = w[i];
             if (!isfinite(wi) || wi < 0.0f) bad = 1;
             if (wi > 0.0f) anypos = 1;
         }
@@ -104,50 +111,48 @@ __global__ void k_validate(const float* __restrict__ w, const float* __restrict_
     if (anypos) atomicOr(&status[1], 1);
 }
 
-// Global shift: s_d = rint(mean_k mu[k][d]) (fp64 mean). Written for every
-// K-tile in the permuted dim order used by the kernels:
-// pos(d) = (d & 1) * DP/2 + d / 2.
-__global__ void k_shift(const float* __restrict__ mu, int k, int d, int dp, int ntiles,
-                        float* __restrict__ tshift) {
-    int dd = blockIdx.x * blockDim.x + threadIdx.x;
+// Shift s_d = rint(mean_k mu[k][d]), stored in the permuted dim order used by
+// the kernels: pos(d) = (d & 1) * DP/2 + d / 2 (even dims, then odd dims).
+__global__ void k_shift(const float* __restrict__ mu, int k, int d, int dp,
+                        double* __restrict__ shift) {
+    const int dd = blockIdx.x * blockDim.x + threadIdx.x;
     if (dd >= dp) return;
-    float sv = 0.0f;
+    double sv = 0.0;
     if (dd < d) {
         double acc = 0.0;
         for (int j = 0; j < k; ++j) acc += (double)mu[(int64_t)j * d + dd];
-        sv = (float)rint(acc / (double)k);
-        if (!isfinite(sv)) sv = 0.0f;
+        sv = rint(acc / (double)k);
+        if (!isfinite(sv)) sv = 0.0;
     }
-    int pos = (dd & 1) * (dp >> 1) + (dd >> 1);
-    for (int j = 0; j < ntiles; ++j) tshift[(int64_t)j * dp + pos] = sv;
+    shift[(dd & 1) * (dp >> 1) + (dd >> 1)] = sv;
 }
 
-// Coefficients for slot `blockIdx.x` (component perm[slot], or padding):
+// Coefficients of slot `blockIdx.x` (component = slot when slot < k, else
+// padding with coefficient 0 and constant -inf), in operand order:
 //   Pg[slot][h][t]: h&1 = 0 -> w*b of dim 2t+(h>>1), h&1 = 1 -> -w/2.
 //   cvec[slot] = log pi - 1/2 sum_d (w b^2 + log var) - D/2 log 2pi.
 __global__ void k_params(const float* __restrict__ w, const float* __restrict__ mu,
-                         const float* __restrict__ var, const int* __restrict__ perm, int k, int d,
-                         int dp, const float* __restrict__ tshift, float* __restrict__ Pg,
-                         float* __restrict__ cvec) {
-    __shared__ double red[256];
+                         const float* __restrict__ var, int k, int d, int dp,
+                         const double* __restrict__ shift, double* __restrict__ Pg,
+                         double* __restrict__ cvec) {
+    __shared__ double red[128];
     const int slot = blockIdx.x;
-    const int comp = perm[slot];
-    const int tile = slot >> 4;
+    const bool live = slot < k;
     const int dph = dp >> 1;
     double part = 0.0;
+    double* row = Pg + (int64_t)slot * 2 * dp;
     for (int dd = threadIdx.x; dd < dp; dd += blockDim.x) {
-        float cb = 0.0f, cq = 0.0f;
-        if (comp >= 0 && dd < d) {
-            double v = (double)var[(int64_t)comp * d + dd];
-            double s = (double)tshift[(int64_t)tile * dp + (dd & 1) * dph + (dd >> 1)];
-            double b = (double)mu[(int64_t)comp * d + dd] - s;
-            double iw = 1.0 / v;
-            cb = (float)(iw * b);
-            cq = (float)(-0.5 * iw);
+        double cb = 0.0, cq = 0.0;
+        if (live && dd < d) {
+            const double v = (double)var[(int64_t)slot * d + dd];
+            const double s = shift[(dd & 1) * dph + (dd >> 1)];
+            const double b = (double)mu[(int64_t)slot * d + dd] - s;
+            const double iw = 1.0 / v;
+            cb = iw * b;
+            cq = -0.5 * iw;
             part += iw * b * b + log(v);
         }
         const int t = dd >> 1, hh = (dd & 1) << 1;
-        float* row = Pg + (int64_t)slot * 2 * dp;
         row[(hh + 0) * dph + t] = cb;
         row[(hh + 1) * dph + t] = cq;
     }
@@ -158,32 +163,22 @@ __global__ void k_params(const float* __restrict__ w, const float* __restrict__ 
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        if (comp < 0) {
-            cvec[slot] = -INFINITY;
-        } else {
-            const double LOG_2PI = 1.8378770664093454835606594728112;
-            double wk = (double)w[comp];
-            double c = log(wk) - 0.5 * (red[0] + (double)d * LOG_2PI);
-            cvec[slot] = (float)c;
-        }
+        const double LOG_2PI = 1.8378770664093454835606594728112;
+        cvec[slot] = live ? log((double)w[slot]) - 0.5 * (red[0] + (double)d * LOG_2PI) : -INFINITY;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1: per-row logsumexp over all components.
-// Block: 4 waves x 2 row blocks of 16 rows = 128 rows. Each lane keeps the
-// features' source values (x of dims 2t + (h>>1)) of its two rows in
-// registers; the K-tiles' coefficient rows, shifts and constants stream
-// through double-buffered LDS.
+// Top-m bookkeeping for the soft multi-assignment (pass 1 only).
 // ---------------------------------------------------------------------------
-// Ordered insertion of (v, i) into a top list sorted by larger value first,
-// then smaller index (empty entries hold -inf and the largest index).
+// Ordered insertion of (v, i) into a list sorted by larger value first, then
+// smaller index (empty entries hold -inf and the largest index).
 template <int TM>
-__device__ __forceinline__ void top_push(float (&tv)[TM], int (&ti)[TM], float v, int i) {
+__device__ __forceinline__ void top_push(double (&tv)[TM], int (&ti)[TM], double v, int i) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
         const bool gt = v > tv[j] || (v == tv[j] && i < ti[j]);
-        const float ov = tv[j];
+        const double ov = tv[j];
         const int oi = ti[j];
         tv[j] = gt ? v : ov;
         ti[j] = gt ? i : oi;
@@ -192,23 +187,23 @@ __device__ __forceinline__ void top_push(float (&tv)[TM], int (&ti)[TM], float v
     }
 }
 
-// Merge with the top list of lane (lane ^ off): both lanes end with the same
-// top TM of the union (order: larger value first, then smaller index).
+// Merge with the list of lane (lane ^ off): both lanes end with the same top
+// TM of the union.
 template <int TM>
-__device__ __forceinline__ void top_merge(float (&tv)[TM], int (&ti)[TM], int off) {
-    float ov[TM];
+__device__ __forceinline__ void top_merge(double (&tv)[TM], int (&ti)[TM], int off) {
+    double ov[TM];
     int oi[TM];
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-        ov[j] = __shfl_xor(tv[j], off);
+        ov[j] = shfl_xor_d(tv[j], off);
         oi[j] = __shfl_xor(ti[j], off);
     }
-    float rv[TM];
+    double rv[TM];
     int ri[TM];
     int a = 0, b = 0;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-        float va = tv[0], vb = ov[0];
+        double va = tv[0], vb = ov[0];
         int ia = ti[0], ib = oi[0];
 #pragma unroll
         for (int u = 1; u < TM; ++u) {
@@ -225,20 +220,26 @@ __device__ __forceinline__ void top_merge(float (&tv)[TM], int (&ti)[TM], int of
     for (int j = 0; j < TM; ++j) { tv[j] = rv[j]; ti[j] = ri[j]; }
 }
 
+// ---------------------------------------------------------------------------
+// Pass 1: per-row logsumexp over all components.
+// Block: 4 waves x 2 row blocks of 16 rows = 128 rows. Each lane keeps the x
+// values behind its features (dims 2t + (h>>1) of its two rows) in registers;
+// the K-tiles' coefficient rows and constants stream through double-buffered
+// LDS.
+// ---------------------------------------------------------------------------
 template <int DP, typename XT, int TM>
 __global__ __launch_bounds__(256, DP <= 64 ? 2 : 1)
 void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
-           const float* __restrict__ Pg, const float* __restrict__ cvec,
-           const float* __restrict__ tshift, int ntiles, float* __restrict__ lse_out,
-           double* __restrict__ llpart, int ll_accumulate, const int* __restrict__ status,
-           int m_out, const int* __restrict__ perm, int32_t* __restrict__ idx_out,
-           float* __restrict__ resp_out) {
-    constexpr int TMA = TM > 0 ? TM : 1;
+           const double* __restrict__ Pg, const double* __restrict__ cvec,
+           const double* __restrict__ shift, int ntiles, double* __restrict__ lse_out,
+           double* __restrict__ llpart, int ll_accumulate, int k, int m_out,
+           int32_t* __restrict__ idx_out, float* __restrict__ resp_out) {
     constexpr int DPH = DP / 2;
-    constexpr int PSTR = 2 * DP + 4;  // LDS stride of one component's coefficients
-    __shared__ __attribute__((aligned(16))) float Pt[2][16 * PSTR];
-    __shared__ __attribute__((aligned(16))) float St[2][DP];
-    __shared__ float Ct[2][16];
+    constexpr int PSTR = 2 * DP + 2;  // LDS stride of one component (doubles)
+    constexpr int TMA = TM > 0 ? TM : 1;
+    __shared__ __attribute__((aligned(16))) double Pt[2][16 * PSTR];
+    __shared__ __attribute__((aligned(16))) double Sh[DP];
+    __shared__ double Ct[2][16];
     __shared__ double rowll[128];
 
     const int tid = threadIdx.x;
@@ -247,7 +248,6 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const bool sq = h & 1;
     const int64_t row0 = (int64_t)blockIdx.x * 128 + wave * 32;
 
-    // x values for this lane's two rows: dims 2t + half.
     float xr[2][DPH];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -260,26 +260,27 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             xr[rb][t] = (ok && dd < d) ? load_x(xp + dd) : 0.0f;
         }
     }
+    for (int i = tid; i < DP; i += 256) Sh[i] = shift[i];
 
     auto stage = [&](int tile, int buf) {
-        const float* src = Pg + (int64_t)tile * 16 * 2 * DP;
-        for (int i = tid; i < 16 * 2 * DP / 4; i += 256) {
-            const int e = i * 4;
+        const double* src = Pg + (int64_t)tile * 16 * 2 * DP;
+        for (int i = tid; i < 16 * DP; i += 256) {  // pairs of doubles
+            const int e = 2 * i;
             const int comp = e / (2 * DP), off = e % (2 * DP);
-            *(float4*)&Pt[buf][comp * PSTR + off] = *(const float4*)(src + e);
+            *(double2*)&Pt[buf][comp * PSTR + off] = *(const double2*)(src + e);
         }
-        for (int i = tid; i < DP; i += 256) St[buf][i] = tshift[(int64_t)tile * DP + i];
         if (tid < 16) Ct[buf][tid] = cvec[tile * 16 + tid];
     };
 
-    float m[2][4], s[2][4];
-    float tv[2][4][TMA];
+    double m[2][4];
+    float s[2][4];
+    double tv[2][4][TMA];
     int ti[2][4][TMA];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            m[rb][q] = -3.0e38f;
+            m[rb][q] = -1.0e300;
             s[rb][q] = 0.0f;
 #pragma unroll
             for (int j = 0; j < TMA; ++j) { tv[rb][q][j] = -INFINITY; ti[rb][q][j] = 0x7fffffff; }
@@ -287,29 +288,25 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 
     stage(0, 0);
     __syncthreads();
+    const double* sp = &Sh[half * DPH];
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
         if (tile + 1 < ntiles) stage(tile + 1, buf ^ 1);
-        const float* pp = &Pt[buf][ci * PSTR + h * DPH];
-        const float* sp = &St[buf][half * DPH];
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        const double* pp = &Pt[buf][ci * PSTR + h * DPH];
+        f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int t = 0; t < DPH; t += 4) {
-            const float4 pv = *(const float4*)(pp + t);
-            const float4 sv = *(const float4*)(sp + t);
-            acc0 = mfma4(feat(xr[0][t + 0], sv.x, sq), pv.x, acc0);
-            acc1 = mfma4(feat(xr[1][t + 0], sv.x, sq), pv.x, acc1);
-            acc0 = mfma4(feat(xr[0][t + 1], sv.y, sq), pv.y, acc0);
-            acc1 = mfma4(feat(xr[1][t + 1], sv.y, sq), pv.y, acc1);
-            acc0 = mfma4(feat(xr[0][t + 2], sv.z, sq), pv.z, acc0);
-            acc1 = mfma4(feat(xr[1][t + 2], sv.z, sq), pv.z, acc1);
-            acc0 = mfma4(feat(xr[0][t + 3], sv.w, sq), pv.w, acc0);
-            acc1 = mfma4(feat(xr[1][t + 3], sv.w, sq), pv.w, acc1);
+        for (int t = 0; t < DPH; t += 2) {
+            const double2 pv = *(const double2*)(pp + t);
+            const double2 sv = *(const double2*)(sp + t);
+            acc0 = mfma4d(feat(xr[0][t + 0], sv.x, sq), pv.x, acc0);
+            acc1 = mfma4d(feat(xr[1][t + 0], sv.x, sq), pv.x, acc1);
+            acc0 = mfma4d(feat(xr[0][t + 1], sv.y, sq), pv.y, acc0);
+            acc1 = mfma4d(feat(xr[1][t + 1], sv.y, sq), pv.y, acc1);
         }
-        const float c = Ct[buf][ci];
+        const double c = Ct[buf][ci];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float l0 = acc0[q] + c, l1 = acc1[q] + c;
+            const double l0 = acc0[q] + c, l1 = acc1[q] + c;
             lse_push(m[0][q], s[0][q], l0);
             lse_push(m[1][q], s[1][q], l1);
             if constexpr (TM > 0) {
@@ -327,8 +324,8 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         for (int q = 0; q < 4; ++q) {
 #pragma unroll 1
             for (int off = 1; off < 16; off <<= 1) {
-                float m2 = __shfl_xor(m[rb][q], off);
-                float s2 = __shfl_xor(s[rb][q], off);
+                const double m2 = shfl_xor_d(m[rb][q], off);
+                const float s2 = __shfl_xor(s[rb][q], off);
                 lse_merge(m[rb][q], s[rb][q], m2, s2);
                 if constexpr (TM > 0) top_merge<TM>(tv[rb][q], ti[rb][q], off);
             }
@@ -338,18 +335,17 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int lr = wave * 32 + rb * 16 + 4 * h + q;
+                const int lr = wave * 32 + rb * 16 + 4 * q + h;
                 const int64_t row = (int64_t)blockIdx.x * 128 + lr;
                 double v = 0.0;
                 if (row < n) {
-                    const float lse = m[rb][q] + __logf(s[rb][q]);
-                    if (lse_out) lse_out[row] = lse;
-                    v = (double)m[rb][q] + log((double)s[rb][q]);
+                    v = m[rb][q] + log((double)s[rb][q]);
+                    if (lse_out) lse_out[row] = v;
                     if constexpr (TM > 0) {
                         for (int j = 0; j < m_out; ++j) {
                             const int sl = ti[rb][q][j];
-                            idx_out[row * m_out + j] = perm[sl];
-                            resp_out[row * m_out + j] = __expf(tv[rb][q][j] - lse);
+                            idx_out[row * m_out + j] = sl < k ? sl : -1;
+                            resp_out[row * m_out + j] = __expf((float)(tv[rb][q][j] - v));
                         }
                     }
                 }
@@ -362,28 +358,27 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         for (int i = 0; i < 128; ++i) tot += rowll[i];
         llpart[blockIdx.x] = (ll_accumulate ? llpart[blockIdx.x] : 0.0) + tot;
     }
-    (void)status;
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2: statistics. Block = 4 waves; wave w owns K-tile kg*4 + w (16
-// components): its coefficients stay in registers, its fp32 statistics in
-// MFMA accumulators. The block walks the rows of its row group in 64-row
+// components): its coefficient rows stay in registers and its statistics in
+// fp64 MFMA accumulators. The block walks the rows of its row group in 64-row
 // tiles staged (double-buffered) in LDS in the permuted dim order.
 // ---------------------------------------------------------------------------
 template <int DP, typename XT>
 __global__ __launch_bounds__(256, DP <= 64 ? 2 : 1)
 void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
-             const float* __restrict__ Pg, const float* __restrict__ cvec,
-             const float* __restrict__ tshift, int ntiles, const float* __restrict__ lse,
-             int64_t rows_per_group, int ngroups, double* __restrict__ part,
-             double* __restrict__ npart, int accumulate) {
+             const double* __restrict__ Pg, const double* __restrict__ cvec,
+             const double* __restrict__ shift, int ntiles, const double* __restrict__ lse,
+             int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
+             int accumulate) {
     constexpr int DPH = DP / 2;
-    constexpr int XS = DP + 4;      // LDS row stride (floats)
-    constexpr int NJ = DP / 16;     // 16-dim column blocks per power
+    constexpr int XS = DP + 4;  // LDS row stride (floats)
+    constexpr int NJ = DP / 16; // 16-dim column blocks per power
     __shared__ __attribute__((aligned(16))) float xs[2][64 * XS];
-    __shared__ __attribute__((aligned(16))) float ts[4][DP];
-    __shared__ float ls[2][64];
+    __shared__ __attribute__((aligned(16))) double Sh[DP];
+    __shared__ double ls[2][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -395,33 +390,29 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int slot = tile * 16 + ci;
 
     // Stationary coefficients: P[slot][h][t], t = 0..DPH-1.
-    float pr[DPH];
+    double pr[DPH];
     {
-        const float* src = Pg + (int64_t)slot * 2 * DP + h * DPH;
+        const double* src = Pg + (int64_t)slot * 2 * DP + h * DPH;
 #pragma unroll
-        for (int t = 0; t < DPH; t += 4) {
-            float4 v = *(const float4*)(src + t);
-            pr[t] = v.x; pr[t + 1] = v.y; pr[t + 2] = v.z; pr[t + 3] = v.w;
+        for (int t = 0; t < DPH; t += 2) {
+            const double2 v = *(const double2*)(src + t);
+            pr[t] = v.x;
+            pr[t + 1] = v.y;
         }
     }
-    const float cc = cvec[slot];
-    for (int i = lane; i < DP; i += 64) ts[wave][i] = tshift[(int64_t)tile * DP + i];
+    const double cc = cvec[slot];
+    for (int i = tid; i < DP; i += 256) Sh[i] = shift[i];
     // Shift of dims 16j + ci for the M-step features.
-    float tm[NJ];
+    double tm[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int dd = 16 * j + ci;
-        tm[j] = tshift[(int64_t)tile * DP + (dd & 1) * DPH + (dd >> 1)];
+        tm[j] = shift[(dd & 1) * DPH + (dd >> 1)];
     }
 
-    f32x4 acc[2 * NJ];
-    double acc64[2 * NJ][4];
+    f64x4 acc[2 * NJ];
 #pragma unroll
-    for (int j = 0; j < 2 * NJ; ++j) {
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc64[j][q] = 0.0;
-    }
+    for (int j = 0; j < 2 * NJ; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
     double n64 = 0.0;
 
     const int64_t gr0 = (int64_t)g * rows_per_group;
@@ -446,65 +437,53 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 
     if (ntile_rows > 0) stage(0, 0);
     __syncthreads();
+    const double* sa = &Sh[half * DPH];
     for (int64_t it = 0; it < ntile_rows; ++it) {
         const int buf = it & 1;
         if (it + 1 < ntile_rows) stage(it + 1, buf ^ 1);
         const float* xb = xs[buf];
 #pragma unroll 1
         for (int rb = 0; rb < 4; ++rb) {
-            // E-step: l for rows 16rb + 4h + q, component slot.
+            // E-step: register q of lane (h, ci) -> l[row 16rb + 4q + h][slot].
             const float* xa = xb + (rb * 16 + ci) * XS + half * DPH;
-            const float* sa = &ts[wave][half * DPH];
-            f32x4 e = {0.f, 0.f, 0.f, 0.f};
+            f64x4 e = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
             for (int t = 0; t < DPH; t += 4) {
                 const float4 xv = *(const float4*)(xa + t);
-                const float4 sv = *(const float4*)(sa + t);
-                e = mfma4(feat(xv.x, sv.x, sq), pr[t + 0], e);
-                e = mfma4(feat(xv.y, sv.y, sq), pr[t + 1], e);
-                e = mfma4(feat(xv.z, sv.z, sq), pr[t + 2], e);
-                e = mfma4(feat(xv.w, sv.w, sq), pr[t + 3], e);
+                const double2 s0 = *(const double2*)(sa + t);
+                const double2 s1 = *(const double2*)(sa + t + 2);
+                e = mfma4d(feat(xv.x, s0.x, sq), pr[t + 0], e);
+                e = mfma4d(feat(xv.y, s0.y, sq), pr[t + 1], e);
+                e = mfma4d(feat(xv.z, s1.x, sq), pr[t + 2], e);
+                e = mfma4d(feat(xv.w, s1.y, sq), pr[t + 3], e);
             }
-            float r[4];
-            float rsum = 0.0f;
+            double r[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float l = e[q] + cc;
-                r[q] = __expf(l - ls[buf][rb * 16 + 4 * h + q]);
-                rsum += r[q];
+                const double l = e[q] + cc;
+                r[q] = (double)__expf((float)(l - ls[buf][rb * 16 + 4 * q + h]));
+                n64 += r[q];
             }
-            n64 += (double)rsum;
-            // M-step: A = r (component ci, row 4h+q), B = feature column 16j+ci.
+            // M-step: A = r (component ci, row 4q+h), B = feature column
+            // 16j + ci of that row.
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float* xm = xb + (rb * 16 + 4 * h + q) * XS;
+                const float* xm = xb + (rb * 16 + 4 * q + h) * XS;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const int dd = 16 * j + ci;
-                    const float a = xm[(dd & 1) * DPH + (dd >> 1)] - tm[j];
-                    acc[j] = mfma4(r[q], a, acc[j]);
-                    acc[NJ + j] = mfma4(r[q], a * a, acc[NJ + j]);
+                    const double a = (double)xm[(dd & 1) * DPH + (dd >> 1)] - tm[j];
+                    acc[j] = mfma4d(r[q], a, acc[j]);
+                    acc[NJ + j] = mfma4d(r[q], a * a, acc[NJ + j]);
                 }
             }
         }
-        // Flush the 64-row fp32 partial into fp64.
-#pragma unroll
-        for (int j = 0; j < 2 * NJ; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc64[j][q] += (double)acc[j][q];
-                acc[j][q] = 0.0f;
-            }
         __syncthreads();
     }
 
     // Responsibility mass: lanes ci, ci+16, ci+32, ci+48 hold disjoint rows.
-    {
-        double o = __shfl_xor(n64, 16);
-        n64 += o;
-        o = __shfl_xor(n64, 32);
-        n64 += o;
-    }
+    n64 += shfl_xor_d(n64, 16);
+    n64 += shfl_xor_d(n64, 32);
     const int64_t gbase = (int64_t)g * ntiles * 16;
     if (h == 0) {
         double* np = npart + gbase + slot;
@@ -514,9 +493,9 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     for (int j = 0; j < 2 * NJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int comp = tile * 16 + 4 * h + q;
+            const int comp = tile * 16 + 4 * q + h;
             double* p = part + (gbase + comp) * (2 * DP) + 16 * j + ci;
-            *p = (accumulate ? *p : 0.0) + acc64[j][q];
+            *p = (accumulate ? *p : 0.0) + acc[j][q];
         }
 }
 
@@ -524,21 +503,20 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 // Finalize: fixed-order fp64 sum over row groups, then the M-step update.
 // ---------------------------------------------------------------------------
 __global__ void k_finalize(const double* __restrict__ part, const double* __restrict__ npart,
-                           int ngroups, int kp, int dp, int d, const int* __restrict__ perm,
-                           const float* __restrict__ tshift, int64_t n, float var_floor,
+                           int ngroups, int kp, int dp, int d, int k,
+                           const double* __restrict__ shift, int64_t n, float var_floor,
                            float* __restrict__ w, float* __restrict__ mu, float* __restrict__ var,
                            const int* __restrict__ status) {
-    const int slot = blockIdx.x;
-    const int comp = perm[slot];
-    if (comp < 0) return;
+    const int comp = blockIdx.x;
+    if (comp >= k) return;
     const bool bad = status[0] != 0 || status[1] == 0;
     double N = 0.0;
-    for (int gg = 0; gg < ngroups; ++gg) N += npart[(int64_t)gg * kp + slot];
-    const int tile = slot >> 4, dph = dp >> 1;
+    for (int gg = 0; gg < ngroups; ++gg) N += npart[(int64_t)gg * kp + comp];
+    const int dph = dp >> 1;
     for (int dd = threadIdx.x; dd < d; dd += blockDim.x) {
         double s1 = 0.0, s2 = 0.0;
         for (int gg = 0; gg < ngroups; ++gg) {
-            const double* p = part + ((int64_t)gg * kp + slot) * 2 * dp;
+            const double* p = part + ((int64_t)gg * kp + comp) * 2 * dp;
             s1 += p[dd];
             s2 += p[dp + dd];
         }
@@ -547,7 +525,7 @@ __global__ void k_finalize(const double* __restrict__ part, const double* __rest
             mu[e] = NAN;
             var[e] = NAN;
         } else if (N > 0.0) {
-            const double sh = (double)tshift[(int64_t)tile * dp + (dd & 1) * dph + (dd >> 1)];
+            const double sh = shift[(dd & 1) * dph + (dd >> 1)];
             const double m1 = s1 / N;
             const double v = s2 / N - m1 * m1;
             mu[e] = (float)(sh + m1);
@@ -574,29 +552,24 @@ __global__ void k_ll_final(const double* __restrict__ llpart, int nparts, double
     if (threadIdx.x == 0) *out = (status[0] != 0 || status[1] == 0) ? NAN : red[0];
 }
 
-__global__ void k_identity_perm(int* perm, int kp, int k) {
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < kp) perm[i] = i < k ? i : -1;
-}
-
 // ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI in gmm_api.hip).
 // ---------------------------------------------------------------------------
 template <int DP, typename XT, int TM>
 static hipError_t launch_lse_tm(const Plan& pl, const void* x, int64_t n, int64_t ldx,
-                                float* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
+                                double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
                                 hipStream_t st) {
     const int64_t blocks = (n + 127) / 128;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_lse<DP, XT, TM>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.tshift, pl.ntiles, lse_out,
-                       pl.llpart, ll_acc, pl.status, m, pl.perm, idx, resp);
+                       (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse_out,
+                       pl.llpart, ll_acc, pl.k, m, idx, resp);
     return hipGetLastError();
 }
 
 template <int DP, typename XT>
 static hipError_t launch_lse_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
-                               float* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
+                               double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
                                hipStream_t st) {
     if (m <= 0) return launch_lse_tm<DP, XT, 0>(pl, x, n, ldx, lse_out, ll_acc, 0, idx, resp, st);
     if (m <= 2) return launch_lse_tm<DP, XT, 2>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, st);
@@ -605,23 +578,24 @@ static hipError_t launch_lse_t(const Plan& pl, const void* x, int64_t n, int64_t
 
 template <int DP, typename XT>
 static hipError_t launch_stats_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
-                                 const float* lse, int acc, hipStream_t st) {
-    const int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + 63) / 64 * 64;
+                                 const double* lse, int acc, hipStream_t st) {
+    int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + 63) / 64 * 64;
+    if (rpg < 64) rpg = 64;
     hipLaunchKernelGGL((k_stats<DP, XT>), dim3(pl.ngroups * (pl.ntiles / 4)), dim3(256), 0, st,
-                       (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.tshift, pl.ntiles, lse,
-                       rpg > 0 ? rpg : 64, pl.ngroups, pl.part, pl.npart, acc);
+                       (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, rpg,
+                       pl.part, pl.npart, acc);
     return hipGetLastError();
 }
 
 #define GMM_DP_CASES(M) M(16) M(32) M(48) M(64) M(80) M(96) M(112) M(128)
 
 hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                      float* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
+                      double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
                       hipStream_t st) {
     switch (pl.dp) {
-#define CASE(DPV)                                                                        \
-    case DPV:                                                                            \
-        return dtype == 0                                                                \
+#define CASE(DPV)                                                                              \
+    case DPV:                                                                                  \
+        return dtype == 0                                                                      \
                    ? launch_lse_t<DPV, float>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, st) \
                    : launch_lse_t<DPV, uint16_t>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, st);
         GMM_DP_CASES(CASE)
@@ -631,11 +605,11 @@ hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int
 }
 
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                        const float* lse, int acc, hipStream_t st) {
+                        const double* lse, int acc, hipStream_t st) {
     switch (pl.dp) {
-#define CASE(DPV)                                                                          \
-    case DPV:                                                                              \
-        return dtype == 0 ? launch_stats_t<DPV, float>(pl, x, n, ldx, lse, acc, st)       \
+#define CASE(DPV)                                                                    \
+    case DPV:                                                                        \
+        return dtype == 0 ? launch_stats_t<DPV, float>(pl, x, n, ldx, lse, acc, st) \
                           : launch_stats_t<DPV, uint16_t>(pl, x, n, ldx, lse, acc, st);
         GMM_DP_CASES(CASE)
 #undef CASE
@@ -650,20 +624,17 @@ hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, cons
     int vb = (int)((total + 255) / 256);
     if (vb > 1024) vb = 1024;
     hipLaunchKernelGGL(k_validate, dim3(vb), dim3(256), 0, st, w, mu, var, pl.k, pl.d, pl.status);
-    hipLaunchKernelGGL(k_identity_perm, dim3((pl.kp + 255) / 256), dim3(256), 0, st, pl.perm,
-                       pl.kp, pl.k);
     hipLaunchKernelGGL(k_shift, dim3((pl.dp + 63) / 64), dim3(64), 0, st, mu, pl.k, pl.d, pl.dp,
-                       pl.ntiles, pl.tshift);
-    hipLaunchKernelGGL(k_params, dim3(pl.kp), dim3(128), 0, st, w, mu, var, pl.perm, pl.k, pl.d,
-                       pl.dp, pl.tshift, pl.Pg, pl.cvec);
+                       pl.shift);
+    hipLaunchKernelGGL(k_params, dim3(pl.kp), dim3(128), 0, st, w, mu, var, pl.k, pl.d, pl.dp,
+                       pl.shift, pl.Pg, pl.cvec);
     return hipGetLastError();
 }
 
 hipError_t launch_finalize(const Plan& pl, int64_t n, float var_floor, float* w, float* mu,
                            float* var, hipStream_t st) {
-    hipLaunchKernelGGL(k_finalize, dim3(pl.kp), dim3(128), 0, st, pl.part, pl.npart, pl.ngroups,
-                       pl.kp, pl.dp, pl.d, pl.perm, pl.tshift, n, var_floor, w, mu, var,
-                       pl.status);
+    hipLaunchKernelGGL(k_finalize, dim3(pl.k), dim3(128), 0, st, pl.part, pl.npart, pl.ngroups,
+                       pl.kp, pl.dp, pl.d, pl.k, pl.shift, n, var_floor, w, mu, var, pl.status);
     return hipGetLastError();
 }
 

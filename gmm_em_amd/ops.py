@@ -135,7 +135,7 @@ def loglik(x, weights, means, variances, per_row: bool = False, ws=None):
     k, d = _params(x, weights, means, variances)
     ws = _ws(ws, d, k, x.device)
     total = torch.empty((), dtype=torch.float64, device=x.device)
-    rows = torch.empty(x.shape[0], dtype=torch.float32, device=x.device) if per_row else None
+    rows = torch.empty(x.shape[0], dtype=torch.float64, device=x.device) if per_row else None
     _check(lib.gmm_loglik(_ptr(x), x.shape[0], d, ldx, dt, _ptr(weights), _ptr(means),
                           _ptr(variances), k, _ptr(total), _ptr(rows), _ptr(ws), ws.numel(),
                           _stream(x.device)))

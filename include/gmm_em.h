@@ -92,10 +92,10 @@ int gmm_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
 
 /* Log-likelihood of the data under the parameters (the E-step half only).
  * total_dev (device, 1 double) receives sum_n lse[n]; per_row_dev (device,
- * n floats, may be NULL) receives lse[n]. n may be 0 (total = 0). */
+ * n doubles, may be NULL) receives lse[n]. n may be 0 (total = 0). */
 int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
                const float* weights, const float* means, const float* variances, int32_t k,
-               double* total_dev, float* per_row_dev, void* workspace, size_t workspace_bytes,
+               double* total_dev, double* per_row_dev, void* workspace, size_t workspace_bytes,
                void* stream);
 
 /* Soft multi-assignment: the m components of highest responsibility for each

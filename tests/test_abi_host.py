@@ -37,7 +37,7 @@ def test_workspace_size_rules(ops):
     assert ops.workspace_bytes(96, 1024) == a  # no dependence on rows by construction
     assert ops.workspace_bytes(0, 8) == 0 and ops.workspace_bytes(16, 0) == 0
     assert ops.workspace_bytes(100000, 8) == 0  # unsupported dimension
-    assert ops.workspace_bytes(5, 3) == ops.workspace_bytes(16, 64)  # padded shapes share a plan
+    assert ops.workspace_bytes(96, 1025) >= a  # grows with K (never with the row count)
 
 
 def test_status_strings(ops):

@@ -117,7 +117,8 @@ def test_loglik_total_and_rows(ops):
     rL, rrows = oracle.loglik(x, *th, per_row=True)
     assert rel(tot.item(), rL) <= 1e-5
     g = rows.cpu().numpy().astype(np.float64)
-    assert np.max(np.abs(g - rrows) / np.maximum(np.abs(rrows), 1.0)) <= 1e-4
+    # the per-row normaliser is m + log(s) with m in fp64 and s an fp32 sum
+    assert np.max(np.abs(g - rrows) / np.maximum(np.abs(rrows), 1.0)) <= 1e-6
 
 
 def test_loglik_empty_input(ops):
@@ -161,17 +162,15 @@ def test_embed_prefix_per_step(ops):
     print("embed per-step worst", worst)
 
 
-def test_descriptor_prefix_first_step(ops):
+def test_descriptor_prefix_per_step(ops):
+    # integer descriptor data: after one step some components sit at the
+    # variance floor in some dims (w = 1e6), the hardest case for the
+    # expanded Gaussian exponent
     W = dg.WORKLOADS["descriptor"]
     x = dg.rows(W, 200_000)
     w0, m0, v0 = dg.init_params(W, x)
-    xt, w, mu, var = _to_dev(x, w0, m0, v0)
-    Lg = _gpu_step(ops, xt, w, mu, var)
-    rw, rmu, rv, rL, nk = oracle.em_step(x, w0, m0, v0)
-    e = param_errors(_host(w, mu, var), (rw, rmu, rv), nk, len(x))
-    print("descriptor prefix step 0:", e, "loglik rel", rel(Lg, rL))
-    assert rel(Lg, rL) <= 1e-5
-    assert e["mu"] <= 1e-4 and e["var"] <= 1e-4 and e["w"] <= 1e-4, e
+    worst = _per_step(ops, x, w0, m0, v0, 4, W.var_floor, label="descriptor prefix")
+    print("descriptor per-step worst", worst)
 
 
 def test_bitwise_determinism(ops):
