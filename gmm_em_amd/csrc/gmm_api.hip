@@ -20,9 +20,9 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     p.dp = (d + 15) / 16 * 16;
     if (p.dp > MAX_DP) return false;
     p.k = k;
-    p.kp = (k + 63) / 64 * 64;
+    p.kp = (k + 127) / 128 * 128;  // whole 8-tile groups of the statistics pass
     p.ntiles = p.kp / 16;
-    const int kgroups = p.ntiles / 4;
+    const int kgroups = p.ntiles / (p.dp <= 64 ? 8 : 4);
     int g = (1024 + kgroups - 1) / kgroups;
     p.ngroups = g < 1 ? 1 : (g > 512 ? 512 : g);
     size_t off = 0;
@@ -36,7 +36,7 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     const size_t o_pg = take((size_t)p.kp * 2 * p.dp * sizeof(double));
     const size_t o_c = take((size_t)p.kp * sizeof(double));
     const size_t o_lse = take((size_t)CHUNK_ROWS * sizeof(double));
-    const size_t o_ll = take((size_t)(CHUNK_ROWS / 128) * sizeof(double));
+    const size_t o_ll = take((size_t)(CHUNK_ROWS / LL_ROWS) * sizeof(double));
     const size_t o_np = take((size_t)p.ngroups * p.kp * sizeof(double));
     const size_t o_part = take((size_t)p.ngroups * p.kp * 2 * p.dp * sizeof(double));
     const size_t o_lt = take(sizeof(double));
@@ -126,7 +126,7 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
 
 static int ll_parts(int64_t n) {
     const int64_t first = n < CHUNK_ROWS ? n : CHUNK_ROWS;
-    return (int)((first + 127) / 128);
+    return (int)((first + LL_ROWS - 1) / LL_ROWS);
 }
 
 extern "C" {

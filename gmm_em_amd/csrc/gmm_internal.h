@@ -11,11 +11,13 @@ constexpr int MAX_DP = 128;
 // Rows per chunk: bounds the per-row normaliser scratch (lse) so that the
 // workspace size does not depend on the number of rows.
 constexpr int64_t CHUNK_ROWS = (int64_t)1 << 22;
+// Rows per normaliser-pass block (one log-likelihood partial each).
+constexpr int LL_ROWS = 128;
 
 // Workspace layout and launch geometry for one (d, k).
 struct Plan {
     int d = 0, dp = 0;         // data dimension and its padding to a multiple of 16
-    int k = 0, kp = 0;         // components and their padding to a multiple of 64
+    int k = 0, kp = 0;         // components and their padding to a multiple of 128
     int ntiles = 0;            // 16-component K-tiles (kp / 16)
     int ngroups = 0;           // row groups of the statistics pass
     size_t bytes = 0;          // workspace bytes
@@ -25,7 +27,7 @@ struct Plan {
     double* Pg = nullptr;      // [kp][2*dp] coefficient rows, MFMA operand order
     double* cvec = nullptr;    // [kp] per-component constants
     double* lse = nullptr;     // [CHUNK_ROWS] per-row normaliser of the current chunk
-    double* llpart = nullptr;  // [CHUNK_ROWS / 128] log-likelihood partials
+    double* llpart = nullptr;  // [CHUNK_ROWS / LL_ROWS] log-likelihood partials
     double* npart = nullptr;   // [ngroups][kp] responsibility mass partials
     double* part = nullptr;    // [ngroups][kp][2*dp] first/second moment partials
     double* ll_tmp = nullptr;  // [1] scratch total

@@ -222,13 +222,18 @@ __device__ __forceinline__ void top_merge(double (&tv)[TM], int (&ti)[TM], int o
 
 // ---------------------------------------------------------------------------
 // Pass 1: per-row logsumexp over all components.
-// Block: 4 waves x 2 row blocks of 16 rows = 128 rows. Each lane keeps the x
-// values behind its features (dims 2t + (h>>1) of its two rows) in registers;
-// the K-tiles' coefficient rows and constants stream through double-buffered
-// LDS.
+// Block: 8 waves x 16 rows. Each lane holds the fp64 features of its row in
+// E-operand order (feature (dim 2t + (h>>1), power 1 + (h&1)) for t = 0..
+// DP/2-1), computed once; the K-tiles' coefficient rows and constants stream
+// through double-buffered LDS shared by the 8 waves.
 // ---------------------------------------------------------------------------
+constexpr int LSE_WAVES = 8;
+constexpr int LSE_ROWS = LSE_WAVES * 16;
+static_assert(LSE_ROWS == 128, "the block's log-likelihood sum reads two rows per lane");
+static_assert(LSE_ROWS == LL_ROWS, "one log-likelihood partial per normaliser block");
+
 template <int DP, typename XT, int TM>
-__global__ __launch_bounds__(256, DP <= 64 ? 2 : 1)
+__global__ __launch_bounds__(LSE_WAVES * 64, 1)
 void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
            const double* __restrict__ Pg, const double* __restrict__ cvec,
            const double* __restrict__ shift, int ntiles, double* __restrict__ lse_out,
@@ -237,34 +242,33 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     constexpr int DPH = DP / 2;
     constexpr int PSTR = 2 * DP + 2;  // LDS stride of one component (doubles)
     constexpr int TMA = TM > 0 ? TM : 1;
+    constexpr int NT = LSE_WAVES * 64;
     __shared__ __attribute__((aligned(16))) double Pt[2][16 * PSTR];
-    __shared__ __attribute__((aligned(16))) double Sh[DP];
     __shared__ double Ct[2][16];
-    __shared__ double rowll[128];
+    __shared__ double rowll[LSE_ROWS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int ci = lane & 15, h = lane >> 4, half = h >> 1;
     const bool sq = h & 1;
-    const int64_t row0 = (int64_t)blockIdx.x * 128 + wave * 32;
+    const int64_t rowb = (int64_t)blockIdx.x * LSE_ROWS + wave * 16;
 
-    float xr[2][DPH];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int64_t row = row0 + rb * 16 + ci;
+    double fe[DPH];
+    {
+        const int64_t row = rowb + ci;
         const bool ok = row < n;
         const XT* xp = x + (ok ? row : 0) * ldx;
 #pragma unroll
         for (int t = 0; t < DPH; ++t) {
             const int dd = 2 * t + half;
-            xr[rb][t] = (ok && dd < d) ? load_x(xp + dd) : 0.0f;
+            const float xv = (ok && dd < d) ? load_x(xp + dd) : 0.0f;
+            fe[t] = feat(xv, shift[half * DPH + t], sq);
         }
     }
-    for (int i = tid; i < DP; i += 256) Sh[i] = shift[i];
 
     auto stage = [&](int tile, int buf) {
         const double* src = Pg + (int64_t)tile * 16 * 2 * DP;
-        for (int i = tid; i < 16 * DP; i += 256) {  // pairs of doubles
+        for (int i = tid; i < 16 * DP; i += NT) {  // pairs of doubles
             const int e = 2 * i;
             const int comp = e / (2 * DP), off = e % (2 * DP);
             *(double2*)&Pt[buf][comp * PSTR + off] = *(const double2*)(src + e);
@@ -272,121 +276,124 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         if (tid < 16) Ct[buf][tid] = cvec[tile * 16 + tid];
     };
 
-    double m[2][4];
-    float s[2][4];
-    double tv[2][4][TMA];
-    int ti[2][4][TMA];
+    double m[4];
+    float s[4];
+    double tv[4][TMA];
+    int ti[4][TMA];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int q = 0; q < 4; ++q) {
+        m[q] = -1.0e300;
+        s[q] = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            m[rb][q] = -1.0e300;
-            s[rb][q] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < TMA; ++j) { tv[rb][q][j] = -INFINITY; ti[rb][q][j] = 0x7fffffff; }
-        }
+        for (int j = 0; j < TMA; ++j) { tv[q][j] = -INFINITY; ti[q][j] = 0x7fffffff; }
+    }
 
     stage(0, 0);
     __syncthreads();
-    const double* sp = &Sh[half * DPH];
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
         if (tile + 1 < ntiles) stage(tile + 1, buf ^ 1);
         const double* pp = &Pt[buf][ci * PSTR + h * DPH];
-        f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int t = 0; t < DPH; t += 2) {
             const double2 pv = *(const double2*)(pp + t);
-            const double2 sv = *(const double2*)(sp + t);
-            acc0 = mfma4d(feat(xr[0][t + 0], sv.x, sq), pv.x, acc0);
-            acc1 = mfma4d(feat(xr[1][t + 0], sv.x, sq), pv.x, acc1);
-            acc0 = mfma4d(feat(xr[0][t + 1], sv.y, sq), pv.y, acc0);
-            acc1 = mfma4d(feat(xr[1][t + 1], sv.y, sq), pv.y, acc1);
+            acc = mfma4d(fe[t + 0], pv.x, acc);
+            acc = mfma4d(fe[t + 1], pv.y, acc);
         }
         const double c = Ct[buf][ci];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const double l0 = acc0[q] + c, l1 = acc1[q] + c;
-            lse_push(m[0][q], s[0][q], l0);
-            lse_push(m[1][q], s[1][q], l1);
-            if constexpr (TM > 0) {
-                top_push<TM>(tv[0][q], ti[0][q], l0, tile * 16 + ci);
-                top_push<TM>(tv[1][q], ti[1][q], l1, tile * 16 + ci);
-            }
+            const double l = acc[q] + c;
+            lse_push(m[q], s[q], l);
+            if constexpr (TM > 0) top_push<TM>(tv[q], ti[q], l, tile * 16 + ci);
         }
         __syncthreads();
     }
 
     // Merge the 16 lanes that hold the same rows (fixed butterfly order).
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll 1
-            for (int off = 1; off < 16; off <<= 1) {
-                const double m2 = shfl_xor_d(m[rb][q], off);
-                const float s2 = __shfl_xor(s[rb][q], off);
-                lse_merge(m[rb][q], s[rb][q], m2, s2);
-                if constexpr (TM > 0) top_merge<TM>(tv[rb][q], ti[rb][q], off);
-            }
+        for (int off = 1; off < 16; off <<= 1) {
+            const double m2 = shfl_xor_d(m[q], off);
+            const float s2 = __shfl_xor(s[q], off);
+            lse_merge(m[q], s[q], m2, s2);
+            if constexpr (TM > 0) top_merge<TM>(tv[q], ti[q], off);
         }
+    }
     if (ci == 0) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int lr = wave * 32 + rb * 16 + 4 * q + h;
-                const int64_t row = (int64_t)blockIdx.x * 128 + lr;
-                double v = 0.0;
-                if (row < n) {
-                    v = m[rb][q] + log((double)s[rb][q]);
-                    if (lse_out) lse_out[row] = v;
-                    if constexpr (TM > 0) {
-                        for (int j = 0; j < m_out; ++j) {
-                            const int sl = ti[rb][q][j];
-                            idx_out[row * m_out + j] = sl < k ? sl : -1;
-                            resp_out[row * m_out + j] = __expf((float)(tv[rb][q][j] - v));
-                        }
+        for (int q = 0; q < 4; ++q) {
+            const int lr = wave * 16 + 4 * q + h;
+            const int64_t row = (int64_t)blockIdx.x * LSE_ROWS + lr;
+            double v = 0.0;
+            if (row < n) {
+                v = m[q] + log((double)s[q]);
+                if (lse_out) lse_out[row] = v;
+                if constexpr (TM > 0) {
+                    for (int j = 0; j < m_out; ++j) {
+                        const int sl = ti[q][j];
+                        idx_out[row * m_out + j] = sl < k ? sl : -1;
+                        resp_out[row * m_out + j] = __expf((float)(tv[q][j] - v));
                     }
                 }
-                rowll[lr] = v;
             }
+            rowll[lr] = v;
+        }
     }
     __syncthreads();
-    if (tid == 0) {
-        double tot = 0.0;
-        for (int i = 0; i < 128; ++i) tot += rowll[i];
-        llpart[blockIdx.x] = (ll_accumulate ? llpart[blockIdx.x] : 0.0) + tot;
+    // Fixed-order sum of the block's rows: lane l of wave 0 adds rows l and
+    // l + 64, then a butterfly over the 64 lanes.
+    if (wave == 0) {
+        double tot = rowll[lane] + rowll[lane + 64];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) tot += shfl_xor_d(tot, off);
+        if (lane == 0) llpart[blockIdx.x] = (ll_accumulate ? llpart[blockIdx.x] : 0.0) + tot;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: statistics. Block = 4 waves; wave w owns K-tile kg*4 + w (16
+// Pass 2: statistics. Block = WV waves; wave w owns K-tile kg*WV + w (16
 // components): its coefficient rows stay in registers and its statistics in
-// fp64 MFMA accumulators. The block walks the rows of its row group in 64-row
-// tiles staged (double-buffered) in LDS in the permuted dim order.
+// fp64 MFMA accumulators. The block walks the rows of its row group in
+// 32-row tiles whose fp64 features are staged (double-buffered) in LDS as
+// feats[row][p][t] = power (1 + (p&1)) of dim 2t + (p>>1), the E-operand order,
+// so the E-step reads its A operand directly and the M-step reads a single
+// feature per MFMA. Global loads of the next tile are issued before the
+// current tile's MFMAs and written to LDS after them.
 // ---------------------------------------------------------------------------
+constexpr int STATS_ROWS = 32;  // two 16-row MFMA blocks per staged tile
+
+template <int DP>
+struct StatsGeom {
+    static constexpr int DPH = DP / 2;
+    static constexpr int HS = DPH;           // stride of one (parity, power) section
+    static constexpr int S = 4 * DPH + 10;   // row stride (doubles); see bank analysis
+    static constexpr int WV = DP <= 64 ? 8 : 4;  // 8 waves fit 256 registers each only up to 64
+    static constexpr int NT = WV * 64;
+    static constexpr int PER = (STATS_ROWS * DP + NT - 1) / NT;  // x values per thread
+};
+
 template <int DP, typename XT>
-__global__ __launch_bounds__(256, DP <= 64 ? 2 : 1)
+__global__ __launch_bounds__(StatsGeom<DP>::NT, 1)
 void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
              const double* __restrict__ Pg, const double* __restrict__ cvec,
              const double* __restrict__ shift, int ntiles, const double* __restrict__ lse,
              int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
              int accumulate) {
-    constexpr int DPH = DP / 2;
-    constexpr int XS = DP + 4;  // LDS row stride (floats)
-    constexpr int NJ = DP / 16; // 16-dim column blocks per power
-    __shared__ __attribute__((aligned(16))) float xs[2][64 * XS];
-    __shared__ __attribute__((aligned(16))) double Sh[DP];
-    __shared__ double ls[2][64];
+    using G = StatsGeom<DP>;
+    constexpr int DPH = G::DPH, HS = G::HS, S = G::S, WV = G::WV, NT = G::NT, PER = G::PER;
+    constexpr int NJ = DP / 16;  // 16-dim column blocks per power
+    __shared__ __attribute__((aligned(16))) double fs[2][STATS_ROWS * S];
+    __shared__ double ls[2][STATS_ROWS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int ci = lane & 15, h = lane >> 4, half = h >> 1;
-    const bool sq = h & 1;
-    const int kgroups = ntiles >> 2;
+    const int ci = lane & 15, h = lane >> 4;
+    const int kgroups = ntiles / WV;
     const int g = blockIdx.x / kgroups;
-    const int tile = (blockIdx.x % kgroups) * 4 + wave;
+    const int tile = (blockIdx.x % kgroups) * WV + wave;
     const int slot = tile * 16 + ci;
 
     // Stationary coefficients: P[slot][h][t], t = 0..DPH-1.
@@ -401,14 +408,6 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         }
     }
     const double cc = cvec[slot];
-    for (int i = tid; i < DP; i += 256) Sh[i] = shift[i];
-    // Shift of dims 16j + ci for the M-step features.
-    double tm[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int dd = 16 * j + ci;
-        tm[j] = shift[(dd & 1) * DPH + (dd >> 1)];
-    }
 
     f64x4 acc[2 * NJ];
 #pragma unroll
@@ -418,66 +417,89 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int64_t gr0 = (int64_t)g * rows_per_group;
     int64_t gr1 = gr0 + rows_per_group;
     if (gr1 > n) gr1 = n;
-    const int64_t ntile_rows = gr1 > gr0 ? (gr1 - gr0 + 63) / 64 : 0;
+    const int64_t ntile_rows = gr1 > gr0 ? (gr1 - gr0 + STATS_ROWS - 1) / STATS_ROWS : 0;
 
-    auto stage = [&](int64_t it, int buf) {
-        const int64_t rbase = gr0 + it * 64;
-        for (int i = tid; i < 64 * DP; i += 256) {
-            const int r = i / DP, dd = i % DP;
+    // Staging: thread tid handles elements tid + NT*i of the tile's
+    // STATS_ROWS x DP values (row-major, coalesced global reads).
+    float xv[PER];
+    double lv = 0.0;
+    auto load = [&](int64_t it) {
+        const int64_t rbase = gr0 + it * STATS_ROWS;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + NT * i;
+            const int r = e / DP, dd = e % DP;
             const int64_t row = rbase + r;
-            float v = 0.0f;
-            if (row < gr1 && dd < d) v = load_x(x + row * ldx + dd);
-            xs[buf][r * XS + (dd & 1) * DPH + (dd >> 1)] = v;
+            xv[i] = (e < STATS_ROWS * DP && row < gr1 && dd < d) ? load_x(x + row * ldx + dd) : 0.0f;
         }
-        if (tid < 64) {
+        if (tid < STATS_ROWS) {
             const int64_t row = rbase + tid;
-            ls[buf][tid] = row < gr1 ? lse[row] : INFINITY;
+            lv = row < gr1 ? lse[row] : INFINITY;
         }
     };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + NT * i;
+            if (e < STATS_ROWS * DP) {
+                const int r = e / DP, dd = e % DP;
+                const int pp = 2 * (dd & 1), t = dd >> 1;
+                const double a = (double)xv[i] - shift[(dd & 1) * DPH + t];
+                fs[buf][r * S + pp * HS + t] = a;
+                fs[buf][r * S + (pp + 1) * HS + t] = a * a;
+            }
+        }
+        if (tid < STATS_ROWS) ls[buf][tid] = lv;
+    };
 
-    if (ntile_rows > 0) stage(0, 0);
+    if (ntile_rows > 0) {
+        load(0);
+        store(0);
+    }
     __syncthreads();
-    const double* sa = &Sh[half * DPH];
     for (int64_t it = 0; it < ntile_rows; ++it) {
         const int buf = it & 1;
-        if (it + 1 < ntile_rows) stage(it + 1, buf ^ 1);
-        const float* xb = xs[buf];
-#pragma unroll 1
-        for (int rb = 0; rb < 4; ++rb) {
-            // E-step: register q of lane (h, ci) -> l[row 16rb + 4q + h][slot].
-            const float* xa = xb + (rb * 16 + ci) * XS + half * DPH;
-            f64x4 e = {0.0, 0.0, 0.0, 0.0};
+        const bool more = it + 1 < ntile_rows;
+        if (more) load(it + 1);
+        const double* fb = fs[buf];
+        // E-step for both 16-row blocks as two independent MFMA chains:
+        // register q of lane (h, ci) of chain rb -> l[row 16rb + 4q + h][slot].
+        const double* fa0 = fb + ci * S + h * HS;
+        const double* fa1 = fa0 + 16 * S;
+        f64x4 e0 = {0.0, 0.0, 0.0, 0.0}, e1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int t = 0; t < DPH; t += 4) {
-                const float4 xv = *(const float4*)(xa + t);
-                const double2 s0 = *(const double2*)(sa + t);
-                const double2 s1 = *(const double2*)(sa + t + 2);
-                e = mfma4d(feat(xv.x, s0.x, sq), pr[t + 0], e);
-                e = mfma4d(feat(xv.y, s0.y, sq), pr[t + 1], e);
-                e = mfma4d(feat(xv.z, s1.x, sq), pr[t + 2], e);
-                e = mfma4d(feat(xv.w, s1.y, sq), pr[t + 3], e);
-            }
-            double r[4];
+        for (int t = 0; t < DPH; t += 2) {
+            const double2 f0 = *(const double2*)(fa0 + t);
+            const double2 f1 = *(const double2*)(fa1 + t);
+            e0 = mfma4d(f0.x, pr[t + 0], e0);
+            e1 = mfma4d(f1.x, pr[t + 0], e1);
+            e0 = mfma4d(f0.y, pr[t + 1], e0);
+            e1 = mfma4d(f1.y, pr[t + 1], e1);
+        }
+        double r[2][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            r[0][q] = (double)__expf((float)(e0[q] + cc - ls[buf][4 * q + h]));
+            r[1][q] = (double)__expf((float)(e1[q] + cc - ls[buf][16 + 4 * q + h]));
+            n64 += r[0][q];
+            n64 += r[1][q];
+        }
+        // M-step: A = r (component ci, row 16rb + 4q + h), B = feature
+        // column 16j + ci of that row (a, then a^2).
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const double l = e[q] + cc;
-                r[q] = (double)__expf((float)(l - ls[buf][rb * 16 + 4 * q + h]));
-                n64 += r[q];
-            }
-            // M-step: A = r (component ci, row 4q+h), B = feature column
-            // 16j + ci of that row.
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float* xm = xb + (rb * 16 + 4 * q + h) * XS;
+                const double* fm = fb + (rb * 16 + 4 * q + h) * S;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const int dd = 16 * j + ci;
-                    const double a = (double)xm[(dd & 1) * DPH + (dd >> 1)] - tm[j];
-                    acc[j] = mfma4d(r[q], a, acc[j]);
-                    acc[NJ + j] = mfma4d(r[q], a * a, acc[NJ + j]);
+                    const double a = fm[2 * (dd & 1) * HS + (dd >> 1)];
+                    acc[j] = mfma4d(r[rb][q], a, acc[j]);
+                    acc[NJ + j] = mfma4d(r[rb][q], a * a, acc[NJ + j]);
                 }
             }
-        }
+        if (more) store(buf ^ 1);
         __syncthreads();
     }
 
@@ -559,9 +581,9 @@ template <int DP, typename XT, int TM>
 static hipError_t launch_lse_tm(const Plan& pl, const void* x, int64_t n, int64_t ldx,
                                 double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
                                 hipStream_t st) {
-    const int64_t blocks = (n + 127) / 128;
+    const int64_t blocks = (n + LSE_ROWS - 1) / LSE_ROWS;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_lse<DP, XT, TM>), dim3((unsigned)blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_lse<DP, XT, TM>), dim3((unsigned)blocks), dim3(LSE_WAVES * 64), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse_out,
                        pl.llpart, ll_acc, pl.k, m, idx, resp);
     return hipGetLastError();
@@ -579,9 +601,10 @@ static hipError_t launch_lse_t(const Plan& pl, const void* x, int64_t n, int64_t
 template <int DP, typename XT>
 static hipError_t launch_stats_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
                                  const double* lse, int acc, hipStream_t st) {
-    int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + 63) / 64 * 64;
-    if (rpg < 64) rpg = 64;
-    hipLaunchKernelGGL((k_stats<DP, XT>), dim3(pl.ngroups * (pl.ntiles / 4)), dim3(256), 0, st,
+    using G = StatsGeom<DP>;
+    int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
+    if (rpg < STATS_ROWS) rpg = STATS_ROWS;
+    hipLaunchKernelGGL((k_stats<DP, XT>), dim3(pl.ngroups * (pl.ntiles / G::WV)), dim3(G::NT), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, rpg,
                        pl.part, pl.npart, acc);
     return hipGetLastError();
