@@ -26,6 +26,31 @@ if ROOT not in sys.path:
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense FP32 matrix peak (the metric's reference)
 PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (the contractions' own dtype)
 
+# HBM bytes per launch of the statistics kernel on the headline workload, from
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this bench (profiles/
+# k_stats_descriptor_n10M_d96_k1024_hbm.md), each scaled by what the counter
+# reads for a plain 3.84 GB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0).
+# Keyed by the kernels' source hash: a changed kernel reports null until it
+# is profiled again.
+MEASURED_TRAFFIC = {
+    "890927928625f41d": {"workload": "descriptor", "bytes_per_launch": 1.5268e9},
+}
+
+
+def _kernel_hash() -> str:
+    import hashlib
+
+    path = os.path.join(ROOT, "gmm_em_amd", "csrc", "gmm_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(workload: str, launches_per_step: float):
+    rec = MEASURED_TRAFFIC.get(_kernel_hash())
+    if rec is None or rec["workload"] != workload or launches_per_step != 3:
+        return None
+    return rec["bytes_per_launch"]
+
 
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -34,7 +59,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="descriptor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=100_000)
+    ap.add_argument("--cpu-rows", type=int, default=3_000_000)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of the data matrix's size (calibrates the "
+                         "HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the fused EM step runs on a single MI355X; "
@@ -48,6 +76,16 @@ def main() -> int:
     from gmm_em_amd import ops
 
     W = dg.WORKLOADS[args.workload]
+    if args.copy_probe:
+        nbytes = W.n * W.d * (2 if W.dtype == "bf16" else 4)
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
+                          "copies": 3}), flush=True)
+        return 0
     t0 = time.time()
     x = dg.rows(W)
     w0, m0, v0 = dg.init_params(W, x)
@@ -111,7 +149,7 @@ def main() -> int:
         "peak": PEAK_FP64_MFMA_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP64_MFMA_TFLOPS, 4),
-        "traffic": None,
+        "traffic": _traffic(W.key, launches_per_step),
         "avg_launch_ms": round(avg_ms, 4),
         "launches_per_step": launches_per_step,
         "alg_flops_per_launch": alg_flops_launch,

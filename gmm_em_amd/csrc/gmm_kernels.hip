@@ -111,20 +111,27 @@ __global__ void k_validate(const float* __restrict__ w, const float* __restrict_
     if (anypos) atomicOr(&status[1], 1);
 }
 
-// Shift s_d = rint(mean_k mu[k][d]), stored in the permuted dim order used by
-// the kernels: pos(d) = (d & 1) * DP/2 + d / 2 (even dims, then odd dims).
+// Shift s_d = rint(mean_k mu[k][d]) (one block per dim, fixed-order fp64
+// sum), stored in the permuted dim order used by the kernels:
+// pos(d) = (d & 1) * DP/2 + d / 2 (even dims, then odd dims).
 __global__ void k_shift(const float* __restrict__ mu, int k, int d, int dp,
                         double* __restrict__ shift) {
-    const int dd = blockIdx.x * blockDim.x + threadIdx.x;
-    if (dd >= dp) return;
-    double sv = 0.0;
-    if (dd < d) {
-        double acc = 0.0;
-        for (int j = 0; j < k; ++j) acc += (double)mu[(int64_t)j * d + dd];
-        sv = rint(acc / (double)k);
-        if (!isfinite(sv)) sv = 0.0;
+    __shared__ double red[256];
+    const int dd = blockIdx.x;
+    double acc = 0.0;
+    if (dd < d)
+        for (int j = threadIdx.x; j < k; j += 256) acc += (double)mu[(int64_t)j * d + dd];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int sft = 128; sft > 0; sft >>= 1) {
+        if (threadIdx.x < sft) red[threadIdx.x] += red[threadIdx.x + sft];
+        __syncthreads();
     }
-    shift[(dd & 1) * (dp >> 1) + (dd >> 1)] = sv;
+    if (threadIdx.x == 0) {
+        double sv = dd < d ? rint(red[0] / (double)k) : 0.0;
+        if (!isfinite(sv)) sv = 0.0;
+        shift[(dd & 1) * (dp >> 1) + (dd >> 1)] = sv;
+    }
 }
 
 // Coefficients of slot `blockIdx.x` (component = slot when slot < k, else
@@ -392,8 +399,14 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int lane = tid & 63, wave = tid >> 6;
     const int ci = lane & 15, h = lane >> 4;
     const int kgroups = ntiles / WV;
-    const int g = blockIdx.x / kgroups;
-    const int tile = (blockIdx.x % kgroups) * WV + wave;
+    // Workgroups are dispatched to the 8 XCDs round-robin by index. Remap so
+    // that the blocks of one XCD take consecutive (row group, K-group) pairs:
+    // all K-groups of a row group then run on one XCD and share its L2 copy
+    // of each row tile instead of fetching it from HBM once per XCD.
+    const int nb = gridDim.x;
+    const int o = (nb % 8 == 0) ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int g = o / kgroups;
+    const int tile = (o % kgroups) * WV + wave;
     const int slot = tile * 16 + ci;
 
     // Stationary coefficients: P[slot][h][t], t = 0..DPH-1.
@@ -647,8 +660,7 @@ hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, cons
     int vb = (int)((total + 255) / 256);
     if (vb > 1024) vb = 1024;
     hipLaunchKernelGGL(k_validate, dim3(vb), dim3(256), 0, st, w, mu, var, pl.k, pl.d, pl.status);
-    hipLaunchKernelGGL(k_shift, dim3((pl.dp + 63) / 64), dim3(64), 0, st, mu, pl.k, pl.d, pl.dp,
-                       pl.shift);
+    hipLaunchKernelGGL(k_shift, dim3(pl.dp), dim3(256), 0, st, mu, pl.k, pl.d, pl.dp, pl.shift);
     hipLaunchKernelGGL(k_params, dim3(pl.kp), dim3(128), 0, st, w, mu, var, pl.k, pl.d, pl.dp,
                        pl.shift, pl.Pg, pl.cvec);
     return hipGetLastError();
