@@ -225,3 +225,66 @@ def test_bf16_input(ops):
     rw, rmu, rv, rL, nk = oracle.em_step(x, w0, m0, v0)
     assert rel(Lg, rL) <= 1e-5
     assert_params_close(_host(w, mu, var), (rw, rmu, rv), nk, len(x), 5e-3, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# Full-size checks on the headline workload, in the configuration bench.py
+# times (N = 10,000,000 rows, D = 96, K = 1024, three 2^22-row chunks).
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def descriptor_full():
+    W = dg.WORKLOADS["descriptor"]
+    x = dg.rows(W)
+    w0, m0, v0 = dg.init_params(W, x)
+    return W, x, w0, m0, v0
+
+
+def test_descriptor_full_first_step_matches_oracle(ops, descriptor_full):
+    W, x, w0, m0, v0 = descriptor_full
+    xt, w, mu, var = _to_dev(x, w0, m0, v0)
+    Lg = _gpu_step(ops, xt, w, mu, var, W.var_floor)
+    rw, rmu, rv, rL, nk = oracle.em_step(x, w0, m0, v0, W.var_floor)
+    assert rel(Lg, rL) <= 1e-5
+    e = assert_params_close(_host(w, mu, var), (rw, rmu, rv), nk, len(x), 1e-4, "descriptor full step 0")
+    print("descriptor full-size step 0:", e, "loglik rel", rel(Lg, rL))
+    assert abs(float(w.sum().item()) - 1.0) < 1e-5
+
+
+def test_descriptor_full_loglik_rows_and_topm_sampled(ops, descriptor_full):
+    W, x, w0, m0, v0 = descriptor_full
+    xt, w, mu, var = _to_dev(x, w0, m0, v0)
+    ws = ops.workspace(W.d, W.k, DEV)
+    for _ in range(2):  # move away from the initial parameters
+        ops.em_step(xt, w, mu, var, W.var_floor, ws=ws)
+    th = _host(w, mu, var)
+    tot, rows = ops.loglik(xt, w, mu, var, per_row=True, ws=ws)
+    idx, resp = ops.assign_topm(xt, w, mu, var, 2, ws=ws)
+    torch.cuda.synchronize()
+    g = rows.cpu().numpy()
+    # the total is the fixed-order sum of the rows; the rows span all chunks
+    assert rel(tot.item(), float(np.sum(g))) <= 1e-9
+    rng = np.random.default_rng(123)
+    pick = np.sort(rng.choice(len(x), 4000, replace=False))
+    pick[-1] = len(x) - 1  # the ragged tail of the last chunk
+    rL, rrows = oracle.loglik(x[pick], *th, per_row=True)
+    np.testing.assert_allclose(g[pick], rrows, rtol=1e-6, atol=1e-6)
+    ridx, rresp, gap = oracle.topm(x[pick], *th, 2)
+    ell_top = np.abs(np.log(np.maximum(rresp[:, 0], 1e-300)))
+    _check_topm(idx.cpu().numpy()[pick], resp.cpu().numpy()[pick], ridx, rresp, gap, ell_top)
+
+
+def test_bf16_large_prefix_per_step(ops):
+    W = dg.WORKLOADS["bf16_large"]
+    x = dg.rows(W, 60_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    xt = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    w, mu, var = _to_dev(w0, m0, v0)
+    ws = ops.workspace(W.d, W.k, DEV)
+    for t in range(2):
+        th = _host(w, mu, var)
+        Lg = _gpu_step(ops, xt, w, mu, var, W.var_floor, ws)
+        rw, rmu, rv, rL, nk = oracle.em_step(x, *th, W.var_floor)
+        assert rel(Lg, rL) <= 1e-5
+        # bf16 data: the 5e-3 bar applies; the arithmetic itself is fp64
+        e = assert_params_close(_host(w, mu, var), (rw, rmu, rv), nk, len(x), 5e-3, f"bf16_large step {t}")
+        print(f"bf16_large prefix step {t}:", e)
