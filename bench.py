@@ -33,7 +33,8 @@ PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (the contractions
 # Keyed by the kernels' source hash: a changed kernel reports null until it
 # is profiled again.
 MEASURED_TRAFFIC = {
-    "890927928625f41d": {"workload": "descriptor", "bytes_per_launch": 1.5268e9},
+    "890927928625f41d": {"workload": "descriptor", "kernel": "k_stats (pass 2)",
+                         "bytes_per_launch": 1.5268e9},
 }
 
 
@@ -45,9 +46,9 @@ def _kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(workload: str, launches_per_step: float):
+def _traffic(workload: str, kernel: str):
     rec = MEASURED_TRAFFIC.get(_kernel_hash())
-    if rec is None or rec["workload"] != workload or launches_per_step != 3:
+    if rec is None or rec["workload"] != workload or rec["kernel"] != kernel:
         return None
     return rec["bytes_per_launch"]
 
@@ -131,10 +132,13 @@ def main() -> int:
     tflops = flops_step * its / 1e12
     hist = ll[: args.steps].cpu().numpy()
 
-    # dominant kernel: the pass with the larger summed time
+    # dominant kernel: the pass with the larger summed time (in the
+    # cooperative single-pass schedule there is no pass 1 and the one kernel
+    # does both contractions)
     (ms1, n1), (ms2, n2) = prof["pass1"], prof["pass2"]
     if ms2 >= ms1:
-        kname, kms, kn, kflops = "k_stats (pass 2)", ms2, n2, 8.0 * W.d * W.k
+        kname = "k_stats (pass 2)" if n1 > 0 else "k_coop (single pass)"
+        kms, kn, kflops = ms2, n2, 8.0 * W.d * W.k
     else:
         kname, kms, kn, kflops = "k_lse (pass 1)", ms1, n1, 4.0 * W.d * W.k
     rows_per_launch = min(W.n, 1 << 22) if W.n > (1 << 22) else W.n
@@ -149,7 +153,8 @@ def main() -> int:
         "peak": PEAK_FP64_MFMA_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP64_MFMA_TFLOPS, 4),
-        "traffic": _traffic(W.key, launches_per_step),
+        "traffic": _traffic(W.key, kname),
+        "schedule": "two-pass" if n1 > 0 else "cooperative single pass",
         "avg_launch_ms": round(avg_ms, 4),
         "launches_per_step": launches_per_step,
         "alg_flops_per_launch": alg_flops_launch,

@@ -5,6 +5,8 @@
 #include <stdint.h>
 
 #include <new>
+#include <stdlib.h>
+#include <string.h>
 
 #include "gmm_em.h"
 #include "gmm_internal.h"
@@ -22,7 +24,8 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     p.k = k;
     p.kp = (k + 127) / 128 * 128;  // whole 8-tile groups of the statistics pass
     p.ntiles = p.kp / 16;
-    const int kgroups = p.ntiles / (p.dp <= 64 ? 8 : 4);
+    const int kgroups = p.ntiles / waves_per_stats_block(p.dp);
+    p.kgroups = kgroups;
     int g = (1024 + kgroups - 1) / kgroups;
     p.ngroups = g < 1 ? 1 : (g > 512 ? 512 : g);
     size_t off = 0;
@@ -40,6 +43,8 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     const size_t o_np = take((size_t)p.ngroups * p.kp * sizeof(double));
     const size_t o_part = take((size_t)p.ngroups * p.kp * 2 * p.dp * sizeof(double));
     const size_t o_lt = take(sizeof(double));
+    const size_t o_xb = take((size_t)p.ngroups * 4 * kgroups * 32 * sizeof(double2));
+    const size_t o_cnt = take((size_t)p.ngroups * kgroups * sizeof(unsigned));
     p.bytes = off;
     if (ws) {
         char* b = (char*)ws;
@@ -52,6 +57,8 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
         p.npart = (double*)(b + o_np);
         p.part = (double*)(b + o_part);
         p.ll_tmp = (double*)(b + o_lt);
+        p.xbuf = (double2*)(b + o_xb);
+        p.counters = (unsigned*)(b + o_cnt);
     }
     *pl = p;
     return true;
@@ -124,6 +131,41 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
     return hipSuccess;
 }
 
+// Schedule of the EM step. The default is the two-pass schedule; the
+// cooperative single pass (GMM_EM_SCHEDULE=coop) removes the normaliser
+// pass but pays a cross-workgroup exchange per 32-row tile, which measured
+// slower on MI355X at the headline shape (321 vs 217 ms per step at N=1e7,
+// D=96, K=1024). coop fails with GMM_E_UNSUPPORTED where the grid cannot be
+// co-resident.
+enum { SCHED_TWO_PASS = 1, SCHED_COOP = 2 };
+
+static int schedule_choice() {
+    const char* v = getenv("GMM_EM_SCHEDULE");
+    if (v && !strcmp(v, "coop")) return SCHED_COOP;
+    return SCHED_TWO_PASS;
+}
+
+// Row groups of the cooperative pass for the current device, or 0 if it
+// cannot run: every block must be co-resident, and each XCD (8 of them,
+// workgroups dispatched round-robin) must hold whole row groups.
+static int coop_groups(const Plan& pl) {
+    static int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev != cached_dev) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess || !prop.cooperativeLaunch) return 0;
+        cached_cus = prop.multiProcessorCount;
+        cached_dev = dev;
+    }
+    const int bpc = coop_blocks_per_cu(pl.dp);
+    if (bpc < 1 || pl.kgroups < 1 || pl.kgroups > 64) return 0;  // one wave watches the flags
+    int groups = (cached_cus * bpc) / pl.kgroups;
+    groups = groups / 8 * 8;
+    if (groups > pl.ngroups) groups = pl.ngroups / 8 * 8;
+    return groups >= 8 ? groups : 0;
+}
+
 static int ll_parts(int64_t n) {
     const int64_t first = n < CHUNK_ROWS ? n : CHUNK_ROWS;
     return (int)((first + LL_ROWS - 1) / LL_ROWS);
@@ -145,10 +187,27 @@ int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtyp
     if (rc) return rc;
     if (n < 1 || !(var_floor >= 0.0f) || !isfinite(var_floor)) return GMM_E_INVALID;
     hipStream_t st = (hipStream_t)stream;
+    const int sched = schedule_choice();
+    const int cg = sched == SCHED_TWO_PASS ? 0 : coop_groups(pl);
+    if (sched == SCHED_COOP && cg == 0) return GMM_E_UNSUPPORTED;
+    double* ll_out = loglik_dev ? loglik_dev : pl.ll_tmp;
     hipError_t e = launch_prologue(pl, weights, means, variances, st);
-    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, true, st);
-    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(n), loglik_dev ? loglik_dev : pl.ll_tmp, st);
-    if (e == hipSuccess) e = launch_finalize(pl, n, var_floor, weights, means, variances, st);
+    if (e != hipSuccess) return GMM_E_HIP;
+    if (cg > 0) {
+        prof_mark(2, true, st);
+        e = launch_coop(pl, x, n, ldx, x_dtype, cg, st);
+        prof_mark(2, false, st);
+        if (e == hipSuccess) {
+            e = launch_ll_final(pl, cg, ll_out, st);
+            if (e == hipSuccess) e = launch_finalize(pl, cg, n, var_floor, weights, means, variances, st);
+            return hip_status(e);
+        }
+        if (sched == SCHED_COOP) return GMM_E_HIP;
+        (void)hipGetLastError();  // fall back to the two-pass schedule
+    }
+    e = run_passes(pl, x, n, ldx, x_dtype, true, st);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(n), ll_out, st);
+    if (e == hipSuccess) e = launch_finalize(pl, pl.ngroups, n, var_floor, weights, means, variances, st);
     return hip_status(e);
 }
 
@@ -221,9 +280,10 @@ int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
 int gmm_device_status(const void* workspace, void* stream) {
     if (!workspace) return GMM_E_INVALID;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GMM_E_HIP;
-    int st[2] = {0, 0};
-    if (hipMemcpy(st, workspace, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return GMM_E_HIP;
-    return (st[0] != 0 || st[1] == 0) ? GMM_E_PARAMS : GMM_OK;
+    int st2[4] = {0, 0, 0, 0};
+    if (hipMemcpy(st2, workspace, sizeof(st2), hipMemcpyDeviceToHost) != hipSuccess) return GMM_E_HIP;
+    if (st2[2] != 0) return GMM_E_SYNC;
+    return (st2[0] != 0 || st2[1] == 0) ? GMM_E_PARAMS : GMM_OK;
 }
 
 const char* gmm_status_string(int status) {
@@ -234,7 +294,8 @@ const char* gmm_status_string(int status) {
         case GMM_E_WORKSPACE: return "workspace missing, misaligned or too small";
         case GMM_E_PARAMS: return "invalid parameter values";
         case GMM_E_HIP: return "HIP runtime error";
-        case GMM_E_UNSUPPORTED: return "shape not supported by this build";
+        case GMM_E_UNSUPPORTED: return "shape or schedule not supported by this build or device";
+        case GMM_E_SYNC: return "cooperative exchange between workgroups timed out";
         default: return "unknown status";
     }
 }

@@ -31,6 +31,9 @@ struct Plan {
     double* npart = nullptr;   // [ngroups][kp] responsibility mass partials
     double* part = nullptr;    // [ngroups][kp][2*dp] first/second moment partials
     double* ll_tmp = nullptr;  // [1] scratch total
+    double2* xbuf = nullptr;   // [ngroups][4][kgroups][32] cooperative exchange slots
+    unsigned* counters = nullptr;  // [ngroups][kgroups] cooperative progress flags
+    int kgroups = 0;           // K-groups of the statistics pass (blocks per row group)
 };
 
 bool make_plan(int d, int k, void* ws, Plan* pl);
@@ -44,8 +47,14 @@ hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int
                       hipStream_t st);
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                         const double* lse, int acc, hipStream_t st);
-hipError_t launch_finalize(const Plan& pl, int64_t n, float var_floor, float* w, float* mu,
-                           float* var, hipStream_t st);
+hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floor, float* w,
+                           float* mu, float* var, hipStream_t st);
+// Cooperative single pass over all n rows with `groups` row groups (every
+// block co-resident); fails if the grid cannot be co-resident.
+hipError_t launch_coop(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                       int groups, hipStream_t st);
+int coop_blocks_per_cu(int dp);
+int waves_per_stats_block(int dp);
 hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st);
 
 }  // namespace gmm

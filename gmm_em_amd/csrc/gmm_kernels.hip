@@ -535,6 +535,278 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 }
 
 // ---------------------------------------------------------------------------
+// Cooperative single pass: the statistics pass with the normaliser computed
+// in flight. The KG blocks of a row group (one per K-group of WV K-tiles) are
+// co-resident (cooperative launch) and on one XCD (block order remapped as in
+// k_stats), walk the same 32-row tiles, and exchange per-row partial
+// logsumexp pairs (max, scaled sum) over their components through a small
+// buffer in L2, so no pass recomputes the E-step. Per tile:
+//   E-step of tile it+1 (registers) -> block partial per row -> publish
+//   (release-store: flag[g][kg] = it+2) -> wait until every flag[g][*] >= it+1
+//   (acquire) -> merge the KG partials of tile it in fixed order (every block
+//   gets the same lse) -> M-step of tile it.
+// Each block has its own progress flag: a shared count would be reached by
+// blocks running ahead before a slow block has published.
+// A block can run two tiles ahead of a reader, so partials rotate over four
+// slots. Waits are bounded: a timeout sets status[2] and every block stops
+// waiting (results are then invalid and reported by gmm_device_status).
+// ---------------------------------------------------------------------------
+constexpr int COOP_SLOTS = 4;
+
+__global__ void k_zero_u32(unsigned* p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+template <int DP, typename XT>
+__global__ __launch_bounds__(StatsGeom<DP>::NT, 1)
+void k_coop(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
+            const double* __restrict__ Pg, const double* __restrict__ cvec,
+            const double* __restrict__ shift, int ntiles, int64_t rows_per_group,
+            double* __restrict__ part, double* __restrict__ npart, double2* __restrict__ xbuf,
+            unsigned* __restrict__ flags, double* __restrict__ llpart, int* __restrict__ status,
+            int spin_limit) {
+    using G = StatsGeom<DP>;
+    constexpr int DPH = G::DPH, HS = G::HS, S = G::S, WV = G::WV, NT = G::NT, PER = G::PER;
+    constexpr int NJ = DP / 16;
+    __shared__ __attribute__((aligned(16))) double fs[2][STATS_ROWS * S];
+    __shared__ double ls[STATS_ROWS];
+    __shared__ double2 wpart[WV][STATS_ROWS];
+    __shared__ int abort_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int ci = lane & 15, h = lane >> 4;
+    const int kgroups = ntiles / WV;
+    const int nb = gridDim.x;
+    const int o = (nb % 8 == 0) ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int g = o / kgroups;
+    const int kg = o % kgroups;
+    const int tile = kg * WV + wave;
+    const int slot = tile * 16 + ci;
+
+    double pr[DPH];
+    {
+        const double* src = Pg + (int64_t)slot * 2 * DP + h * DPH;
+#pragma unroll
+        for (int t = 0; t < DPH; t += 2) {
+            const double2 v = *(const double2*)(src + t);
+            pr[t] = v.x;
+            pr[t + 1] = v.y;
+        }
+    }
+    const double cc = cvec[slot];
+    f64x4 acc[2 * NJ];
+#pragma unroll
+    for (int j = 0; j < 2 * NJ; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    double n64 = 0.0, ll = 0.0;
+    if (tid == 0) abort_flag = 0;
+    __syncthreads();
+
+    const int64_t gr0 = (int64_t)g * rows_per_group;
+    int64_t gr1 = gr0 + rows_per_group;
+    if (gr1 > n) gr1 = n;
+    const int64_t T = gr1 > gr0 ? (gr1 - gr0 + STATS_ROWS - 1) / STATS_ROWS : 0;
+    double2* gx = xbuf + (int64_t)g * COOP_SLOTS * kgroups * STATS_ROWS;
+
+    float xv[PER];
+    auto load = [&](int64_t it) {
+        const int64_t rbase = gr0 + it * STATS_ROWS;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + NT * i;
+            const int r = e / DP, dd = e % DP;
+            const int64_t row = rbase + r;
+            xv[i] = (e < STATS_ROWS * DP && row < gr1 && dd < d) ? load_x(x + row * ldx + dd) : 0.0f;
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + NT * i;
+            if (e < STATS_ROWS * DP) {
+                const int r = e / DP, dd = e % DP;
+                const int pp = 2 * (dd & 1), t = dd >> 1;
+                const double a = (double)xv[i] - shift[(dd & 1) * DPH + t];
+                fs[buf][r * S + pp * HS + t] = a;
+                fs[buf][r * S + (pp + 1) * HS + t] = a * a;
+            }
+        }
+    };
+    // E-step of the tile in fs[buf]: ell[rb] register q <- l[row 16rb+4q+h][slot].
+    auto estep = [&](int buf, f64x4 (&ell)[2]) {
+        const double* fa0 = fs[buf] + ci * S + h * HS;
+        const double* fa1 = fa0 + 16 * S;
+        f64x4 e0 = {0.0, 0.0, 0.0, 0.0}, e1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int t = 0; t < DPH; t += 2) {
+            const double2 f0 = *(const double2*)(fa0 + t);
+            const double2 f1 = *(const double2*)(fa1 + t);
+            e0 = mfma4d(f0.x, pr[t + 0], e0);
+            e1 = mfma4d(f1.x, pr[t + 0], e1);
+            e0 = mfma4d(f0.y, pr[t + 1], e0);
+            e1 = mfma4d(f1.y, pr[t + 1], e1);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            e0[q] += cc;
+            e1[q] += cc;
+        }
+        ell[0] = e0;
+        ell[1] = e1;
+    };
+    // Block partial (max, scaled sum) of each row over this block's
+    // components, written to the exchange slot of tile `it`, then released.
+    auto publish = [&](const f64x4 (&ell)[2], int64_t it) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                double m = ell[rb][q];
+                float sm = 1.0f;
+                if (!(m > -1.0e300)) {  // padding component: contributes nothing
+                    m = -1.0e300;
+                    sm = 0.0f;
+                }
+#pragma unroll 1
+                for (int off = 1; off < 16; off <<= 1) {
+                    const double m2 = shfl_xor_d(m, off);
+                    const float s2 = __shfl_xor(sm, off);
+                    lse_merge(m, sm, m2, s2);
+                }
+                if (ci == 0) wpart[wave][rb * 16 + 4 * q + h] = double2{m, (double)sm};
+            }
+        __syncthreads();
+        // Message passing without cache-wide fences: wave 0 writes the
+        // partials with device-scope stores (they bypass the non-coherent L1),
+        // drains them (s_waitcnt 0), then stores the flag; readers load the
+        // flag and then the partials with device-scope loads.
+        if (tid < STATS_ROWS) {
+            double m = wpart[0][tid].x;
+            float sm = (float)wpart[0][tid].y;
+            for (int w2 = 1; w2 < WV; ++w2) lse_merge(m, sm, wpart[w2][tid].x, (float)wpart[w2][tid].y);
+            double* dst = (double*)&gx[((it % COOP_SLOTS) * kgroups + kg) * STATS_ROWS + tid];
+            __hip_atomic_store(dst, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dst + 1, (double)sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (wave == 0) {
+            __builtin_amdgcn_s_waitcnt(0);
+            if (lane == 0)
+                __hip_atomic_store(&flags[(int64_t)g * kgroups + kg], (unsigned)(it + 1),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    // Wave 0 waits until every block of the row group has published tile
+    // `it` (lane j watches block j's flag).
+    auto wait_and_lse = [&](int64_t it) {
+        if (wave == 0) {
+            const unsigned target = (unsigned)(it + 1);
+            const unsigned* fl = flags + (int64_t)g * kgroups;
+            int spins = 0;
+            while (!abort_flag) {
+                bool ok = true;
+                if (lane < kgroups)
+                    ok = __hip_atomic_load(&fl[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+                if (__all(ok)) break;
+                if (++spins > spin_limit ||
+                    __hip_atomic_load(&status[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                    if (lane == 0) {
+                        abort_flag = 1;
+                        __hip_atomic_fetch_or(&status[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __syncthreads();
+        if (tid < STATS_ROWS) {
+            const double* src = (const double*)(gx + (it % COOP_SLOTS) * kgroups * STATS_ROWS + tid);
+            double m = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float sm = (float)__hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int k2 = 1; k2 < kgroups; ++k2) {
+                const double* p2 = src + 2 * k2 * STATS_ROWS;
+                const double m2 = __hip_atomic_load(p2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const double s2 = __hip_atomic_load(p2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lse_merge(m, sm, m2, (float)s2);
+            }
+            const int64_t row = gr0 + it * STATS_ROWS + tid;
+            const double v = m + log((double)sm);
+            ls[tid] = row < gr1 ? v : INFINITY;
+            wpart[0][tid].x = row < gr1 ? v : 0.0;  // for the log-likelihood sum
+        }
+        __syncthreads();
+        if (kg == 0 && tid == 0)
+            for (int r2 = 0; r2 < STATS_ROWS; ++r2) ll += wpart[0][r2].x;
+    };
+    auto mstep = [&](int buf, const f64x4 (&ell)[2]) {
+        const double* fb = fs[buf];
+        double r[2][4];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                r[rb][q] = (double)__expf((float)(ell[rb][q] - ls[rb * 16 + 4 * q + h]));
+                n64 += r[rb][q];
+            }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double* fm = fb + (rb * 16 + 4 * q + h) * S;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int dd = 16 * j + ci;
+                    const double a = fm[2 * (dd & 1) * HS + (dd >> 1)];
+                    acc[j] = mfma4d(r[rb][q], a, acc[j]);
+                    acc[NJ + j] = mfma4d(r[rb][q], a * a, acc[NJ + j]);
+                }
+            }
+    };
+
+    f64x4 ecur[2], enext[2];
+    enext[0] = enext[1] = f64x4{0.0, 0.0, 0.0, 0.0};
+    if (T > 0) {
+        load(0);
+        store(0);
+        if (T > 1) {
+            load(1);
+            store(1);
+        }
+        __syncthreads();
+        estep(0, ecur);
+        publish(ecur, 0);
+    }
+    for (int64_t it = 0; it < T; ++it) {
+        const int buf = it & 1;
+        if (it + 2 < T) load(it + 2);
+        if (it + 1 < T) {
+            estep(buf ^ 1, enext);
+            publish(enext, it + 1);
+        }
+        wait_and_lse(it);
+        mstep(buf, ecur);
+        __syncthreads();
+        if (it + 2 < T) store(buf);
+        __syncthreads();
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) ecur[rb] = enext[rb];
+    }
+
+    n64 += shfl_xor_d(n64, 16);
+    n64 += shfl_xor_d(n64, 32);
+    const int64_t gbase = (int64_t)g * ntiles * 16;
+    if (h == 0) npart[gbase + slot] = n64;
+#pragma unroll
+    for (int j = 0; j < 2 * NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int comp = tile * 16 + 4 * q + h;
+            part[(gbase + comp) * (2 * DP) + 16 * j + ci] = acc[j][q];
+        }
+    if (kg == 0 && tid == 0) llpart[g] = ll;
+}
+
+// ---------------------------------------------------------------------------
 // Finalize: fixed-order fp64 sum over row groups, then the M-step update.
 // ---------------------------------------------------------------------------
 __global__ void k_finalize(const double* __restrict__ part, const double* __restrict__ npart,
@@ -544,7 +816,7 @@ __global__ void k_finalize(const double* __restrict__ part, const double* __rest
                            const int* __restrict__ status) {
     const int comp = blockIdx.x;
     if (comp >= k) return;
-    const bool bad = status[0] != 0 || status[1] == 0;
+    const bool bad = status[0] != 0 || status[1] == 0 || status[2] != 0;
     double N = 0.0;
     for (int gg = 0; gg < ngroups; ++gg) N += npart[(int64_t)gg * kp + comp];
     const int dph = dp >> 1;
@@ -584,7 +856,7 @@ __global__ void k_ll_final(const double* __restrict__ llpart, int nparts, double
         if (threadIdx.x < sft) red[threadIdx.x] += red[threadIdx.x + sft];
         __syncthreads();
     }
-    if (threadIdx.x == 0) *out = (status[0] != 0 || status[1] == 0) ? NAN : red[0];
+    if (threadIdx.x == 0) *out = (status[0] != 0 || status[1] == 0 || status[2] != 0) ? NAN : red[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -653,6 +925,56 @@ hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, i
     return hipErrorInvalidValue;
 }
 
+
+template <int DP, typename XT>
+static hipError_t launch_coop_t(const Plan& pl, const void* x, int64_t n, int64_t ldx, int groups,
+                                hipStream_t st) {
+    using G = StatsGeom<DP>;
+    const int kgroups = pl.ntiles / G::WV;
+    int64_t rpg = ((n + groups - 1) / groups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
+    if (rpg < STATS_ROWS) rpg = STATS_ROWS;
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(256), 0, st, pl.counters, groups * kgroups);
+    const XT* xp = (const XT*)x;
+    int dd = pl.d, nt = pl.ntiles;
+    int spin = 1 << 22;
+    void* args[] = {(void*)&xp,      (void*)&n,         (void*)&dd,        (void*)&ldx,
+                    (void*)&pl.Pg,   (void*)&pl.cvec,   (void*)&pl.shift,  (void*)&nt,
+                    (void*)&rpg,     (void*)&pl.part,   (void*)&pl.npart,  (void*)&pl.xbuf,
+                    (void*)&pl.counters, (void*)&pl.llpart, (void*)&pl.status, (void*)&spin};
+    return hipLaunchCooperativeKernel((const void*)k_coop<DP, XT>, dim3(groups * kgroups),
+                                      dim3(G::NT), args, 0, st);
+}
+
+int coop_blocks_per_cu(int dp) {
+    int nb = 0;
+    switch (dp) {
+#define CASE(DPV)                                                                              \
+    case DPV:                                                                                  \
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_coop<DPV, float>,              \
+                                                         StatsGeom<DPV>::NT, 0) != hipSuccess) \
+            nb = 0;                                                                            \
+        break;
+        GMM_DP_CASES(CASE)
+#undef CASE
+    }
+    return nb;
+}
+
+int waves_per_stats_block(int dp) { return dp <= 64 ? StatsGeom<64>::WV : StatsGeom<128>::WV; }
+
+hipError_t launch_coop(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                       int groups, hipStream_t st) {
+    switch (pl.dp) {
+#define CASE(DPV)                                                                          \
+    case DPV:                                                                              \
+        return dtype == 0 ? launch_coop_t<DPV, float>(pl, x, n, ldx, groups, st)          \
+                          : launch_coop_t<DPV, uint16_t>(pl, x, n, ldx, groups, st);
+        GMM_DP_CASES(CASE)
+#undef CASE
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
                            hipStream_t st) {
     hipLaunchKernelGGL(k_status_reset, dim3(1), dim3(64), 0, st, pl.status);
@@ -666,9 +988,9 @@ hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, cons
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const Plan& pl, int64_t n, float var_floor, float* w, float* mu,
-                           float* var, hipStream_t st) {
-    hipLaunchKernelGGL(k_finalize, dim3(pl.k), dim3(128), 0, st, pl.part, pl.npart, pl.ngroups,
+hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floor, float* w,
+                           float* mu, float* var, hipStream_t st) {
+    hipLaunchKernelGGL(k_finalize, dim3(pl.k), dim3(128), 0, st, pl.part, pl.npart, groups,
                        pl.kp, pl.dp, pl.d, pl.k, pl.shift, n, var_floor, w, mu, var, pl.status);
     return hipGetLastError();
 }

@@ -39,7 +39,8 @@ for _f in (lib.gmm_em_step, lib.gmm_fit, lib.gmm_loglik, lib.gmm_assign_topm, li
            lib.gmm_profile_begin, lib.gmm_profile_end):
     _f.restype = ctypes.c_int
 
-GMM_OK, GMM_E_INVALID, GMM_E_DTYPE, GMM_E_WORKSPACE, GMM_E_PARAMS, GMM_E_HIP, GMM_E_UNSUPPORTED = range(7)
+(GMM_OK, GMM_E_INVALID, GMM_E_DTYPE, GMM_E_WORKSPACE, GMM_E_PARAMS, GMM_E_HIP, GMM_E_UNSUPPORTED,
+ GMM_E_SYNC) = range(8)
 
 
 class GmmError(RuntimeError):

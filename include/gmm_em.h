@@ -54,7 +54,8 @@ typedef enum {
     GMM_E_WORKSPACE = 3, /* workspace missing or too small */
     GMM_E_PARAMS = 4,    /* invalid parameter values (reported by gmm_device_status) */
     GMM_E_HIP = 5,       /* a HIP runtime call failed */
-    GMM_E_UNSUPPORTED = 6 /* shape outside what this build supports */
+    GMM_E_UNSUPPORTED = 6, /* shape outside what this build supports */
+    GMM_E_SYNC = 7       /* cooperative exchange timed out (reported by gmm_device_status) */
 } gmm_status;
 
 typedef enum { GMM_F32 = 0, GMM_BF16 = 1 } gmm_dtype;
@@ -74,6 +75,10 @@ size_t gmm_workspace_bytes(int32_t d, int32_t k);
  *   w'[k] = N[k]/n, mu'[k] = S1[k]/N[k], var'[k] = max(S2[k]/N[k] - mu'[k]^2, var_floor)
  * (a component with N[k] == 0 keeps its mean and variance and gets weight 0).
  * r is never stored: it lives in registers between the two contractions.
+ * Schedule: two passes over the rows (normalisers, then statistics) by
+ * default; GMM_EM_SCHEDULE=coop selects a single cooperative pass in which
+ * the workgroups of a row group exchange per-row partial normalisers through
+ * L2 (it returns GMM_E_UNSUPPORTED where the grid cannot be co-resident).
  * loglik_dev (device, 1 double, may be NULL) receives sum_n lse[n] for the
  * INPUT parameters. var_floor must be finite and >= 0. n >= 1. */
 int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
@@ -110,8 +115,9 @@ int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
                     size_t workspace_bytes, void* stream);
 
 /* Synchronises the stream and returns GMM_E_PARAMS if the last call that used
- * this workspace found invalid parameter values, GMM_OK otherwise, or
- * GMM_E_HIP if the synchronisation failed. */
+ * this workspace found invalid parameter values, GMM_E_SYNC if its
+ * cooperative exchange timed out, GMM_OK otherwise, or GMM_E_HIP if the
+ * synchronisation failed. */
 int gmm_device_status(const void* workspace, void* stream);
 
 /* Static description of a status code. */
@@ -119,7 +125,8 @@ const char* gmm_status_string(int status);
 
 /* Measurement hook. gmm_profile_begin(max_launches) starts recording HIP
  * events on the caller's stream around every normaliser-pass (pass 1) and
- * statistics-pass (pass 2) kernel launch of the following calls, up to
+ * statistics-pass (pass 2: the two-pass schedule's statistics kernel, or the
+ * single cooperative kernel) launch of the following calls, up to
  * max_launches of each (events are created on first use; no device memory is
  * allocated). gmm_profile_end() synchronises those events and returns the
  * summed milliseconds and launch counts of each pass, then stops recording.

@@ -288,3 +288,54 @@ def test_bf16_large_prefix_per_step(ops):
         # bf16 data: the 5e-3 bar applies; the arithmetic itself is fp64
         e = assert_params_close(_host(w, mu, var), (rw, rmu, rv), nk, len(x), 5e-3, f"bf16_large step {t}")
         print(f"bf16_large prefix step {t}:", e)
+
+
+# ---------------------------------------------------------------------------
+# Both schedules of the EM step (the cooperative single pass, chosen by
+# default where it fits, and the two-pass schedule) against the oracle.
+# ---------------------------------------------------------------------------
+@pytest.fixture(params=["two_pass", "coop"])
+def schedule(request, monkeypatch):
+    monkeypatch.setenv("GMM_EM_SCHEDULE", request.param)
+    return request.param
+
+
+def test_schedules_descriptor_prefix(ops, schedule):
+    W = dg.WORKLOADS["descriptor"]
+    x = dg.rows(W, 150_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    worst = _per_step(ops, x, w0, m0, v0, 3, W.var_floor, label=f"descriptor {schedule}")
+    print(schedule, "descriptor per-step worst", worst)
+
+
+@pytest.mark.parametrize("n,d,k,seed", [(1007, 5, 3, 1), (3001, 20, 70, 2), (5000, 128, 100, 5)])
+def test_schedules_ragged(ops, schedule, n, d, k, seed):
+    x, pl, _ = dg.custom(n, d, k, seed=seed)
+    rng = np.random.default_rng(seed)
+    w0 = rng.dirichlet(np.ones(k)).astype(np.float32)
+    m0 = x[rng.choice(n, k, replace=False)].copy()
+    v0 = rng.uniform(0.5, 2.0, size=(k, d)).astype(np.float32)
+    _per_step(ops, x, w0, m0, v0, 2, label=f"{schedule} n={n} d={d} k={k}")
+
+
+def test_schedules_agree_and_are_deterministic(ops, monkeypatch):
+    W = dg.WORKLOADS["embed"]
+    x = dg.rows(W, 40_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    res = {}
+    for sch in ("coop", "coop", "two_pass"):
+        monkeypatch.setenv("GMM_EM_SCHEDULE", sch)
+        xt, w, mu, var = _to_dev(x, w0, m0, v0)
+        ws = ops.workspace(W.d, W.k, DEV)
+        L = ops.em_step(xt, w, mu, var, ws=ws)
+        assert ops.device_status(ws, DEV) == ops.GMM_OK
+        out = (L.item(), *_host(w, mu, var))
+        if sch in res:  # bitwise repeatable
+            assert out[0] == res[sch][0]
+            for a, b in zip(out[1:], res[sch][1:]):
+                assert np.array_equal(a, b)
+        res[sch] = out
+    # the two schedules merge the per-row partial sums in different orders:
+    # equal to rounding
+    assert rel(res["coop"][0], res["two_pass"][0]) <= 1e-10
+    np.testing.assert_allclose(res["coop"][2], res["two_pass"][2], rtol=1e-6, atol=1e-7)
