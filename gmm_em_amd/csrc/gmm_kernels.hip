@@ -302,11 +302,28 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         if (tile + 1 < ntiles) stage(tile + 1, buf ^ 1);
         const double* pp = &Pt[buf][ci * PSTR + h * DPH];
         f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+        // coefficients stream from LDS through a two-batch register ring
+        constexpr int EB = DPH % 8 == 0 ? 8 : DPH;
+        double2 ring[2][EB / 2];
 #pragma unroll
-        for (int t = 0; t < DPH; t += 2) {
-            const double2 pv = *(const double2*)(pp + t);
-            acc = mfma4d(fe[t + 0], pv.x, acc);
-            acc = mfma4d(fe[t + 1], pv.y, acc);
+        for (int u = 0; u < EB / 2; ++u) ring[0][u] = *(const double2*)(pp + 2 * u);
+        __builtin_amdgcn_sched_group_barrier(0x100, EB / 2, 0);
+#pragma unroll
+        for (int bt = 0; bt < DPH / EB; ++bt) {
+            const int cur = bt & 1;
+            if (bt + 1 < DPH / EB) {
+#pragma unroll
+                for (int u = 0; u < EB / 2; ++u)
+                    ring[cur ^ 1][u] = *(const double2*)(pp + (bt + 1) * EB + 2 * u);
+            }
+#pragma unroll
+            for (int u = 0; u < EB / 2; ++u) {
+                const int t = bt * EB + 2 * u;
+                acc = mfma4d(fe[t + 0], ring[cur][u].x, acc);
+                acc = mfma4d(fe[t + 1], ring[cur][u].y, acc);
+            }
+            if (bt + 1 < DPH / EB) __builtin_amdgcn_sched_group_barrier(0x100, EB / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, EB, 0);
         }
         const double c = Ct[buf][ci];
 #pragma unroll
@@ -436,6 +453,13 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     // STATS_ROWS x DP values (row-major, coalesced global reads).
     float xv[PER];
     double lv = 0.0;
+    // shift of the dims this thread stages (fixed for the whole launch)
+    double shv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int dd = (tid + NT * i) % DP;
+        shv[i] = shift[(dd & 1) * DPH + (dd >> 1)];
+    }
     auto load = [&](int64_t it) {
         const int64_t rbase = gr0 + it * STATS_ROWS;
 #pragma unroll
@@ -457,7 +481,7 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             if (e < STATS_ROWS * DP) {
                 const int r = e / DP, dd = e % DP;
                 const int pp = 2 * (dd & 1), t = dd >> 1;
-                const double a = (double)xv[i] - shift[(dd & 1) * DPH + t];
+                const double a = (double)xv[i] - shv[i];
                 fs[buf][r * S + pp * HS + t] = a;
                 fs[buf][r * S + (pp + 1) * HS + t] = a * a;
             }
@@ -480,14 +504,38 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         const double* fa0 = fb + ci * S + h * HS;
         const double* fa1 = fa0 + 16 * S;
         f64x4 e0 = {0.0, 0.0, 0.0, 0.0}, e1 = {0.0, 0.0, 0.0, 0.0};
+        // Features stream from LDS through a two-batch register ring, so each
+        // batch's reads are in flight during the previous batch's MFMAs.
+        constexpr int EB = DPH % 8 == 0 ? 8 : DPH;  // t-steps per batch
+        double2 ring0[2][EB / 2], ring1[2][EB / 2];
 #pragma unroll
-        for (int t = 0; t < DPH; t += 2) {
-            const double2 f0 = *(const double2*)(fa0 + t);
-            const double2 f1 = *(const double2*)(fa1 + t);
-            e0 = mfma4d(f0.x, pr[t + 0], e0);
-            e1 = mfma4d(f1.x, pr[t + 0], e1);
-            e0 = mfma4d(f0.y, pr[t + 1], e0);
-            e1 = mfma4d(f1.y, pr[t + 1], e1);
+        for (int u = 0; u < EB / 2; ++u) {
+            ring0[0][u] = *(const double2*)(fa0 + 2 * u);
+            ring1[0][u] = *(const double2*)(fa1 + 2 * u);
+        }
+        // scheduling groups: batch 0 reads, then per batch: next reads, MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, EB, 0);
+#pragma unroll
+        for (int bt = 0; bt < DPH / EB; ++bt) {
+            const int cur = bt & 1;
+            if (bt + 1 < DPH / EB) {
+#pragma unroll
+                for (int u = 0; u < EB / 2; ++u) {
+                    ring0[cur ^ 1][u] = *(const double2*)(fa0 + (bt + 1) * EB + 2 * u);
+                    ring1[cur ^ 1][u] = *(const double2*)(fa1 + (bt + 1) * EB + 2 * u);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < EB / 2; ++u) {
+                const int t = bt * EB + 2 * u;
+                e0 = mfma4d(ring0[cur][u].x, pr[t + 0], e0);
+                e1 = mfma4d(ring1[cur][u].x, pr[t + 0], e1);
+                e0 = mfma4d(ring0[cur][u].y, pr[t + 1], e0);
+                e1 = mfma4d(ring1[cur][u].y, pr[t + 1], e1);
+            }
+            // keep the next batch's LDS reads ahead of this batch's MFMAs
+            if (bt + 1 < DPH / EB) __builtin_amdgcn_sched_group_barrier(0x100, EB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * EB, 0);
         }
         double r[2][4];
 #pragma unroll
@@ -512,6 +560,9 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
                     acc[NJ + j] = mfma4d(r[rb][q], a * a, acc[NJ + j]);
                 }
             }
+        // keep the next tile's staging after this tile's MFMAs: its global
+        // loads were issued at the top of the iteration and have arrived
+        __builtin_amdgcn_sched_barrier(0);
         if (more) store(buf ^ 1);
         __syncthreads();
     }
