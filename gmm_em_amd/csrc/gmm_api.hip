@@ -72,6 +72,8 @@ static int check_common(const void* x, int64_t n, int32_t d, int64_t ldx, int32_
                         const void* w, const void* mu, const void* var, int32_t k, void* ws,
                         size_t ws_bytes, Plan* pl) {
     if (n < 0 || d < 1 || k < 1 || ldx < d) return GMM_E_INVALID;
+    // the statistics pass addresses a 32-row tile with 32-bit byte offsets
+    if (ldx > MAX_LDX) return GMM_E_UNSUPPORTED;
     if (n > 0 && !x) return GMM_E_INVALID;
     if (!w || !mu || !var) return GMM_E_INVALID;
     if (x_dtype != GMM_F32 && x_dtype != GMM_BF16) return GMM_E_DTYPE;

@@ -11,6 +11,9 @@ constexpr int MAX_DP = 128;
 // Rows per chunk: bounds the per-row normaliser scratch (lse) so that the
 // workspace size does not depend on the number of rows.
 constexpr int64_t CHUNK_ROWS = (int64_t)1 << 22;
+// Largest leading dimension (elements): 32 rows of fp32 values must span
+// fewer than 2^31 bytes (the statistics pass's per-tile buffer offsets).
+constexpr int64_t MAX_LDX = ((int64_t)1 << 24) - 1;
 // Rows per normaliser-pass block (one log-likelihood partial each).
 constexpr int LL_ROWS = 128;
 

@@ -48,6 +48,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gmm_internal.h"
 
 namespace gmm {
@@ -57,6 +59,27 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float load_x(const float* p) { return *p; }
 __device__ __forceinline__ float load_x(const uint16_t* p) {
     return __uint_as_float(((uint32_t)(*p)) << 16);
+}
+
+// Buffer-resource loads (the buffer unit returns 0 for an offset past the
+// resource's range instead of accessing memory). Word 3 of the resource:
+// raw (untyped) buffer, 32-bit data format field, as used by the CDNA
+// compute libraries.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+template <typename XT>
+__device__ __forceinline__ float buf_load_x(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ float buf_load_x<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float buf_load_x<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0)) << 16);
+}
+__device__ __forceinline__ double buf_load_f64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 4), 0, 0);
+    return __hiloint2double((int)hi, (int)lo);
 }
 
 __device__ __forceinline__ f64x4 mfma4d(double a, double b, f64x4 c) {
@@ -273,14 +296,32 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         }
     }
 
-    auto stage = [&](int tile, int buf) {
+    // K-tile staging in two halves: the global loads of a tile are issued one
+    // iteration before their LDS stores, so no wave waits on an L2 round trip
+    // between two tiles' MFMAs.
+    constexpr int SPT = (16 * DP + NT - 1) / NT;  // coefficient pairs per thread
+    double pvx[2 * SPT];
+    double cv = 0.0;
+    auto gload = [&](int tile) {
         const double* src = Pg + (int64_t)tile * 16 * 2 * DP;
-        for (int i = tid; i < 16 * DP; i += NT) {  // pairs of doubles
-            const int e = 2 * i;
-            const int comp = e / (2 * DP), off = e % (2 * DP);
-            *(double2*)&Pt[buf][comp * PSTR + off] = *(const double2*)(src + e);
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int i = tid + NT * u;
+            if (SPT * NT == 16 * DP || i < 16 * DP) { const double2 v = *(const double2*)(src + 2 * i); pvx[2 * u] = v.x; pvx[2 * u + 1] = v.y; }
         }
-        if (tid < 16) Ct[buf][tid] = cvec[tile * 16 + tid];
+        if (tid < 16) cv = cvec[tile * 16 + tid];
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int i = tid + NT * u;
+            if (SPT * NT == 16 * DP || i < 16 * DP) {
+                const int e = 2 * i;
+                const int comp = e / (2 * DP), off = e % (2 * DP);
+                *(double2*)&Pt[buf][comp * PSTR + off] = double2{pvx[2 * u], pvx[2 * u + 1]};
+            }
+        }
+        if (tid < 16) Ct[buf][tid] = cv;
     };
 
     double m[4];
@@ -295,11 +336,38 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         for (int j = 0; j < TMA; ++j) { tv[q][j] = -INFINITY; ti[q][j] = 0x7fffffff; }
     }
 
-    stage(0, 0);
+    // Above D = 96 the features already fill the register budget: the next
+    // tile is loaded and stored at the top of its predecessor's iteration.
+    constexpr bool AHEAD = DP <= 96;
+    auto stage_now = [&](int tile, int buf) {
+        const double* src = Pg + (int64_t)tile * 16 * 2 * DP;
+        for (int i = tid; i < 16 * DP; i += NT) {  // pairs of doubles
+            const int e = 2 * i;
+            const int comp = e / (2 * DP), off = e % (2 * DP);
+            *(double2*)&Pt[buf][comp * PSTR + off] = *(const double2*)(src + e);
+        }
+        if (tid < 16) Ct[buf][tid] = cvec[tile * 16 + tid];
+    };
+    if constexpr (AHEAD) {
+        gload(0);
+        lstore(0);
+        if (ntiles > 1) gload(1);
+    } else {
+        stage_now(0, 0);
+    }
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
         const int buf = tile & 1;
-        if (tile + 1 < ntiles) stage(tile + 1, buf ^ 1);
+        // buffer buf^1 was last read in the previous iteration (before its
+        // closing barrier); tile+1 arrived in registers during that iteration
+        if constexpr (AHEAD) {
+            if (tile + 1 < ntiles) lstore(buf ^ 1);
+            // unconditional (clamped) so the registers are redefined every
+            // iteration instead of merged at the loop join
+            gload(tile + 2 < ntiles ? tile + 2 : ntiles - 1);
+        } else if (tile + 1 < ntiles) {
+            stage_now(tile + 1, buf ^ 1);
+        }
         const double* pp = &Pt[buf][ci * PSTR + h * DPH];
         f64x4 acc = {0.0, 0.0, 0.0, 0.0};
         // coefficients stream from LDS through a two-batch register ring
@@ -384,8 +452,15 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 // 32-row tiles whose fp64 features are staged (double-buffered) in LDS as
 // feats[row][p][t] = power (1 + (p&1)) of dim 2t + (p>>1), the E-operand order,
 // so the E-step reads its A operand directly and the M-step reads a single
-// feature per MFMA. Global loads of the next tile are issued before the
-// current tile's MFMAs and written to LDS after them.
+// feature per MFMA.
+//
+// Schedule of one tile (one wave has a SIMD to itself, so nothing else hides
+// its non-MFMA work): the E-step MFMAs of tile it are interleaved with the
+// staging of tile it+1 (LDS stores of values loaded one iteration earlier)
+// and the global loads of tile it+2; then the responsibilities; then the
+// M-step, whose feature reads run one 4-row group ahead of its MFMAs. Row
+// indices are clamped instead of branched on so that the staging stays in
+// the E-step's basic block; values of rows outside the row group are zeroed.
 // ---------------------------------------------------------------------------
 constexpr int STATS_ROWS = 32;  // two 16-row MFMA blocks per staged tile
 
@@ -397,6 +472,7 @@ struct StatsGeom {
     static constexpr int WV = DP <= 64 ? 8 : 4;  // 8 waves fit 256 registers each only up to 64
     static constexpr int NT = WV * 64;
     static constexpr int PER = (STATS_ROWS * DP + NT - 1) / NT;  // x values per thread
+    static_assert(PER * NT == STATS_ROWS * DP, "every thread stages the same number of values");
 };
 
 template <int DP, typename XT>
@@ -409,6 +485,10 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     using G = StatsGeom<DP>;
     constexpr int DPH = G::DPH, HS = G::HS, S = G::S, WV = G::WV, NT = G::NT, PER = G::PER;
     constexpr int NJ = DP / 16;  // 16-dim column blocks per power
+    constexpr int EB = DPH % 8 == 0 ? 8 : DPH;  // E-step t-steps per batch
+    constexpr int NB = DPH / EB;                // E-step batches
+    static_assert(PER % NB == 0, "staging slices must split evenly over the E batches");
+    constexpr int SL = PER / NB;                // staged values per batch
     __shared__ __attribute__((aligned(16))) double fs[2][STATS_ROWS * S];
     __shared__ double ls[2][STATS_ROWS];
 
@@ -450,75 +530,93 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int64_t ntile_rows = gr1 > gr0 ? (gr1 - gr0 + STATS_ROWS - 1) / STATS_ROWS : 0;
 
     // Staging: thread tid handles elements tid + NT*i of the tile's
-    // STATS_ROWS x DP values (row-major, coalesced global reads).
+    // STATS_ROWS x DP values (row-major, coalesced global reads). Loads go
+    // through a buffer resource built per tile (scalar instructions only):
+    // its range ends after the last valid value of the tile's last row in
+    // the row group, and the buffer unit returns 0 for offsets past it, so
+    // rows past the row group need no clamping or select. Padding dims use
+    // an offset past every range and read as 0 too. The per-element offsets
+    // are loop-invariant: no vector instruction is spent on addressing.
     float xv[PER];
     double lv = 0.0;
-    // shift of the dims this thread stages (fixed for the whole launch)
-    double shv[PER];
+    double shv[PER];     // shift of the dims this thread stages
+    uint32_t xoff[PER];  // byte offset of the element within its tile
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int dd = (tid + NT * i) % DP;
+        const int e = tid + NT * i;
+        const int r = e / DP, dd = e % DP;
         shv[i] = shift[(dd & 1) * DPH + (dd >> 1)];
+        xoff[i] = dd < d ? (uint32_t)(((int64_t)r * ldx + dd) * (int64_t)sizeof(XT)) : 0xFFFFFFF0u;
     }
     auto load = [&](int64_t it) {
         const int64_t rbase = gr0 + it * STATS_ROWS;
+        int64_t nv = gr1 - rbase;
+        nv = nv < 0 ? 0 : (nv > STATS_ROWS ? STATS_ROWS : nv);
+        const int xbytes = nv > 0 ? (int)(((nv - 1) * ldx + d) * (int64_t)sizeof(XT)) : 0;
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + rbase * ldx), (short)0, xbytes, BUF_RSRC_WORD3);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = tid + NT * i;
-            const int r = e / DP, dd = e % DP;
-            const int64_t row = rbase + r;
-            xv[i] = (e < STATS_ROWS * DP && row < gr1 && dd < d) ? load_x(x + row * ldx + dd) : 0.0f;
-        }
-        if (tid < STATS_ROWS) {
-            const int64_t row = rbase + tid;
-            lv = row < gr1 ? lse[row] : INFINITY;
-        }
+        for (int i = 0; i < PER; ++i) xv[i] = buf_load_x<XT>(xr, xoff[i]);
+        // normalisers: rows past the row group get +inf (responsibility 0)
+        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
+        const int lrow = tid & (STATS_ROWS - 1);
+        const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
+        lv = lrow < nv ? v : INFINITY;
     };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = tid + NT * i;
-            if (e < STATS_ROWS * DP) {
-                const int r = e / DP, dd = e % DP;
-                const int pp = 2 * (dd & 1), t = dd >> 1;
-                const double a = (double)xv[i] - shv[i];
-                fs[buf][r * S + pp * HS + t] = a;
-                fs[buf][r * S + (pp + 1) * HS + t] = a * a;
-            }
-        }
-        if (tid < STATS_ROWS) ls[buf][tid] = lv;
+    // (several threads write the same normaliser: same value, same slot)
+    auto storel = [&](double* lsb) { lsb[tid & (STATS_ROWS - 1)] = lv; };
+    auto store1 = [&](double* fsb, int i) {
+        const int e = tid + NT * i;
+        const int r = e / DP, dd = e % DP;
+        const int pp = 2 * (dd & 1), t = dd >> 1;
+        const double a = (double)xv[i] - shv[i];
+        fsb[r * S + pp * HS + t] = a;
+        fsb[r * S + (pp + 1) * HS + t] = a * a;
     };
 
     if (ntile_rows > 0) {
         load(0);
-        store(0);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) store1(fs[0], i);
+        storel(ls[0]);
+        load(1);
     }
     __syncthreads();
-    for (int64_t it = 0; it < ntile_rows; ++it) {
-        const int buf = it & 1;
-        const bool more = it + 1 < ntile_rows;
-        if (more) load(it + 1);
-        const double* fb = fs[buf];
+
+    // One tile; BUF (the LDS buffer holding tile it) is a compile-time
+    // constant so every LDS address is a register plus an immediate offset.
+    auto tile_step = [&](int64_t it, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        const double* fb = fs[BUF];
         // E-step for both 16-row blocks as two independent MFMA chains:
         // register q of lane (h, ci) of chain rb -> l[row 16rb + 4q + h][slot].
+        // Interleaved: LDS stores of tile it+1 (its values arrived during the
+        // previous iteration) and the global loads of tile it+2. Buffer BUF^1
+        // was last read before the previous iteration's closing barrier.
         const double* fa0 = fb + ci * S + h * HS;
         const double* fa1 = fa0 + 16 * S;
         f64x4 e0 = {0.0, 0.0, 0.0, 0.0}, e1 = {0.0, 0.0, 0.0, 0.0};
         // Features stream from LDS through a two-batch register ring, so each
         // batch's reads are in flight during the previous batch's MFMAs.
-        constexpr int EB = DPH % 8 == 0 ? 8 : DPH;  // t-steps per batch
         double2 ring0[2][EB / 2], ring1[2][EB / 2];
 #pragma unroll
         for (int u = 0; u < EB / 2; ++u) {
             ring0[0][u] = *(const double2*)(fa0 + 2 * u);
             ring1[0][u] = *(const double2*)(fa1 + 2 * u);
         }
-        // scheduling groups: batch 0 reads, then per batch: next reads, MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, EB, 0);
+        double lsr[2][4];
 #pragma unroll
-        for (int bt = 0; bt < DPH / EB; ++bt) {
+        for (int q = 0; q < 4; ++q) {
+            lsr[0][q] = ls[BUF][4 * q + h];
+            lsr[1][q] = ls[BUF][16 + 4 * q + h];
+        }
+        storel(ls[BUF ^ 1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, EB + 8, 0);
+#pragma unroll
+        for (int bt = 0; bt < NB; ++bt) {
             const int cur = bt & 1;
-            if (bt + 1 < DPH / EB) {
+            if (bt + 1 < NB) {
 #pragma unroll
                 for (int u = 0; u < EB / 2; ++u) {
                     ring0[cur ^ 1][u] = *(const double2*)(fa0 + (bt + 1) * EB + 2 * u);
@@ -533,38 +631,69 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
                 e0 = mfma4d(ring0[cur][u].y, pr[t + 1], e0);
                 e1 = mfma4d(ring1[cur][u].y, pr[t + 1], e1);
             }
-            // keep the next batch's LDS reads ahead of this batch's MFMAs
-            if (bt + 1 < DPH / EB) __builtin_amdgcn_sched_group_barrier(0x100, EB, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * EB, 0);
+#pragma unroll
+            for (int i = bt * SL; i < (bt + 1) * SL; ++i) store1(fs[BUF ^ 1], i);
+            // order: next batch's LDS reads, then this batch's MFMAs with the
+            // staging stores spread between them
+            if (bt + 1 < NB) __builtin_amdgcn_sched_group_barrier(0x100, EB, 0);
+#pragma unroll
+            for (int u = 0; u < 2 * EB; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                if (u % 8 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
         }
+        // the next-but-one tile's values are loaded once this tile's staging
+        // registers have been written to LDS
+        load(it + 2);
+        __builtin_amdgcn_sched_barrier(0);
         double r[2][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            r[0][q] = (double)__expf((float)(e0[q] + cc - ls[buf][4 * q + h]));
-            r[1][q] = (double)__expf((float)(e1[q] + cc - ls[buf][16 + 4 * q + h]));
+            r[0][q] = (double)__expf((float)(e0[q] + cc - lsr[0][q]));
+            r[1][q] = (double)__expf((float)(e1[q] + cc - lsr[1][q]));
             n64 += r[0][q];
             n64 += r[1][q];
         }
         // M-step: A = r (component ci, row 16rb + 4q + h), B = feature
-        // column 16j + ci of that row (a, then a^2).
+        // column 16j + ci of that row (a, then a^2, both read from LDS). The
+        // features of the next 4-row group are read while this group's
+        // MFMAs run. A group whose 64 responsibilities are all exactly zero
+        // (fp32 exp underflow) is skipped: its MFMAs would add exact zeros.
+        double fc[NJ], qc[NJ], fn[NJ], qn[NJ];
+        auto mread = [&](int grp, double (&f)[NJ], double (&fq)[NJ]) {
+            const double* fm = fb + ((grp >> 2) * 16 + 4 * (grp & 3) + h) * S;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+            for (int j = 0; j < NJ; ++j) {
+                const int dd = 16 * j + ci;
+                f[j] = fm[2 * (dd & 1) * HS + (dd >> 1)];
+                fq[j] = fm[(2 * (dd & 1) + 1) * HS + (dd >> 1)];
+            }
+        };
+        mread(0, fc, qc);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const double* fm = fb + (rb * 16 + 4 * q + h) * S;
+        for (int grp = 0; grp < 8; ++grp) {
+            if (grp + 1 < 8) mread(grp + 1, fn, qn);
+            const double rv = r[grp >> 2][grp & 3];
+            if (__builtin_amdgcn_ballot_w64(rv != 0.0) != 0) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[j] = mfma4d(rv, fc[j], acc[j]);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[NJ + j] = mfma4d(rv, qc[j], acc[NJ + j]);
+            }
+            if (grp + 1 < 8) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const int dd = 16 * j + ci;
-                    const double a = fm[2 * (dd & 1) * HS + (dd >> 1)];
-                    acc[j] = mfma4d(r[rb][q], a, acc[j]);
-                    acc[NJ + j] = mfma4d(r[rb][q], a * a, acc[NJ + j]);
+                    fc[j] = fn[j];
+                    qc[j] = qn[j];
                 }
             }
-        // keep the next tile's staging after this tile's MFMAs: its global
-        // loads were issued at the top of the iteration and have arrived
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) store(buf ^ 1);
+        }
         __syncthreads();
+    };
+    for (int64_t it = 0; it < ntile_rows; it += 2) {
+        tile_step(it, std::integral_constant<int, 0>());
+        if (it + 1 < ntile_rows) tile_step(it + 1, std::integral_constant<int, 1>());
     }
 
     // Responsibility mass: lanes ci, ci+16, ci+32, ci+48 hold disjoint rows.
@@ -803,6 +932,8 @@ void k_coop(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                // all 64 responsibilities exactly zero: nothing to add
+                if (__builtin_amdgcn_ballot_w64(r[rb][q] != 0.0) == 0) continue;
                 const double* fm = fb + (rb * 16 + 4 * q + h) * S;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {

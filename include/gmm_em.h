@@ -14,7 +14,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Data X: device pointer, row-major, n rows of d values with a leading
- *   dimension ldx >= d (in elements), fp32 or bf16 (x_dtype).
+ *   dimension ldx >= d (in elements, at most 2^24 - 1: GMM_E_UNSUPPORTED
+ *   above), fp32 or bf16 (x_dtype). Only the n*d values are read, never the
+ *   gap between d and ldx.
  * Parameters: device pointers, fp32, row-major:
  *   weights[k] (mixture weights, >= 0, not all 0),
  *   means[k*d], variances[k*d] (> 0).

@@ -65,6 +65,7 @@ def test_bad_arguments_rejected_before_any_launch(ops):
     assert _em(ops, mu=None) == ops.GMM_E_INVALID
     assert _em(ops, dt=7) == ops.GMM_E_DTYPE
     assert _em(ops, d=4000, ldx=4000) == ops.GMM_E_UNSUPPORTED
+    assert _em(ops, ldx=1 << 24) == ops.GMM_E_UNSUPPORTED  # row stride past 32-bit tile offsets
     assert _em(ops, ws=None) == ops.GMM_E_WORKSPACE
     assert _em(ops, wsb=16) == ops.GMM_E_WORKSPACE
     need = ops.workspace_bytes(4, 2)
