@@ -20,14 +20,21 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     Plan p;
     p.d = d;
     p.dp = (d + 15) / 16 * 16;
-    if (p.dp > MAX_DP) return false;
+    if (p.dp > MAX_DP) {
+        p.wide = true;
+        p.dp = (d + 127) / 128 * 128;
+        if (p.dp > WIDE_MAX_DP) return false;
+    }
     p.k = k;
     p.kp = (k + 127) / 128 * 128;  // whole 8-tile groups of the statistics pass
     p.ntiles = p.kp / 16;
-    const int kgroups = p.ntiles / waves_per_stats_block(p.dp);
+    // narrow: one block per (row group, K-group of waves); wide: one block per
+    // (row group, K-tile)
+    const int kgroups = p.wide ? p.ntiles : p.ntiles / waves_per_stats_block(p.dp);
     p.kgroups = kgroups;
     int g = (1024 + kgroups - 1) / kgroups;
     p.ngroups = g < 1 ? 1 : (g > 512 ? 512 : g);
+    p.chunk = p.wide ? WIDE_CHUNK_ROWS : CHUNK_ROWS;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -45,6 +52,10 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     const size_t o_lt = take(sizeof(double));
     const size_t o_xb = take((size_t)p.ngroups * 4 * kgroups * 32 * sizeof(double2));
     const size_t o_cnt = take((size_t)p.ngroups * kgroups * sizeof(unsigned));
+    const size_t wpart = p.wide ? (size_t)WIDE_CHUNK_ROWS * p.ntiles : 0;
+    const size_t o_wl = take(wpart * sizeof(double2));
+    const size_t o_wv = take(wpart * WIDE_TM * sizeof(double));
+    const size_t o_wi = take(wpart * WIDE_TM * sizeof(int32_t));
     p.bytes = off;
     if (ws) {
         char* b = (char*)ws;
@@ -59,6 +70,11 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
         p.ll_tmp = (double*)(b + o_lt);
         p.xbuf = (double2*)(b + o_xb);
         p.counters = (unsigned*)(b + o_cnt);
+        if (p.wide) {
+            p.wlpart = (double2*)(b + o_wl);
+            p.wtval = (double*)(b + o_wv);
+            p.wtidx = (int32_t*)(b + o_wi);
+        }
     }
     *pl = p;
     return true;
@@ -114,18 +130,21 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
                              bool stats, hipStream_t st, int m = 0, int32_t* idx = nullptr,
                              float* resp = nullptr, double* lse_rows = nullptr) {
     const size_t esz = dtype == GMM_BF16 ? 2 : 4;
-    for (int64_t c0 = 0, ci = 0; c0 < n; c0 += CHUNK_ROWS, ++ci) {
-        const int64_t cn = n - c0 < CHUNK_ROWS ? n - c0 : CHUNK_ROWS;
+    for (int64_t c0 = 0, ci = 0; c0 < n; c0 += pl.chunk, ++ci) {
+        const int64_t cn = n - c0 < pl.chunk ? n - c0 : pl.chunk;
         const void* xc = (const char*)x + (size_t)c0 * (size_t)ldx * esz;
         double* lse = lse_rows ? lse_rows + c0 : pl.lse;
+        int32_t* ic = m > 0 ? idx + c0 * m : nullptr;
+        float* rc = m > 0 ? resp + c0 * m : nullptr;
         prof_mark(1, true, st);
-        hipError_t e = launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m,
-                                  m > 0 ? idx + c0 * m : nullptr, m > 0 ? resp + c0 * m : nullptr, st);
+        hipError_t e = pl.wide ? launch_wide_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st)
+                               : launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st);
         prof_mark(1, false, st);
         if (e != hipSuccess) return e;
         if (stats) {
             prof_mark(2, true, st);
-            e = launch_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+            e = pl.wide ? launch_wide_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st)
+                        : launch_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
             prof_mark(2, false, st);
             if (e != hipSuccess) return e;
         }
@@ -160,6 +179,7 @@ static int coop_groups(const Plan& pl) {
         cached_cus = prop.multiProcessorCount;
         cached_dev = dev;
     }
+    if (pl.wide) return 0;  // the cooperative kernel holds a K-group's rows in registers
     const int bpc = coop_blocks_per_cu(pl.dp);
     if (bpc < 1 || pl.kgroups < 1 || pl.kgroups > 64) return 0;  // one wave watches the flags
     int groups = (cached_cus * bpc) / pl.kgroups;
@@ -168,8 +188,8 @@ static int coop_groups(const Plan& pl) {
     return groups >= 8 ? groups : 0;
 }
 
-static int ll_parts(int64_t n) {
-    const int64_t first = n < CHUNK_ROWS ? n : CHUNK_ROWS;
+static int ll_parts(const Plan& pl, int64_t n) {
+    const int64_t first = n < pl.chunk ? n : pl.chunk;
     return (int)((first + LL_ROWS - 1) / LL_ROWS);
 }
 
@@ -208,7 +228,7 @@ int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtyp
         (void)hipGetLastError();  // fall back to the two-pass schedule
     }
     e = run_passes(pl, x, n, ldx, x_dtype, true, st);
-    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(n), ll_out, st);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), ll_out, st);
     if (e == hipSuccess) e = launch_finalize(pl, pl.ngroups, n, var_floor, weights, means, variances, st);
     return hip_status(e);
 }
@@ -260,7 +280,7 @@ int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype
     hipError_t e = launch_prologue(pl, weights, means, variances, st);
     if (e == hipSuccess)
         e = run_passes(pl, x, n, ldx, x_dtype, false, st, 0, nullptr, nullptr, per_row_dev);
-    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(n), total_dev, st);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), total_dev, st);
     return hip_status(e);
 }
 

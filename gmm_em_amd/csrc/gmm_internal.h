@@ -6,8 +6,16 @@
 
 namespace gmm {
 
-// Largest padded dimension the register-tiled kernels are built for.
+// Largest padded dimension of the narrow kernels (features or coefficients of
+// a K-tile in registers); wider data uses the D-sliced wide kernels, whose
+// padded dimension is a multiple of 128 up to WIDE_MAX_DP (16 rows of fp64
+// values in LDS).
 constexpr int MAX_DP = 128;
+constexpr int WIDE_MAX_DP = 768;
+// Rows per chunk of the wide path (bounds its per-(row, K-tile) partials).
+constexpr int64_t WIDE_CHUNK_ROWS = 4096;
+// Top-m candidates kept per (row, K-tile) by the wide normaliser pass.
+constexpr int WIDE_TM = 4;
 // Rows per chunk: bounds the per-row normaliser scratch (lse) so that the
 // workspace size does not depend on the number of rows.
 constexpr int64_t CHUNK_ROWS = (int64_t)1 << 22;
@@ -37,6 +45,11 @@ struct Plan {
     double2* xbuf = nullptr;   // [ngroups][4][kgroups][32] cooperative exchange slots
     unsigned* counters = nullptr;  // [ngroups][kgroups] cooperative progress flags
     int kgroups = 0;           // K-groups of the statistics pass (blocks per row group)
+    bool wide = false;         // dp > MAX_DP: the D-sliced wide kernels
+    int64_t chunk = 0;         // rows per chunk (CHUNK_ROWS or WIDE_CHUNK_ROWS)
+    double2* wlpart = nullptr; // wide: [chunk][ntiles] per-(row, K-tile) (max, sum)
+    double* wtval = nullptr;   // wide: [chunk][ntiles][WIDE_TM] top-m candidate values
+    int32_t* wtidx = nullptr;  // wide: [chunk][ntiles][WIDE_TM] candidate components
 };
 
 bool make_plan(int d, int k, void* ws, Plan* pl);
@@ -56,6 +69,14 @@ hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floo
 // block co-resident); fails if the grid cannot be co-resident.
 hipError_t launch_coop(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                        int groups, hipStream_t st);
+// Wide path (pl.wide): normaliser partials + merge (writes lse_out, the
+// log-likelihood partials and, with m > 0, the top-m outputs), and the
+// statistics pass.
+hipError_t launch_wide_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                           double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
+                           hipStream_t st);
+hipError_t launch_wide_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                             const double* lse, int acc, hipStream_t st);
 int coop_blocks_per_cu(int dp);
 int waves_per_stats_block(int dp);
 hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st);

@@ -15,8 +15,8 @@
  * ---------------------------------------
  * Data X: device pointer, row-major, n rows of d values with a leading
  *   dimension ldx >= d (in elements, at most 2^24 - 1: GMM_E_UNSUPPORTED
- *   above), fp32 or bf16 (x_dtype). Only the n*d values are read, never the
- *   gap between d and ldx.
+ *   above), fp32 or bf16 (x_dtype). Values between d and ldx are never
+ *   used (they may be read, never past the last row's d-th value).
  * Parameters: device pointers, fp32, row-major:
  *   weights[k] (mixture weights, >= 0, not all 0),
  *   means[k*d], variances[k*d] (> 0).
@@ -63,7 +63,10 @@ typedef enum {
 typedef enum { GMM_F32 = 0, GMM_BF16 = 1 } gmm_dtype;
 
 /* Bytes of device workspace needed for data of dimension d and k components.
- * Independent of the number of rows. Returns 0 for unsupported shapes. */
+ * Independent of the number of rows. Returns 0 for unsupported shapes:
+ * d <= 768 and k <= 2^22 are supported (d <= 128 uses register-tiled
+ * kernels; wider rows use kernels that split the dimension over the waves of
+ * a workgroup and process rows in chunks of 4096). */
 size_t gmm_workspace_bytes(int32_t d, int32_t k);
 
 /* One EM iteration (E-step, responsibilities, M-step) in place.
