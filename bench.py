@@ -61,6 +61,9 @@ def main() -> int:
     ap.add_argument("--workload", default="descriptor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3_000_000)
+    ap.add_argument("--rows", type=int, default=0,
+                    help="time a prefix of this many rows instead of the workload's N (the "
+                         "JSON line then reports the prefix; EM cost is linear in N)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of the data matrix's size (calibrates the "
                          "HBM byte counters) and exit")
@@ -88,9 +91,10 @@ def main() -> int:
                           "copies": 3}), flush=True)
         return 0
     t0 = time.time()
-    x = dg.rows(W)
+    n_rows = args.rows if 0 < args.rows < W.n else W.n
+    x = dg.rows(W, n_rows)
     w0, m0, v0 = dg.init_params(W, x)
-    print(f"# generated {W.key}: N={W.n} D={W.d} K={W.k} in {time.time() - t0:.1f}s", file=sys.stderr,
+    print(f"# generated {W.key}: N={n_rows} D={W.d} K={W.k} in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
     dev = torch.device("cuda:0")
     if W.dtype == "bf16":
@@ -109,7 +113,8 @@ def main() -> int:
         t.copy_(s)
     torch.cuda.synchronize()
 
-    ops.profile_begin(4 * args.steps + 8)
+    chunk = 4096 if W.d > 128 else (1 << 22)  # rows per launch of each pass
+    ops.profile_begin(args.steps * (-(-n_rows // chunk)) + 8)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -128,7 +133,7 @@ def main() -> int:
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
     its = 1000.0 / ms_step
-    flops_step = 8.0 * W.n * W.d * W.k
+    flops_step = 8.0 * n_rows * W.d * W.k
     tflops = flops_step * its / 1e12
     hist = ll[: args.steps].cpu().numpy()
 
@@ -136,15 +141,17 @@ def main() -> int:
     # cooperative single-pass schedule there is no pass 1 and the one kernel
     # does both contractions)
     (ms1, n1), (ms2, n2) = prof["pass1"], prof["pass2"]
+    wide = W.d > 128  # rows past 128 dims run the D-sliced wide kernels
     if ms2 >= ms1:
-        kname = "k_stats (pass 2)" if n1 > 0 else "k_coop (single pass)"
+        kname = ("k_wide statistics (pass 2)" if wide else "k_stats (pass 2)") if n1 > 0 \
+            else "k_coop (single pass)"
         kms, kn, kflops = ms2, n2, 8.0 * W.d * W.k
     else:
-        kname, kms, kn, kflops = "k_lse (pass 1)", ms1, n1, 4.0 * W.d * W.k
-    rows_per_launch = min(W.n, 1 << 22) if W.n > (1 << 22) else W.n
+        kname = "k_wide normaliser + k_wmerge (pass 1)" if wide else "k_lse (pass 1)"
+        kms, kn, kflops = ms1, n1, 4.0 * W.d * W.k
     launches_per_step = kn / args.steps
     avg_ms = kms / kn
-    alg_flops_launch = kflops * W.n / launches_per_step
+    alg_flops_launch = kflops * n_rows / launches_per_step
     achieved = alg_flops_launch / (avg_ms * 1e-3) / 1e12
     roofline = {
         "kernel": kname,
@@ -161,28 +168,29 @@ def main() -> int:
         "pass1_ms_per_step": round(ms1 / args.steps, 3),
         "pass2_ms_per_step": round(ms2 / args.steps, 3),
     }
-    del rows_per_launch
 
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import oracle
 
-        nr = min(args.cpu_rows, W.n)
+        nr = min(args.cpu_rows, n_rows)
         xs = x[:nr]
         t1 = time.perf_counter()
         oracle.em_step(xs, w0, m0, v0, W.var_floor)
         dt = time.perf_counter() - t1
         cpu = {
-            "value": round(1.0 / (dt * W.n / nr), 6),
+            "value": round(1.0 / (dt * n_rows / nr), 6),
             "unit": "EM it/s",
             "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"one EM step from the initial parameters on the first {nr} of {W.n} rows "
+            "sample": f"one EM step from the initial parameters on the first {nr} of {n_rows} rows "
                       f"({dt:.2f} s), scaled linearly to all rows",
         }
 
+    headline = W.key == "descriptor" and n_rows == W.n
     out = {
-        "metric": "EM iterations/s and % MFMA roofline at N=10M,D=96,K=1024 (1 MI355X)",
+        "metric": ("EM iterations/s and % MFMA roofline at N=10M,D=96,K=1024 (1 MI355X)" if headline
+                   else f"EM iterations/s, {W.key} workload (1 MI355X)"),
         "value": round(its, 4),
         "unit": "EM it/s",
         "n_gpus": 1,
@@ -194,8 +202,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": f"{W.key}: N={W.n} D={W.d} K={W.k} {W.dtype}, EM from seeded init",
-                   "n": W.n, "d": W.d, "k": W.k, "x_dtype": W.dtype, "var_floor": W.var_floor},
+        "config": {"workload": f"{W.key}: N={n_rows} D={W.d} K={W.k} {W.dtype}, EM from seeded init"
+                               + ("" if n_rows == W.n else f" (row prefix of N={W.n})"),
+                   "n": n_rows, "d": W.d, "k": W.k, "x_dtype": W.dtype, "var_floor": W.var_floor},
         "x_dtype": W.dtype,
         "achieved_tflops": round(tflops, 2),
         # the metric's reference: 8*N*D*K flops per iteration against the
