@@ -291,8 +291,8 @@ def test_bf16_large_prefix_per_step(ops):
 
 
 # ---------------------------------------------------------------------------
-# Both schedules of the EM step (the cooperative single pass, chosen by
-# default where it fits, and the two-pass schedule) against the oracle.
+# Both schedules of the EM step (the default two-pass schedule and the
+# opt-in cooperative single pass) against the oracle.
 # ---------------------------------------------------------------------------
 @pytest.fixture(params=["two_pass", "coop"])
 def schedule(request, monkeypatch):
