@@ -368,6 +368,111 @@ int oracle_topm(const float* x, int64_t n, int d, int k, const double* w, const 
     return fail ? 3 : 0;
 }
 
+/* One Lloyd (k-means) step: the hard-assignment quantizer the Flash-GMM
+ * pages replace with a GMM in the IVF coarse quantizer ("Flash-GMM: A
+ * Memory-Efficient Kernel for Scalable Soft Clustering", section 3, the
+ * comparison with K-Means). It is the limit of the EM step with equal
+ * weights and equal spherical variances as the variance goes to zero. Steps:
+ *
+ *   1. distance    D[n][k] = sum_d (x[n][d] - c[k][d])^2   (direct form)
+ *   2. assignment  z[n] = argmin_k D[n][k]  (ties: the smaller k)
+ *   3. inertia     I = sum_n D[n][z[n]]     (for the input centroids)
+ *   4. update      N[k] = #{n : z[n] = k}
+ *                  N[k] > 0: c'[k] = c[k] + (1/N[k]) sum_{z[n]=k} (x[n] - c[k])
+ *                  N[k] = 0: c'[k] = c[k]
+ *
+ * Same fixed-block determinism as oracle_em_step. z_out and nk_out may be
+ * NULL. */
+int oracle_kmeans_step(const float* x, int64_t n, int d, int k, const double* c,
+                       double* c_out, int32_t* z_out, double* inertia, double* nk_out) {
+    if (n < 1 || d < 1 || k < 1) return 1;
+    for (int64_t e = 0; e < (int64_t)k * d; ++e)
+        if (!isfinite(c[e])) return 2;
+    double* c_t = (double*)malloc(sizeof(double) * (size_t)d * k); /* [d][k] */
+    if (!c_t) return 3;
+    for (int j = 0; j < k; ++j)
+        for (int t = 0; t < d; ++t) c_t[(int64_t)t * k + j] = c[(int64_t)j * d + t];
+
+    const int64_t nblocks = (n + ORACLE_BLOCK_ROWS - 1) / ORACLE_BLOCK_ROWS;
+    const int64_t stride = 1 + (int64_t)k * (1 + (int64_t)d); /* I, N[k], T1[k][d] */
+    int64_t batch = threads_for(nblocks);
+    const int64_t budget = (int64_t)2 << 30;
+    while (batch > 1 && batch * stride * (int64_t)sizeof(double) > budget) batch /= 2;
+    double* total = (double*)calloc((size_t)stride, sizeof(double));
+    double* part = (double*)malloc(sizeof(double) * (size_t)(batch * stride));
+    if (!total || !part) {
+        free(total);
+        free(part);
+        free(c_t);
+        return 3;
+    }
+    int fail = 0;
+    for (int64_t b0 = 0; b0 < nblocks && !fail; b0 += batch) {
+        const int64_t b1 = b0 + batch < nblocks ? b0 + batch : nblocks;
+#pragma omp parallel num_threads(threads_for(b1 - b0))
+        {
+            double* dist = (double*)malloc(sizeof(double) * k);
+            if (!dist) {
+#pragma omp atomic write
+                fail = 1;
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t b = b0; b < b1; ++b) {
+                if (!dist) continue;
+                double* s = part + (b - b0) * stride;
+                memset(s, 0, sizeof(double) * (size_t)stride);
+                double* sI = s;
+                double* sN = s + 1;
+                double* sT1 = sN + k;
+                const int64_t lo = b * ORACLE_BLOCK_ROWS;
+                const int64_t hi = lo + ORACLE_BLOCK_ROWS < n ? lo + ORACLE_BLOCK_ROWS : n;
+                for (int64_t i = lo; i < hi; ++i) {
+                    const float* xr = x + i * d;
+                    for (int j = 0; j < k; ++j) dist[j] = 0.0;
+                    for (int t = 0; t < d; ++t) {
+                        const double xv = (double)xr[t];
+                        const double* ct = c_t + (int64_t)t * k;
+                        for (int j = 0; j < k; ++j) {
+                            const double diff = xv - ct[j];
+                            dist[j] += diff * diff;
+                        }
+                    }
+                    int z = 0;
+                    for (int j = 1; j < k; ++j)
+                        if (dist[j] < dist[z]) z = j;
+                    if (z_out) z_out[i] = z;
+                    *sI += dist[z];
+                    sN[z] += 1.0;
+                    const double* cz = c + (int64_t)z * d;
+                    double* t1 = sT1 + (int64_t)z * d;
+                    for (int t = 0; t < d; ++t) t1[t] += (double)xr[t] - cz[t];
+                }
+            }
+            free(dist);
+        }
+        for (int64_t b = b0; b < b1 && !fail; ++b) {
+            const double* s = part + (b - b0) * stride;
+            for (int64_t e = 0; e < stride; ++e) total[e] += s[e];
+        }
+    }
+    if (!fail) {
+        const double* N = total + 1;
+        const double* T1 = N + k;
+        *inertia = total[0];
+        for (int j = 0; j < k; ++j) {
+            if (nk_out) nk_out[j] = N[j];
+            for (int t = 0; t < d; ++t) {
+                const int64_t e = (int64_t)j * d + t;
+                c_out[e] = N[j] > 0.0 ? c[e] + T1[e] / N[j] : c[e];
+            }
+        }
+    }
+    free(total);
+    free(part);
+    free(c_t);
+    return fail ? 3 : 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

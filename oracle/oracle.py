@@ -12,6 +12,9 @@ Two independent implementations of the same definition live here:
   numpy fp64 and uses the two-pass variance; it is for tiny inputs only and
   serves as a cross-check of the streaming C code.
 
+``kmeans_step`` (C) is one Lloyd step, the hard-assignment quantizer the
+pages compare the GMM with (same source, section 3).
+
 The EM definition followed is the textbook diagonal-covariance one that the
 Flash-GMM pages tile ("Flash-GMM: A Memory-Efficient Kernel for Scalable Soft
 Clustering", section 1, responsibility matrix; section 3, EM with per-tile
@@ -77,7 +80,9 @@ def _load():
     lib.oracle_logdensity.argtypes = [fp, i64, i32, i32, dp, dp, dp, dp]
     lib.oracle_em_step.argtypes = [fp, i64, i32, i32, dp, dp, dp, dbl, dp, dp, dp, dp, dp]
     lib.oracle_topm.argtypes = [fp, i64, i32, i32, dp, dp, dp, i32, ip, dp, dp]
-    for f in (lib.oracle_loglik, lib.oracle_logdensity, lib.oracle_em_step, lib.oracle_topm):
+    lib.oracle_kmeans_step.argtypes = [fp, i64, i32, i32, dp, dp, ip, dp, dp]
+    for f in (lib.oracle_loglik, lib.oracle_logdensity, lib.oracle_em_step, lib.oracle_topm,
+              lib.oracle_kmeans_step):
         f.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -159,6 +164,21 @@ def logdensity(x, w, mu, var) -> np.ndarray:
                                  _ptr(w, ctypes.c_double), _ptr(mu, ctypes.c_double),
                                  _ptr(var, ctypes.c_double), _ptr(out, ctypes.c_double)))
     return out
+
+
+def kmeans_step(x, c):
+    """One Lloyd step from centroids c: (c', assignment int32, inertia of c, N_k)."""
+    lib = _load()
+    x = _x32(x)
+    n, d = x.shape
+    c = _p64(c)
+    k = c.shape[0]
+    c2, z, nk = np.empty((k, d)), np.empty(n, np.int32), np.empty(k)
+    inertia = ctypes.c_double(0.0)
+    _check(lib.oracle_kmeans_step(_ptr(x, ctypes.c_float), n, d, k, _ptr(c, ctypes.c_double),
+                                  _ptr(c2, ctypes.c_double), _ptr(z, ctypes.c_int32),
+                                  ctypes.byref(inertia), _ptr(nk, ctypes.c_double)))
+    return c2, z, inertia.value, nk
 
 
 def topm(x, w, mu, var, m: int):

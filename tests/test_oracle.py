@@ -335,3 +335,66 @@ def test_thread_count_independence():
         outs.append(subprocess.run([sys.executable, "-c", code], env=env, check=True,
                                    capture_output=True).stdout)
     assert outs[0] == outs[1] == outs[2]
+
+
+# ---------------------------------------------------------------------------
+# Lloyd (k-means) step: the hard-assignment quantizer the pages compare with.
+# ---------------------------------------------------------------------------
+def test_kmeans_step_matches_sklearn_lloyd_iteration():
+    from sklearn.cluster import KMeans
+
+    x, _, _ = dg.custom(3000, 6, 5, seed=41)
+    c = x[[3, 500, 1200, 2000, 2900]].astype(np.float64)
+    c2, z, inertia, nk = oracle.kmeans_step(x, c)
+    assert np.all(nk > 0)
+    km = KMeans(n_clusters=5, init=c, n_init=1, max_iter=1, tol=0.0, algorithm="lloyd")
+    km.fit(x.astype(np.float64))
+    np.testing.assert_allclose(c2, km.cluster_centers_, rtol=1e-10, atol=1e-12)
+
+
+def test_kmeans_assignment_and_inertia_match_cdist():
+    from scipy.spatial.distance import cdist
+
+    rng = np.random.default_rng(43)
+    x = rng.normal(0, 3, size=(700, 9)).astype(np.float32)
+    c = rng.normal(0, 3, size=(12, 9))
+    c2, z, inertia, nk = oracle.kmeans_step(x, c)
+    dist = cdist(x.astype(np.float64), c, "sqeuclidean")
+    np.testing.assert_array_equal(z, np.argmin(dist, axis=1))  # first minimum on ties
+    assert inertia == pytest.approx(np.min(dist, axis=1).sum(), rel=1e-12)
+    np.testing.assert_array_equal(nk, np.bincount(z, minlength=12))
+
+
+def test_kmeans_lloyd_inertia_never_increases():
+    x, _, _ = dg.custom(5000, 4, 6, seed=47)
+    c = x[:6].astype(np.float64)
+    prev = np.inf
+    for _ in range(6):
+        c, _, inertia, _ = oracle.kmeans_step(x, c)
+        assert inertia <= prev * (1 + 1e-12)
+        prev = inertia
+
+
+def test_kmeans_single_cluster_closed_form():
+    rng = np.random.default_rng(53)
+    x = rng.normal(2.0, 1.5, size=(4000, 3)).astype(np.float32)
+    c0 = np.zeros((1, 3))
+    c2, z, inertia, nk = oracle.kmeans_step(x, c0)
+    X = x.astype(np.float64)
+    np.testing.assert_allclose(c2[0], X.mean(0), rtol=1e-12)
+    assert inertia == pytest.approx((X ** 2).sum(), rel=1e-12)  # about the input centroid 0
+    assert nk[0] == 4000 and np.all(z == 0)
+
+
+def test_kmeans_empty_cluster_and_ties():
+    x = np.array([[0.0, 0.0], [1.0, 0.0], [0.0, 1.0], [10.0, 10.0]], np.float32)
+    # centroid 1 duplicates centroid 0 (ties go to 0); centroid 2 is far away
+    c = np.array([[0.0, 0.0], [0.0, 0.0], [1e3, 1e3], [10.0, 10.0]])
+    c2, z, inertia, nk = oracle.kmeans_step(x, c)
+    np.testing.assert_array_equal(z, [0, 0, 0, 3])
+    np.testing.assert_array_equal(nk, [3, 0, 0, 1])
+    np.testing.assert_allclose(c2[0], [1 / 3, 1 / 3], rtol=1e-15)
+    np.testing.assert_array_equal(c2[1], c[1])  # empty: kept
+    np.testing.assert_array_equal(c2[2], c[2])
+    np.testing.assert_array_equal(c2[3], [10.0, 10.0])
+    assert inertia == pytest.approx(2.0, rel=1e-15)
