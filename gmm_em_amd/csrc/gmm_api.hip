@@ -299,6 +299,39 @@ int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
     return hip_status(e);
 }
 
+int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                    float* centroids, int32_t k, int32_t* assign_dev, double* inertia_dev,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 1 || !centroids) return GMM_E_INVALID;
+    Plan pl;
+    // (the check wants three parameter pointers; k-means has only centroids)
+    int rc = check_common(x, n, d, ldx, x_dtype, centroids, centroids, centroids, k, workspace,
+                          workspace_bytes, &pl);
+    if (rc) return rc;
+    if (pl.wide) return GMM_E_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    // weights and variances null: the k-means coefficients (2c, -1, -|c|^2)
+    hipError_t e = launch_prologue(pl, nullptr, centroids, nullptr, st);
+    const size_t esz = x_dtype == GMM_BF16 ? 2 : 4;
+    for (int64_t c0 = 0, ci = 0; e == hipSuccess && c0 < n; c0 += pl.chunk, ++ci) {
+        const int64_t cn = n - c0 < pl.chunk ? n - c0 : pl.chunk;
+        const void* xc = (const char*)x + (size_t)c0 * (size_t)ldx * esz;
+        // without an output array the chunk's assignments live in the
+        // normaliser scratch (CHUNK_ROWS doubles hold CHUNK_ROWS int32)
+        int32_t* zc = assign_dev ? assign_dev + c0 : (int32_t*)pl.lse;
+        prof_mark(1, true, st);
+        e = launch_lse(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, 1, zc, nullptr, st, 1);
+        prof_mark(1, false, st);
+        if (e != hipSuccess) break;
+        prof_mark(2, true, st);
+        e = launch_stats(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, st, zc);
+        prof_mark(2, false, st);
+    }
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), inertia_dev ? inertia_dev : pl.ll_tmp, st, -1.0);
+    if (e == hipSuccess) e = launch_kmfinal(pl, centroids, st);
+    return hip_status(e);
+}
+
 int gmm_device_status(const void* workspace, void* stream) {
     if (!workspace) return GMM_E_INVALID;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GMM_E_HIP;

@@ -58,11 +58,15 @@ hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, cons
                            hipStream_t st);
 // lse_out may be null (normalisers not kept); m > 0 also writes the top-m
 // components (idx, resp, row-major n x m) of each row.
+// km (k-means mode, with m = 1): the row value summed into the partials is
+// the best log-density instead of the normaliser.
 hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                       double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                      hipStream_t st);
+                      hipStream_t st, int km = 0);
+// z non-null: k-means mode, one-hot responsibilities from the assignment z
+// (no E-step).
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                        const double* lse, int acc, hipStream_t st);
+                        const double* lse, int acc, hipStream_t st, const int32_t* z = nullptr);
 hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floor, float* w,
                            float* mu, float* var, hipStream_t st);
 // Cooperative single pass over all n rows with `groups` row groups (every
@@ -79,6 +83,9 @@ hipError_t launch_wide_stats(const Plan& pl, const void* x, int64_t n, int64_t l
                              const double* lse, int acc, hipStream_t st);
 int coop_blocks_per_cu(int dp);
 int waves_per_stats_block(int dp);
-hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st);
+hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st,
+                           double scale = 1.0);
+// k-means centroid update from the statistics partials.
+hipError_t launch_kmfinal(const Plan& pl, float* c, hipStream_t st);
 
 }  // namespace gmm

@@ -62,16 +62,17 @@ __global__ void k_status_reset(int* status) {
     if (threadIdx.x < 4) status[threadIdx.x] = 0;
 }
 
+// (w and var null: k-means mode, centroids only; every weight counts as 1)
 __global__ void k_validate(const float* __restrict__ w, const float* __restrict__ mu,
                            const float* __restrict__ var, int k, int d, int* status) {
     const int64_t total = (int64_t)k * d;
     int bad = 0, anypos = 0;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        const float m = mu[i], v = var[i];
+        const float m = mu[i], v = var ? var[i] : 1.0f;
         if (!isfinite(m) || !isfinite(v) || !(v > 0.0f)) bad = 1;
         if (i < k) {
-            const float wi = w[i];
+            const float wi = w ? w[i] : 1.0f;
             if (!isfinite(wi) || wi < 0.0f) bad = 1;
             if (wi > 0.0f) anypos = 1;
         }
@@ -107,6 +108,8 @@ __global__ void k_shift(const float* __restrict__ mu, int k, int d, int dp,
 // padding with coefficient 0 and constant -inf), in operand order:
 //   Pg[slot][h][t]: h&1 = 0 -> w*b of dim 2t+(h>>1), h&1 = 1 -> -w/2.
 //   cvec[slot] = log pi - 1/2 sum_d (w b^2 + log var) - D/2 log 2pi.
+// k-means mode (w and var null): w = 2 and no log terms, so that
+//   l = sum_d (2 b a - a^2) - sum_d b^2 = -|x - c|^2 exactly.
 __global__ void k_params(const float* __restrict__ w, const float* __restrict__ mu,
                          const float* __restrict__ var, int k, int d, int dp,
                          const double* __restrict__ shift, double* __restrict__ Pg,
@@ -114,19 +117,26 @@ __global__ void k_params(const float* __restrict__ w, const float* __restrict__ 
     __shared__ double red[128];
     const int slot = blockIdx.x;
     const bool live = slot < k;
+    const bool km = w == nullptr;
     const int dph = dp >> 1;
     double part = 0.0;
     double* row = Pg + (int64_t)slot * 2 * dp;
     for (int dd = threadIdx.x; dd < dp; dd += blockDim.x) {
         double cb = 0.0, cq = 0.0;
         if (live && dd < d) {
-            const double v = (double)var[(int64_t)slot * d + dd];
             const double s = shift[(dd & 1) * dph + (dd >> 1)];
             const double b = (double)mu[(int64_t)slot * d + dd] - s;
-            const double iw = 1.0 / v;
-            cb = iw * b;
-            cq = -0.5 * iw;
-            part += iw * b * b + log(v);
+            if (km) {
+                cb = 2.0 * b;
+                cq = -1.0;
+                part += 2.0 * b * b;
+            } else {
+                const double v = (double)var[(int64_t)slot * d + dd];
+                const double iw = 1.0 / v;
+                cb = iw * b;
+                cq = -0.5 * iw;
+                part += iw * b * b + log(v);
+            }
         }
         const int t = dd >> 1, hh = (dd & 1) << 1;
         row[(hh + 0) * dph + t] = cb;
@@ -140,12 +150,12 @@ __global__ void k_params(const float* __restrict__ w, const float* __restrict__ 
     }
     if (threadIdx.x == 0) {
         const double LOG_2PI = 1.8378770664093454835606594728112;
-        cvec[slot] = live ? log((double)w[slot]) - 0.5 * (red[0] + (double)d * LOG_2PI) : -INFINITY;
+        cvec[slot] = !live ? -INFINITY
+                     : km  ? -0.5 * red[0]
+                           : log((double)w[slot]) - 0.5 * (red[0] + (double)d * LOG_2PI);
     }
 }
 
-// ---------------------------------------------------------------------------
-// Top-m bookkeeping for the soft multi-assignment (pass 1 only).
 // ---------------------------------------------------------------------------
 // Pass 1: per-row logsumexp over all components.
 // Block: 8 waves x 16 rows. Each lane holds the fp64 features of its row in
@@ -164,7 +174,7 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
            const double* __restrict__ Pg, const double* __restrict__ cvec,
            const double* __restrict__ shift, int ntiles, double* __restrict__ lse_out,
            double* __restrict__ llpart, int ll_accumulate, int k, int m_out,
-           int32_t* __restrict__ idx_out, float* __restrict__ resp_out) {
+           int32_t* __restrict__ idx_out, float* __restrict__ resp_out, int km) {
     constexpr int DPH = DP / 2;
     constexpr int PSTR = 2 * DP + 2;  // LDS stride of one component (doubles)
     constexpr int TMA = TM > 0 ? TM : 1;
@@ -317,13 +327,16 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             const int64_t row = (int64_t)blockIdx.x * LSE_ROWS + lr;
             double v = 0.0;
             if (row < n) {
-                v = m[q] + log((double)s[q]);
+                // k-means mode: the row's value is its best log-density,
+                // -|x - c_z|^2 (the row's contribution to -inertia)
+                if constexpr (TM > 0) v = km ? tv[q][0] : m[q] + log((double)s[q]);
+                else v = m[q] + log((double)s[q]);
                 if (lse_out) lse_out[row] = v;
                 if constexpr (TM > 0) {
                     for (int j = 0; j < m_out; ++j) {
                         const int sl = ti[q][j];
                         idx_out[row * m_out + j] = sl < k ? sl : -1;
-                        resp_out[row * m_out + j] = __expf((float)(tv[q][j] - v));
+                        if (resp_out) resp_out[row * m_out + j] = __expf((float)(tv[q][j] - v));
                     }
                 }
             }
@@ -371,13 +384,17 @@ struct StatsGeom {
     static_assert(PER * NT == STATS_ROWS * DP, "every thread stages the same number of values");
 };
 
-template <int DP, typename XT>
+// KM (k-means mode): the responsibilities are one-hot, r = [z(row) == slot]
+// with the assignment z of each row from the normaliser pass (zasg), so no
+// E-step runs; the M-step then only touches groups that hold a row assigned
+// to one of the wave's components.
+template <int DP, typename XT, bool KM>
 __global__ __launch_bounds__(StatsGeom<DP>::NT, 1)
 void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
              const double* __restrict__ Pg, const double* __restrict__ cvec,
              const double* __restrict__ shift, int ntiles, const double* __restrict__ lse,
-             int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
-             int accumulate) {
+             const int32_t* __restrict__ zasg, int64_t rows_per_group,
+             double* __restrict__ part, double* __restrict__ npart, int accumulate) {
     using G = StatsGeom<DP>;
     constexpr int DPH = G::DPH, HS = G::HS, S = G::S, WV = G::WV, NT = G::NT, PER = G::PER;
     constexpr int NJ = DP / 16;  // 16-dim column blocks per power
@@ -403,8 +420,8 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int slot = tile * 16 + ci;
 
     // Stationary coefficients: P[slot][h][t], t = 0..DPH-1.
-    double pr[DPH];
-    {
+    double pr[KM ? 1 : DPH];
+    if constexpr (!KM) {
         const double* src = Pg + (int64_t)slot * 2 * DP + h * DPH;
 #pragma unroll
         for (int t = 0; t < DPH; t += 2) {
@@ -413,7 +430,7 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             pr[t + 1] = v.y;
         }
     }
-    const double cc = cvec[slot];
+    const double cc = KM ? 0.0 : cvec[slot];
 
     f64x4 acc[2 * NJ];
 #pragma unroll
@@ -453,12 +470,20 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             __builtin_amdgcn_make_buffer_rsrc((void*)(x + rbase * ldx), (short)0, xbytes, BUF_RSRC_WORD3);
 #pragma unroll
         for (int i = 0; i < PER; ++i) xv[i] = buf_load_x<XT>(xr, xoff[i]);
-        // normalisers: rows past the row group get +inf (responsibility 0)
-        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
+        // normalisers: rows past the row group get +inf (responsibility 0);
+        // k-means mode: the assignment as a double, -1 past the row group
         const int lrow = tid & (STATS_ROWS - 1);
-        const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
-        lv = lrow < nv ? v : INFINITY;
+        if constexpr (KM) {
+            const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(zasg + rbase), (short)0, (int)(nv * (int64_t)sizeof(int32_t)), BUF_RSRC_WORD3);
+            const int zv = (int)__builtin_amdgcn_raw_buffer_load_b32(zr, lrow * 4, 0, 0);
+            lv = lrow < nv ? (double)zv : -1.0;
+        } else {
+            const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
+            const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
+            lv = lrow < nv ? v : INFINITY;
+        }
     };
     // (several threads write the same normaliser: same value, same slot)
     auto storel = [&](double* lsb) { lsb[tid & (STATS_ROWS - 1)] = lv; };
@@ -508,6 +533,11 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             lsr[1][q] = ls[BUF][16 + 4 * q + h];
         }
         storel(ls[BUF ^ 1]);
+        if constexpr (KM) {
+            // no E-step: only the staging of tile it+1
+#pragma unroll
+            for (int i = 0; i < PER; ++i) store1(fs[BUF ^ 1], i);
+        } else {
         __builtin_amdgcn_sched_group_barrier(0x100, EB + 8, 0);
 #pragma unroll
         for (int bt = 0; bt < NB; ++bt) {
@@ -539,6 +569,7 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
                 if (u % 8 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
         }
+        }
         // the next-but-one tile's values are loaded once this tile's staging
         // registers have been written to LDS
         load(it + 2);
@@ -546,8 +577,13 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         double r[2][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            r[0][q] = (double)__expf((float)(e0[q] + cc - lsr[0][q]));
-            r[1][q] = (double)__expf((float)(e1[q] + cc - lsr[1][q]));
+            if constexpr (KM) {
+                r[0][q] = lsr[0][q] == (double)slot ? 1.0 : 0.0;
+                r[1][q] = lsr[1][q] == (double)slot ? 1.0 : 0.0;
+            } else {
+                r[0][q] = (double)__expf((float)(e0[q] + cc - lsr[0][q]));
+                r[1][q] = (double)__expf((float)(e1[q] + cc - lsr[1][q]));
+            }
             n64 += r[0][q];
             n64 += r[1][q];
         }
@@ -920,9 +956,11 @@ __global__ void k_finalize(const double* __restrict__ part, const double* __rest
     if (threadIdx.x == 0) w[comp] = bad ? NAN : (N > 0.0 ? (float)(N / (double)n) : 0.0f);
 }
 
-// Fixed-order fp64 sum of the per-block log-likelihood partials.
+// Fixed-order fp64 sum of the per-block log-likelihood partials, times
+// `scale` (1 for the log-likelihood; -1 turns the k-means mode's summed best
+// log-densities -|x - c_z|^2 into the inertia).
 __global__ void k_ll_final(const double* __restrict__ llpart, int nparts, double* __restrict__ out,
-                           const int* __restrict__ status) {
+                           const int* __restrict__ status, double scale) {
     __shared__ double red[256];
     double acc = 0.0;
     const int per = (nparts + 255) / 256;
@@ -934,7 +972,29 @@ __global__ void k_ll_final(const double* __restrict__ llpart, int nparts, double
         if (threadIdx.x < sft) red[threadIdx.x] += red[threadIdx.x + sft];
         __syncthreads();
     }
-    if (threadIdx.x == 0) *out = (status[0] != 0 || status[1] == 0 || status[2] != 0) ? NAN : red[0];
+    if (threadIdx.x == 0)
+        *out = (status[0] != 0 || status[1] == 0 || status[2] != 0) ? NAN : scale * red[0];
+}
+
+// k-means update: c'[k] = s + S1[k] / N[k] for a non-empty cluster (fixed-
+// order fp64 sums over the row groups), the input centroid otherwise.
+__global__ void k_kmfinal(const double* __restrict__ part, const double* __restrict__ npart,
+                          int ngroups, int kp, int dp, int d, int k,
+                          const double* __restrict__ shift, float* __restrict__ c,
+                          const int* __restrict__ status) {
+    const int comp = blockIdx.x;
+    if (comp >= k) return;
+    const bool bad = status[0] != 0;
+    double N = 0.0;
+    for (int gg = 0; gg < ngroups; ++gg) N += npart[(int64_t)gg * kp + comp];
+    const int dph = dp >> 1;
+    for (int dd = threadIdx.x; dd < d; dd += blockDim.x) {
+        double s1 = 0.0;
+        for (int gg = 0; gg < ngroups; ++gg) s1 += part[((int64_t)gg * kp + comp) * 2 * dp + dd];
+        const int64_t e = (int64_t)comp * d + dd;
+        if (bad) c[e] = NAN;
+        else if (N > 0.0) c[e] = (float)(shift[(dd & 1) * dph + (dd >> 1)] + s1 / N);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -943,33 +1003,39 @@ __global__ void k_ll_final(const double* __restrict__ llpart, int nparts, double
 template <int DP, typename XT, int TM>
 static hipError_t launch_lse_tm(const Plan& pl, const void* x, int64_t n, int64_t ldx,
                                 double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                                hipStream_t st) {
+                                int km, hipStream_t st) {
     const int64_t blocks = (n + LSE_ROWS - 1) / LSE_ROWS;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_lse<DP, XT, TM>), dim3((unsigned)blocks), dim3(LSE_WAVES * 64), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse_out,
-                       pl.llpart, ll_acc, pl.k, m, idx, resp);
+                       pl.llpart, ll_acc, pl.k, m, idx, resp, km);
     return hipGetLastError();
 }
 
 template <int DP, typename XT>
 static hipError_t launch_lse_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
                                double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                               hipStream_t st) {
-    if (m <= 0) return launch_lse_tm<DP, XT, 0>(pl, x, n, ldx, lse_out, ll_acc, 0, idx, resp, st);
-    if (m <= 2) return launch_lse_tm<DP, XT, 2>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, st);
-    return launch_lse_tm<DP, XT, 4>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, st);
+                               int km, hipStream_t st) {
+    if (m <= 0) return launch_lse_tm<DP, XT, 0>(pl, x, n, ldx, lse_out, ll_acc, 0, idx, resp, 0, st);
+    if (m <= 2) return launch_lse_tm<DP, XT, 2>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
+    return launch_lse_tm<DP, XT, 4>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
 }
 
 template <int DP, typename XT>
 static hipError_t launch_stats_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
-                                 const double* lse, int acc, hipStream_t st) {
+                                 const double* lse, const int32_t* z, int acc, hipStream_t st) {
     using G = StatsGeom<DP>;
     int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
     if (rpg < STATS_ROWS) rpg = STATS_ROWS;
-    hipLaunchKernelGGL((k_stats<DP, XT>), dim3(pl.ngroups * (pl.ntiles / G::WV)), dim3(G::NT), 0, st,
-                       (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, rpg,
-                       pl.part, pl.npart, acc);
+    const dim3 grid(pl.ngroups * (pl.ntiles / G::WV));
+    if (z)
+        hipLaunchKernelGGL((k_stats<DP, XT, true>), grid, dim3(G::NT), 0, st, (const XT*)x, n,
+                           pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, z, rpg, pl.part,
+                           pl.npart, acc);
+    else
+        hipLaunchKernelGGL((k_stats<DP, XT, false>), grid, dim3(G::NT), 0, st, (const XT*)x, n,
+                           pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, z, rpg, pl.part,
+                           pl.npart, acc);
     return hipGetLastError();
 }
 
@@ -977,13 +1043,14 @@ static hipError_t launch_stats_t(const Plan& pl, const void* x, int64_t n, int64
 
 hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                       double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                      hipStream_t st) {
+                      hipStream_t st, int km) {
     switch (pl.dp) {
-#define CASE(DPV)                                                                              \
-    case DPV:                                                                                  \
-        return dtype == 0                                                                      \
-                   ? launch_lse_t<DPV, float>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, st) \
-                   : launch_lse_t<DPV, uint16_t>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, st);
+#define CASE(DPV)                                                                          \
+    case DPV:                                                                              \
+        return dtype == 0 ? launch_lse_t<DPV, float>(pl, x, n, ldx, lse_out, ll_acc, m, idx, \
+                                                     resp, km, st)                          \
+                          : launch_lse_t<DPV, uint16_t>(pl, x, n, ldx, lse_out, ll_acc, m,   \
+                                                        idx, resp, km, st);
         GMM_DP_CASES(CASE)
 #undef CASE
     }
@@ -991,12 +1058,12 @@ hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int
 }
 
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                        const double* lse, int acc, hipStream_t st) {
+                        const double* lse, int acc, hipStream_t st, const int32_t* z) {
     switch (pl.dp) {
-#define CASE(DPV)                                                                    \
-    case DPV:                                                                        \
-        return dtype == 0 ? launch_stats_t<DPV, float>(pl, x, n, ldx, lse, acc, st) \
-                          : launch_stats_t<DPV, uint16_t>(pl, x, n, ldx, lse, acc, st);
+#define CASE(DPV)                                                                       \
+    case DPV:                                                                           \
+        return dtype == 0 ? launch_stats_t<DPV, float>(pl, x, n, ldx, lse, z, acc, st) \
+                          : launch_stats_t<DPV, uint16_t>(pl, x, n, ldx, lse, z, acc, st);
         GMM_DP_CASES(CASE)
 #undef CASE
     }
@@ -1073,8 +1140,15 @@ hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floo
     return hipGetLastError();
 }
 
-hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st) {
-    hipLaunchKernelGGL(k_ll_final, dim3(1), dim3(256), 0, st, pl.llpart, nparts, out, pl.status);
+hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st, double scale) {
+    hipLaunchKernelGGL(k_ll_final, dim3(1), dim3(256), 0, st, pl.llpart, nparts, out, pl.status,
+                       scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_kmfinal(const Plan& pl, float* c, hipStream_t st) {
+    hipLaunchKernelGGL(k_kmfinal, dim3(pl.k), dim3(128), 0, st, pl.part, pl.npart, pl.ngroups,
+                       pl.kp, pl.dp, pl.d, pl.k, pl.shift, c, pl.status);
     return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ lib.gmm_fit.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _i32, _f32, 
 lib.gmm_loglik.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
 lib.gmm_assign_topm.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp,
                                 _vp, _sz, _vp]
+lib.gmm_kmeans_step.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
 lib.gmm_device_status.argtypes = [_vp, _vp]
 lib.gmm_status_string.argtypes = [ctypes.c_int]
 lib.gmm_status_string.restype = ctypes.c_char_p
@@ -35,8 +36,8 @@ lib.gmm_version.restype = _i32
 lib.gmm_profile_begin.argtypes = [_i32]
 lib.gmm_profile_end.argtypes = [ctypes.POINTER(_f64), ctypes.POINTER(_i32), ctypes.POINTER(_f64),
                                 ctypes.POINTER(_i32)]
-for _f in (lib.gmm_em_step, lib.gmm_fit, lib.gmm_loglik, lib.gmm_assign_topm, lib.gmm_device_status,
-           lib.gmm_profile_begin, lib.gmm_profile_end):
+for _f in (lib.gmm_em_step, lib.gmm_fit, lib.gmm_loglik, lib.gmm_assign_topm, lib.gmm_kmeans_step,
+           lib.gmm_device_status, lib.gmm_profile_begin, lib.gmm_profile_end):
     _f.restype = ctypes.c_int
 
 (GMM_OK, GMM_E_INVALID, GMM_E_DTYPE, GMM_E_WORKSPACE, GMM_E_PARAMS, GMM_E_HIP, GMM_E_UNSUPPORTED,
@@ -154,6 +155,26 @@ def assign_topm(x, weights, means, variances, m: int = 2, ws=None):
                                _ptr(variances), k, m, _ptr(idx), _ptr(resp), _ptr(ws), ws.numel(),
                                _stream(x.device)))
     return idx, resp
+
+
+def kmeans_step(x, centroids, ws=None, assign: bool = True):
+    """One Lloyd step in place on centroids (K, D) float32.
+
+    Returns (inertia 0-d float64 device tensor for the input centroids,
+    assignment int32 (N,) or None).
+    """
+    dt, ldx = _data(x)
+    if centroids.dtype != torch.float32 or not centroids.is_contiguous() or centroids.dim() != 2:
+        raise ValueError("centroids must be a contiguous float32 (K, D) tensor")
+    if centroids.device != x.device or centroids.shape[1] != x.shape[1]:
+        raise ValueError("centroids must be on the device of x and match its D")
+    k, d = centroids.shape
+    ws = _ws(ws, d, k, x.device)
+    inertia = torch.empty((), dtype=torch.float64, device=x.device)
+    z = torch.empty(x.shape[0], dtype=torch.int32, device=x.device) if assign else None
+    _check(lib.gmm_kmeans_step(_ptr(x), x.shape[0], d, ldx, dt, _ptr(centroids), k, _ptr(z),
+                               _ptr(inertia), _ptr(ws), ws.numel(), _stream(x.device)))
+    return inertia, z
 
 
 def device_status(ws, device="cuda") -> int:

@@ -119,6 +119,26 @@ int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
                     int32_t m, int32_t* idx_dev, float* resp_dev, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* One Lloyd (k-means) step, the hard-assignment quantizer that the Flash-GMM
+ * pages compare the GMM against in the IVF coarse quantizer ("Flash-GMM: A
+ * Memory-Efficient Kernel for Scalable Soft Clustering", section 3). It is
+ * the EM step's limit for equal weights and equal spherical variances
+ * shrinking to zero, and runs on the same two passes:
+ *   z[n]  = argmin_k |x_n - c_k|^2       (ties: smaller k)
+ *   c'_k  = mean of the rows with z = k  (c_k kept when no row has z = k)
+ * centroids (device, k x d floats, row-major) is read and overwritten with c'.
+ * assign_dev (device, n int32, may be NULL) receives z. inertia_dev (device,
+ * 1 double, may be NULL) receives sum_n |x_n - c_z[n]|^2 for the INPUT
+ * centroids. The distances use the expanded form 2 a.b - a.a - b.b about a
+ * per-dimension shift (exact up to fp64 rounding), so rows whose two nearest
+ * centroids are within rounding of each other may be assigned either one.
+ * The workspace is the one for (d, k). n >= 1; d <= 128 (GMM_E_UNSUPPORTED
+ * otherwise). A non-finite centroid is reported by gmm_device_status and
+ * turns the outputs into NaN. */
+int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                    float* centroids, int32_t k, int32_t* assign_dev, double* inertia_dev,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronises the stream and returns GMM_E_PARAMS if the last call that used
  * this workspace found invalid parameter values, GMM_E_SYNC if its
  * cooperative exchange timed out, GMM_OK otherwise, or GMM_E_HIP if the

@@ -25,7 +25,7 @@ def ops():
 
 def test_library_exports_every_declared_symbol(ops):
     names = _declared()
-    assert {"gmm_em_step", "gmm_fit", "gmm_loglik", "gmm_assign_topm"} <= set(names)
+    assert {"gmm_em_step", "gmm_fit", "gmm_loglik", "gmm_assign_topm", "gmm_kmeans_step"} <= set(names)
     for nm in names:
         assert hasattr(ops.lib, nm), nm
     assert ops.lib.gmm_version() >= 100
@@ -85,3 +85,16 @@ def test_fit_and_topm_argument_checks(ops):
     assert t(1, 10, 4, 4, 0, 1, 1, 1, 2, 0, 1, 1, 256, need, None) == ops.GMM_E_INVALID
     assert t(1, 10, 4, 4, 0, 1, 1, 1, 2, 3, 1, 1, 256, need, None) == ops.GMM_E_INVALID
     assert t(1, 10, 4, 4, 0, 1, 1, 1, 2, 1, None, 1, 256, need, None) == ops.GMM_E_INVALID
+
+
+def test_kmeans_argument_checks(ops):
+    # host-side rejections happen before any device call
+    km = ops.lib.gmm_kmeans_step
+    need = ops.workspace_bytes(4, 2)
+    assert km(1, 0, 4, 4, 0, 1, 2, None, None, 256, need, None) == ops.GMM_E_INVALID  # n = 0
+    assert km(1, 10, 4, 4, 0, None, 2, None, None, 256, need, None) == ops.GMM_E_INVALID
+    assert km(1, 10, 4, 3, 0, 1, 2, None, None, 256, need, None) == ops.GMM_E_INVALID  # ldx < d
+    assert km(1, 10, 4, 4, 7, 1, 2, None, None, 256, need, None) == ops.GMM_E_DTYPE
+    assert km(1, 10, 4, 4, 0, 1, 2, None, None, 256, need - 1, None) == ops.GMM_E_WORKSPACE
+    wide = ops.workspace_bytes(300, 2)
+    assert km(1, 10, 300, 300, 0, 1, 2, None, None, 256, wide, None) == ops.GMM_E_UNSUPPORTED
