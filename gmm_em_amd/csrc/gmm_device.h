@@ -46,11 +46,15 @@ __device__ __forceinline__ double feat(float x, double s, bool sq) {
 }
 
 // Online logsumexp with the running maximum in fp64 and the scaled sum in
-// fp32 (every exponent argument is <= 0).
+// fp32 (every exponent argument is <= 0). One of the two rescaling factors
+// is always exp(0) = 1, so a push takes a single exponential: with
+// t = v - m, s <- s * exp(-t) + 1 and m <- v when t > 0, else s <- s + exp(t).
 __device__ __forceinline__ void lse_push(double& m, float& s, double v) {
-    const double mn = fmax(m, v);
-    s = s * __expf((float)(m - mn)) + __expf((float)(v - mn));
-    m = mn;
+    const float t = (float)(v - m);
+    const float e = __expf(-fabsf(t));
+    const bool up = t > 0.0f;
+    s = up ? fmaf(s, e, 1.0f) : s + e;
+    m = up ? v : m;
 }
 __device__ __forceinline__ void lse_merge(double& m, float& s, double m2, float s2) {
     const double mn = fmax(m, m2);

@@ -179,8 +179,8 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     constexpr int PSTR = 2 * DP + 2;  // LDS stride of one component (doubles)
     constexpr int TMA = TM > 0 ? TM : 1;
     constexpr int NT = LSE_WAVES * 64;
-    __shared__ __attribute__((aligned(16))) double Pt[2][16 * PSTR];
-    __shared__ double Ct[2][16];
+    __shared__ __attribute__((aligned(16))) double Pt[3][16 * PSTR];
+    __shared__ double Ct[3][16];
     __shared__ double rowll[LSE_ROWS];
 
     const int tid = threadIdx.x;
@@ -202,9 +202,16 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         }
     }
 
-    // K-tile staging in two halves: the global loads of a tile are issued one
-    // iteration before their LDS stores, so no wave waits on an L2 round trip
-    // between two tiles' MFMAs.
+    // K-tiles stream through three LDS buffers: in iteration t the waves
+    // read tile t from buffer t%3 while tile t+2 is written to buffer
+    // (t+2)%3 (last read in iteration t-1). So the one barrier per tile never
+    // separates a buffer's writes from its reads by less than a full
+    // iteration, and the first coefficients of tile t+1 (written in iteration
+    // t-1) are read before the barrier that ends iteration t: a wave starts
+    // its next MFMA chain as soon as it leaves the barrier. Up to D = 96 the
+    // global loads of a tile are also issued one iteration ahead of its LDS
+    // stores, so no wave waits on an L2 round trip inside the loop.
+    constexpr int NBUF = 3;
     constexpr int SPT = (16 * DP + NT - 1) / NT;  // coefficient pairs per thread
     double pvx[2 * SPT];
     double cv = 0.0;
@@ -242,9 +249,9 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         for (int j = 0; j < TMA; ++j) { tv[q][j] = -INFINITY; ti[q][j] = 0x7fffffff; }
     }
 
-    // Above D = 96 the features already fill the register budget: the next
-    // tile is loaded and stored at the top of its predecessor's iteration.
-    constexpr bool AHEAD = DP <= 96;
+    // Above D = 96 (or with the longer top-m lists) the register budget is
+    // spent: tile t+2 is loaded and stored at the top of iteration t.
+    constexpr bool AHEAD = DP <= 96 && TM <= 2;
     auto stage_now = [&](int tile, int buf) {
         const double* src = Pg + (int64_t)tile * 16 * 2 * DP;
         for (int i = tid; i < 16 * DP; i += NT) {  // pairs of doubles
@@ -257,35 +264,69 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     if constexpr (AHEAD) {
         gload(0);
         lstore(0);
-        if (ntiles > 1) gload(1);
+        gload(ntiles > 1 ? 1 : 0);
+        lstore(1);
+        gload(ntiles > 2 ? 2 : ntiles - 1);
     } else {
         stage_now(0, 0);
+        if (ntiles > 1) stage_now(1, 1);
     }
     __syncthreads();
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int buf = tile & 1;
-        // buffer buf^1 was last read in the previous iteration (before its
-        // closing barrier); tile+1 arrived in registers during that iteration
+
+    // coefficients stream from LDS through a two-batch register ring
+    // (shorter batches where the features or top-m lists fill the registers)
+    constexpr int EB = (DP >= 128 || TM > 2) ? 4 : 8;
+    constexpr int NBT = DPH / EB;
+    double2 ring[2][EB / 2];
+    {
+        const double* pp = &Pt[0][ci * PSTR + h * DPH];
+#pragma unroll
+        for (int u = 0; u < EB / 2; ++u) ring[0][u] = *(const double2*)(pp + 2 * u);
+    }
+    // The finished tile's values are folded into the running normaliser
+    // (and top-m list) while the next tile's MFMAs run: lp/cp/pidx hold the
+    // previous tile (none before tile 0: -inf values with an index that
+    // never enters a top-m list).
+    f64x4 lp = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    double cp = 0.0;
+    int pidx = 0x7fffffff;
+    double cc = Ct[0][ci];
+    auto fold = [&]() {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const double l = lp[q] + cp;
+            lse_push(m[q], s[q], l);
+            if constexpr (TM > 0) top_push<TM>(tv[q], ti[q], l, pidx);
+        }
+    };
+    // pins the fold's results at this point of the instruction stream (the
+    // compiler would otherwise sink the arithmetic into a later tile)
+    auto pin_fold = [&]() {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(m[q]), "+v"(s[q]));
+    };
+    // One tile; its buffer index is a compile-time constant so that every
+    // LDS address is one base register plus an immediate offset.
+    auto tile_step = [&](int tile, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        constexpr int bnext = (buf + 1) % NBUF;
+        constexpr int bstore = (buf + 2) % NBUF;
+        // nothing moves between tiles (the fold of tile t-1 stays in tile t)
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (AHEAD) {
-            if (tile + 1 < ntiles) lstore(buf ^ 1);
-            // unconditional (clamped) so the registers are redefined every
-            // iteration instead of merged at the loop join
-            gload(tile + 2 < ntiles ? tile + 2 : ntiles - 1);
-        } else if (tile + 1 < ntiles) {
-            stage_now(tile + 1, buf ^ 1);
+            // unconditional: past the last tile these write a buffer that is
+            // never read again (the loads are clamped to the last tile)
+            lstore(bstore);
+            gload(tile + 3 < ntiles ? tile + 3 : ntiles - 1);
+        } else if (tile + 2 < ntiles) {
+            stage_now(tile + 2, bstore);
         }
         const double* pp = &Pt[buf][ci * PSTR + h * DPH];
         f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-        // coefficients stream from LDS through a two-batch register ring
-        constexpr int EB = DPH % 8 == 0 ? 8 : DPH;
-        double2 ring[2][EB / 2];
 #pragma unroll
-        for (int u = 0; u < EB / 2; ++u) ring[0][u] = *(const double2*)(pp + 2 * u);
-        __builtin_amdgcn_sched_group_barrier(0x100, EB / 2, 0);
-#pragma unroll
-        for (int bt = 0; bt < DPH / EB; ++bt) {
+        for (int bt = 0; bt < NBT; ++bt) {
             const int cur = bt & 1;
-            if (bt + 1 < DPH / EB) {
+            if (bt + 1 < NBT) {
 #pragma unroll
                 for (int u = 0; u < EB / 2; ++u)
                     ring[cur ^ 1][u] = *(const double2*)(pp + (bt + 1) * EB + 2 * u);
@@ -296,18 +337,46 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
                 acc = mfma4d(fe[t + 0], ring[cur][u].x, acc);
                 acc = mfma4d(fe[t + 1], ring[cur][u].y, acc);
             }
-            if (bt + 1 < DPH / EB) __builtin_amdgcn_sched_group_barrier(0x100, EB / 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, EB, 0);
-        }
-        const double c = Ct[buf][ci];
+            if (bt == 0) fold();
+            if (bt + 1 < NBT) __builtin_amdgcn_sched_group_barrier(0x100, EB / 2, 0);
+            if (bt == 0) {
+                // the previous tile's fold spread over this batch's MFMAs
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const double l = acc[q] + c;
-            lse_push(m[q], s[q], l);
-            if constexpr (TM > 0) top_push<TM>(tv[q], ti[q], l, tile * 16 + ci);
+                for (int u = 0; u < EB; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, TM > 0 ? 12 : 6, 0);
+                }
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, EB, 0);
+            }
         }
+        // the next tile's first batch and constant (written one iteration
+        // earlier), then this tile's result becomes the one to fold
+        {
+            const double* pn = &Pt[bnext][ci * PSTR + h * DPH];
+#pragma unroll
+            for (int u = 0; u < EB / 2; ++u) ring[0][u] = *(const double2*)(pn + 2 * u);
+        }
+        lp = acc;
+        cp = cc;
+        cc = Ct[bnext][ci];
+        pidx = tile * 16 + ci;
+        pin_fold();
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
+    int tile = 0;
+    for (; tile + 3 <= ntiles; tile += 3) {
+        tile_step(tile, B0{});
+        tile_step(tile + 1, B1{});
+        tile_step(tile + 2, B2{});
     }
+    if (tile < ntiles) tile_step(tile, B0{});
+    if (tile + 1 < ntiles) tile_step(tile + 1, B1{});
+    fold();
 
     // Merge the 16 lanes that hold the same rows (fixed butterfly order).
 #pragma unroll
