@@ -15,6 +15,10 @@ Two independent implementations of the same definition live here:
 ``kmeans_step`` (C) is one Lloyd step, the hard-assignment quantizer the
 pages compare the GMM with (same source, section 3).
 
+``ivf_lists`` (numpy) builds the inverted lists of an IVF coarse quantizer
+from soft top-m assignments: border vectors stored in several lists, as the
+Flash-GMM abstract describes for the GMM-based quantizer.
+
 The EM definition followed is the textbook diagonal-covariance one that the
 Flash-GMM pages tile ("Flash-GMM: A Memory-Efficient Kernel for Scalable Soft
 Clustering", section 1, responsibility matrix; section 3, EM with per-tile
@@ -244,3 +248,34 @@ def brute_em_step(x, w, mu, var, var_floor: float = 1e-6):
         v2[j] = np.maximum((r[:, j, None] * dev * dev).sum(axis=0) / nk[j], var_floor)
     w2[~live] = 0.0
     return w2, mu2, v2, float(lse.sum()), nk, r
+
+
+def ivf_lists(idx, resp, k: int, min_resp: float = 0.0):
+    """Inverted lists from top-m soft assignments.
+
+    idx (N, m) int component ids and resp (N, m) responsibilities, most
+    responsible first (as ``topm`` returns them). Row n is stored in the list
+    of idx[n, 0] and, for j >= 1, in the list of idx[n, j] when
+    resp[n, j] >= min_resp (the border-vector multi-assignment of the IVF
+    coarse quantizer; "Flash-GMM: A Memory-Efficient Kernel for Scalable Soft
+    Clustering", abstract and section 1). Entries whose id is outside [0, k)
+    are not stored. Each list holds its rows in increasing order.
+
+    Returns (offsets int64 (k + 1,), rows int32, values float32): list c is
+    rows[offsets[c]:offsets[c + 1]], with the responsibilities alongside.
+    """
+    idx = np.asarray(idx)
+    resp = np.asarray(resp, dtype=np.float32)
+    n, m = idx.shape
+    row = np.repeat(np.arange(n, dtype=np.int64), m)
+    col = np.tile(np.arange(m), n)
+    key = idx.reshape(-1).astype(np.int64)
+    val = resp.reshape(-1)
+    keep = (key >= 0) & (key < k) & ((col == 0) | (val >= np.float32(min_resp)))
+    key, row, val = key[keep], row[keep], val[keep]
+    # a stable sort by list id keeps each list's rows in entry (= row) order
+    order = np.argsort(key, kind="stable")
+    counts = np.bincount(key, minlength=k)
+    offsets = np.zeros(k + 1, dtype=np.int64)
+    np.cumsum(counts, out=offsets[1:])
+    return offsets, row[order].astype(np.int32), val[order]

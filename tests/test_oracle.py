@@ -398,3 +398,72 @@ def test_kmeans_empty_cluster_and_ties():
     np.testing.assert_array_equal(c2[2], c[2])
     np.testing.assert_array_equal(c2[3], [10.0, 10.0])
     assert inertia == pytest.approx(2.0, rel=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# IVF inverted lists from top-m soft assignments
+# ---------------------------------------------------------------------------
+def _ivf_by_loops(idx, resp, k, tau):
+    lists = [[] for _ in range(k)]
+    vals = [[] for _ in range(k)]
+    for r in range(idx.shape[0]):
+        for j in range(idx.shape[1]):
+            c = int(idx[r, j])
+            if not (0 <= c < k):
+                continue
+            if j == 0 or resp[r, j] >= np.float32(tau):
+                lists[c].append(r)
+                vals[c].append(resp[r, j])
+    return lists, vals
+
+
+def test_ivf_lists_worked_example():
+    idx = np.array([[2, 0], [0, 1], [2, 1], [1, 2]], np.int32)
+    resp = np.array([[0.6, 0.4], [0.9, 0.1], [0.5, 0.5], [0.7, 0.3]], np.float32)
+    off, rows, vals = oracle.ivf_lists(idx, resp, 3, 0.35)
+    np.testing.assert_array_equal(off, [0, 2, 4, 6])
+    np.testing.assert_array_equal(rows, [0, 1, 2, 3, 0, 2])
+    np.testing.assert_array_equal(vals, np.float32([0.4, 0.9, 0.5, 0.7, 0.6, 0.5]))
+    # threshold 0 keeps every entry; threshold above 1 keeps the top-1 only
+    off0, rows0, _ = oracle.ivf_lists(idx, resp, 3, 0.0)
+    np.testing.assert_array_equal(off0, [0, 2, 5, 8])
+    np.testing.assert_array_equal(rows0, [0, 1, 1, 2, 3, 0, 2, 3])
+    off2, rows2, _ = oracle.ivf_lists(idx, resp, 3, 2.0)
+    np.testing.assert_array_equal(off2, [0, 1, 2, 4])
+    np.testing.assert_array_equal(rows2, [1, 3, 0, 2])
+    # a responsibility equal to the threshold is kept
+    off5, rows5, _ = oracle.ivf_lists(idx, resp, 3, 0.5)
+    np.testing.assert_array_equal(off5, [0, 1, 3, 5])
+    np.testing.assert_array_equal(rows5, [1, 2, 3, 0, 2])
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.05, 0.3, 1.5])
+def test_ivf_lists_match_loops(tau):
+    rng = np.random.default_rng(61)
+    n, m, k = 700, 3, 23
+    idx = rng.integers(-2, k + 2, size=(n, m)).astype(np.int32)  # some ids out of range
+    resp = rng.uniform(0, 1, size=(n, m)).astype(np.float32)
+    off, rows, vals = oracle.ivf_lists(idx, resp, k, tau)
+    lists, lvals = _ivf_by_loops(idx, resp, k, tau)
+    assert off[0] == 0 and off[-1] == len(rows) == sum(len(a) for a in lists)
+    for c in range(k):
+        np.testing.assert_array_equal(rows[off[c]:off[c + 1]], lists[c])
+        np.testing.assert_array_equal(vals[off[c]:off[c + 1]], np.float32(lvals[c]))
+
+
+def test_ivf_lists_top1_is_the_hard_partition():
+    x, _, _ = dg.custom(3000, 6, 9, seed=62)
+    rng = np.random.default_rng(62)
+    w = np.full(9, 1 / 9)
+    mu = x[rng.choice(3000, 9, replace=False)].astype(np.float64)
+    var = np.ones((9, 6))
+    idx, resp, _ = oracle.topm(x, w, mu, var, 2)
+    off, rows, _ = oracle.ivf_lists(idx[:, :1], resp[:, :1], 9)
+    # every row exactly once, in the list of its most responsible component
+    assert len(rows) == 3000 and np.array_equal(np.sort(rows), np.arange(3000))
+    z = oracle.logdensity(x, w, mu, var).argmax(axis=1)
+    for c in range(9):
+        np.testing.assert_array_equal(rows[off[c]:off[c + 1]], np.nonzero(z == c)[0])
+    # with the second entry at threshold 0 every row sits in two lists
+    off2, rows2, _ = oracle.ivf_lists(idx, resp, 9, 0.0)
+    assert len(rows2) == 6000 and np.all(np.bincount(rows2, minlength=3000) == 2)
