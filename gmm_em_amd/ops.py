@@ -29,6 +29,9 @@ lib.gmm_loglik.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _i32, _vp
 lib.gmm_assign_topm.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp,
                                 _vp, _sz, _vp]
 lib.gmm_kmeans_step.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+lib.gmm_ivf_workspace_bytes.argtypes = [_i64, _i32, _i32]
+lib.gmm_ivf_workspace_bytes.restype = _sz
+lib.gmm_ivf_build.argtypes = [_vp, _vp, _i64, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.gmm_device_status.argtypes = [_vp, _vp]
 lib.gmm_status_string.argtypes = [ctypes.c_int]
 lib.gmm_status_string.restype = ctypes.c_char_p
@@ -37,7 +40,7 @@ lib.gmm_profile_begin.argtypes = [_i32]
 lib.gmm_profile_end.argtypes = [ctypes.POINTER(_f64), ctypes.POINTER(_i32), ctypes.POINTER(_f64),
                                 ctypes.POINTER(_i32)]
 for _f in (lib.gmm_em_step, lib.gmm_fit, lib.gmm_loglik, lib.gmm_assign_topm, lib.gmm_kmeans_step,
-           lib.gmm_device_status, lib.gmm_profile_begin, lib.gmm_profile_end):
+           lib.gmm_ivf_build, lib.gmm_device_status, lib.gmm_profile_begin, lib.gmm_profile_end):
     _f.restype = ctypes.c_int
 
 (GMM_OK, GMM_E_INVALID, GMM_E_DTYPE, GMM_E_WORKSPACE, GMM_E_PARAMS, GMM_E_HIP, GMM_E_UNSUPPORTED,
@@ -175,6 +178,33 @@ def kmeans_step(x, centroids, ws=None, assign: bool = True):
     _check(lib.gmm_kmeans_step(_ptr(x), x.shape[0], d, ldx, dt, _ptr(centroids), k, _ptr(z),
                                _ptr(inertia), _ptr(ws), ws.numel(), _stream(x.device)))
     return inertia, z
+
+
+def ivf_build(idx, resp, k: int, min_resp: float = 0.0, values: bool = True):
+    """Inverted lists from top-m assignments idx (N, m) int32 / resp (N, m) float32.
+
+    Returns (offsets int64 (k+1,), rows int32 (entries,), values float32 or
+    None); list c is rows[offsets[c]:offsets[c+1]]. Synchronises once to
+    size the outputs to the entries stored.
+    """
+    if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous() or not idx.is_cuda:
+        raise ValueError("idx must be a contiguous int32 (N, m) device tensor")
+    if resp is not None and (resp.dtype != torch.float32 or tuple(resp.shape) != tuple(idx.shape)
+                             or not resp.is_contiguous() or resp.device != idx.device):
+        raise ValueError("resp must be a contiguous float32 tensor shaped like idx")
+    n, m = idx.shape
+    nb = int(lib.gmm_ivf_workspace_bytes(n, m, k))
+    if nb == 0:
+        raise GmmError(GMM_E_UNSUPPORTED)
+    dev = idx.device
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    offsets = torch.empty(k + 1, dtype=torch.int64, device=dev)
+    rows = torch.empty(max(n * m, 1), dtype=torch.int32, device=dev)
+    vals = torch.empty(max(n * m, 1), dtype=torch.float32, device=dev) if values else None
+    _check(lib.gmm_ivf_build(_ptr(idx), _ptr(resp), n, m, k, min_resp, _ptr(offsets), _ptr(rows),
+                             _ptr(vals), _ptr(ws), nb, _stream(dev)))
+    total = int(offsets[k].item())
+    return offsets, rows[:total], (vals[:total] if values else None)
 
 
 def device_status(ws, device="cuda") -> int:

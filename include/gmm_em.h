@@ -139,6 +139,27 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
                     float* centroids, int32_t k, int32_t* assign_dev, double* inertia_dev,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Inverted lists of an IVF coarse quantizer from top-m soft assignments: the
+ * GMM responsibilities put border vectors in several lists ("Flash-GMM: A
+ * Memory-Efficient Kernel for Scalable Soft Clustering", abstract; the
+ * review page, section 1, for the IVF index). idx_dev and resp_dev (device,
+ * n*m int32 and floats, row-major n x m, most responsible first, as
+ * gmm_assign_topm writes them). Row r goes to list idx[r][0] and, for
+ * j >= 1, to list idx[r][j] when resp[r][j] >= min_resp; ids outside [0, k)
+ * are skipped. resp_dev may be NULL: then every entry is kept and the
+ * stored values are 1. Output (device): offsets_dev (k+1 int64; list c is
+ * entries offsets[c] .. offsets[c+1]-1, offsets[k] = entries stored),
+ * rows_dev (int32 row ids, capacity n*m; each list in increasing row order)
+ * and values_dev (the entries' responsibilities, capacity n*m, may be NULL).
+ * The result does not depend on scheduling (a stable counting sort).
+ * 1 <= k <= 16384 and n*m < 2^31 (GMM_E_UNSUPPORTED otherwise); min_resp
+ * must not be NaN. The workspace (device, 256-byte aligned) has
+ * gmm_ivf_workspace_bytes(n, m, k) bytes; it depends on n. */
+size_t gmm_ivf_workspace_bytes(int64_t n, int32_t m, int32_t k);
+int gmm_ivf_build(const int32_t* idx_dev, const float* resp_dev, int64_t n, int32_t m, int32_t k,
+                  float min_resp, int64_t* offsets_dev, int32_t* rows_dev, float* values_dev,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronises the stream and returns GMM_E_PARAMS if the last call that used
  * this workspace found invalid parameter values, GMM_E_SYNC if its
  * cooperative exchange timed out, GMM_OK otherwise, or GMM_E_HIP if the

@@ -25,7 +25,8 @@ def ops():
 
 def test_library_exports_every_declared_symbol(ops):
     names = _declared()
-    assert {"gmm_em_step", "gmm_fit", "gmm_loglik", "gmm_assign_topm", "gmm_kmeans_step"} <= set(names)
+    assert {"gmm_em_step", "gmm_fit", "gmm_loglik", "gmm_assign_topm", "gmm_kmeans_step",
+            "gmm_ivf_build"} <= set(names)
     for nm in names:
         assert hasattr(ops.lib, nm), nm
     assert ops.lib.gmm_version() >= 100
@@ -98,3 +99,23 @@ def test_kmeans_argument_checks(ops):
     assert km(1, 10, 4, 4, 0, 1, 2, None, None, 256, need - 1, None) == ops.GMM_E_WORKSPACE
     wide = ops.workspace_bytes(300, 2)
     assert km(1, 10, 300, 300, 0, 1, 2, None, None, 256, wide, None) == ops.GMM_E_UNSUPPORTED
+
+
+def test_ivf_workspace_and_argument_checks(ops):
+    wb = ops.lib.gmm_ivf_workspace_bytes
+    assert wb(1000, 2, 64) > 0 and wb(1000, 2, 64) % 256 == 0
+    assert wb(0, 2, 64) > 0                       # empty input still needs the counters
+    assert wb(1000, 2, 16385) == 0                # more lists than LDS counters
+    assert wb(1 << 30, 2, 64) == 0                # n*m beyond 32-bit positions
+    assert wb(-1, 2, 64) == 0 and wb(10, 0, 64) == 0 and wb(10, 2, 0) == 0
+    # the counters matrix stays bounded: tiles grow with n instead
+    assert wb(50_000_000, 2, 4096) <= (1 << 26) + 4096 * 4 + 512
+    b = ops.lib.gmm_ivf_build
+    need = wb(100, 2, 8)
+    assert b(1, 1, 100, 2, 8, 0.0, None, 1, None, 256, need, None) == ops.GMM_E_INVALID  # no offsets
+    assert b(None, 1, 100, 2, 8, 0.0, 1, 1, None, 256, need, None) == ops.GMM_E_INVALID  # no idx
+    assert b(1, 1, 100, 2, 8, float("nan"), 1, 1, None, 256, need, None) == ops.GMM_E_INVALID
+    assert b(1, 1, 100, 2, 8, 0.0, 1, 1, None, 256, need - 1, None) == ops.GMM_E_WORKSPACE
+    assert b(1, 1, 100, 2, 8, 0.0, 1, 1, None, 257, need, None) == ops.GMM_E_WORKSPACE
+    assert b(1, 1, 100, 2, 20000, 0.0, 1, 1, None, 256, need, None) == ops.GMM_E_UNSUPPORTED
+    assert b(1, 1, -5, 2, 8, 0.0, 1, 1, None, 256, need, None) == ops.GMM_E_INVALID
