@@ -9,7 +9,13 @@ sd U[2,10], Zipf(1.1) weights), EM started from K seeded rows with unit
 variances. Prints one JSON line.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--cpu-rows R]
+                       [--no-cpu-baseline] [--cpu-rows R] [--rows R]
+                       [--mode em|kmeans|assign]
+
+--mode kmeans times Lloyd (k-means) steps on the same data from the same
+seeded centroids instead (the quantizer the GMM replaces); --mode assign
+times the top-2 soft assignment pass followed by the IVF list construction.
+Both print one JSON line of their own metric; the default is the EM step.
 """
 from __future__ import annotations
 
@@ -66,6 +72,7 @@ def main() -> int:
     ap.add_argument("--rows", type=int, default=0,
                     help="time a prefix of this many rows instead of the workload's N (the "
                          "JSON line then reports the prefix; EM cost is linear in N)")
+    ap.add_argument("--mode", choices=("em", "kmeans", "assign"), default="em")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of the data matrix's size (calibrates the "
                          "HBM byte counters) and exit")
@@ -104,6 +111,8 @@ def main() -> int:
     else:
         xt = torch.from_numpy(x).to(dev)
     ws = ops.workspace(W.d, W.k, dev)
+    if args.mode != "em":
+        return _other_mode(args, W, x, xt, w0, m0, v0, ws, n_rows)
     th0 = [torch.from_numpy(a).to(dev) for a in (w0, m0, v0)]
     w, mu, var = (t.clone() for t in th0)
     ll = torch.empty(max(args.steps, 1), dtype=torch.float64, device=dev)
@@ -218,6 +227,92 @@ def main() -> int:
         "wall_s": round(wall, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _other_mode(args, W, x, xt, w0, m0, v0, ws, n_rows) -> int:
+    """k-means steps or the soft-assignment pass + IVF lists (see the module doc)."""
+    import torch
+
+    from gmm_em_amd import ops
+
+    dev = xt.device
+    chunk = 4096 if W.d > 128 else (1 << 22)
+    cfg = {"workload": f"{W.key}: N={n_rows} D={W.d} K={W.k} {W.dtype}"
+                       + ("" if n_rows == W.n else f" (row prefix of N={W.n})"),
+           "n": n_rows, "d": W.d, "k": W.k, "x_dtype": W.dtype}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    extra = {}
+    if args.mode == "kmeans":
+        c0 = torch.from_numpy(m0).to(dev)
+        c = c0.clone()
+        for _ in range(args.warmup):
+            ops.kmeans_step(xt, c, ws=ws, assign=False)
+        c.copy_(c0)
+        ops.profile_begin(args.steps * (-(-n_rows // chunk)) + 8)
+        torch.cuda.synchronize()
+        start.record()
+        inertia = []
+        for _ in range(args.steps):
+            inertia.append(ops.kmeans_step(xt, c, ws=ws, assign=False)[0])
+        stop.record()
+        torch.cuda.synchronize()
+        metric, unit = f"k-means (Lloyd) iterations/s, {W.key} workload (1 MI355X)", "k-means it/s"
+        extra["inertia_first_last"] = [float(inertia[0].item()), float(inertia[-1].item())]
+    else:
+        w, mu, var = (torch.from_numpy(a).to(dev) for a in (w0, m0, v0))
+        ops.em_step(xt, w, mu, var, W.var_floor, ws=ws)  # one EM step past the initial parameters
+        for _ in range(args.warmup):
+            ops.assign_topm(xt, w, mu, var, 2, ws=ws)
+        ops.profile_begin(args.steps * (-(-n_rows // chunk)) + 8)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            idx, resp = ops.assign_topm(xt, w, mu, var, 2, ws=ws)
+        stop.record()
+        torch.cuda.synchronize()
+        metric, unit = f"top-2 soft-assignment passes/s, {W.key} workload (1 MI355X)", "passes/s"
+        # the IVF lists from the last assignment (threshold 0.1 for the border copies)
+        ivf_ms = []
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            off, rows, _ = ops.ivf_build(idx, resp, W.k, 0.1)
+            b.record()
+            torch.cuda.synchronize()
+            ivf_ms.append(a.elapsed_time(b))
+        extra["ivf_build_ms"] = round(min(ivf_ms), 3)
+        extra["ivf_entries"] = int(rows.numel())
+    prof = ops.profile_end()
+    if ops.device_status(ws, dev) != ops.GMM_OK:
+        print("device status not ok", file=sys.stderr)
+        return 1
+    ms_step = start.elapsed_time(stop) / args.steps
+    (ms1, n1), (ms2, n2) = prof["pass1"], prof["pass2"]
+    kname, kms, kn = ("k_wide normaliser + k_wmerge (pass 1)" if W.d > 128 else "k_lse (pass 1)"), ms1, n1
+    if ms2 > ms1:
+        kname, kms, kn = "k_stats (pass 2, one-hot)", ms2, n2
+    flops_launch = 4.0 * W.d * W.k * n_rows / (kn / args.steps) if kname.endswith("(pass 1)") else None
+    avg_ms = kms / kn
+    achieved = flops_launch / (avg_ms * 1e-3) / 1e12 if flops_launch else None
+    out = {
+        "metric": metric, "value": round(1000.0 / ms_step, 4), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic", "config": cfg,
+        "roofline": {"kernel": kname, "bound": "mfma",
+                     "achieved": round(achieved, 2) if achieved else None,
+                     "peak": PEAK_FP64_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP64_MFMA_TFLOPS, 4) if achieved else None,
+                     "traffic": None, "avg_launch_ms": round(avg_ms, 4),
+                     "pass1_ms_per_step": round(ms1 / args.steps, 3),
+                     "pass2_ms_per_step": round(ms2 / args.steps, 3)},
+        "cpu_baseline": None,
+        **extra,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -324,7 +324,7 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
         prof_mark(1, false, st);
         if (e != hipSuccess) break;
         prof_mark(2, true, st);
-        e = launch_stats(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, st, zc);
+        e = launch_km_stats(pl, xc, cn, ldx, x_dtype, zc, ci > 0, st);
         prof_mark(2, false, st);
     }
     if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), inertia_dev ? inertia_dev : pl.ll_tmp, st, -1.0);

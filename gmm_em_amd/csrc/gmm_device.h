@@ -82,6 +82,24 @@ __device__ __forceinline__ void top_push(double (&tv)[TM], int (&ti)[TM], double
     }
 }
 
+// The same insertion when i is larger than the index of every entry already
+// in the list (a lane that pushes its components in increasing order): an
+// equal value then never displaces an entry, and an empty entry (index
+// 0x7fffffff) always takes the value, so no index comparison is needed.
+template <int TM>
+__device__ __forceinline__ void top_push_inc(double (&tv)[TM], int (&ti)[TM], double v, int i) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+        const bool gt = v > tv[j] || ti[j] == 0x7fffffff;
+        const double ov = tv[j];
+        const int oi = ti[j];
+        tv[j] = gt ? v : ov;
+        ti[j] = gt ? i : oi;
+        v = gt ? ov : v;
+        i = gt ? oi : i;
+    }
+}
+
 // Merge with the list of lane (lane ^ off): both lanes end with the same top
 // TM of the union.
 template <int TM>

@@ -63,10 +63,8 @@ hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, cons
 hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                       double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
                       hipStream_t st, int km = 0);
-// z non-null: k-means mode, one-hot responsibilities from the assignment z
-// (no E-step).
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                        const double* lse, int acc, hipStream_t st, const int32_t* z = nullptr);
+                        const double* lse, int acc, hipStream_t st);
 hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floor, float* w,
                            float* mu, float* var, hipStream_t st);
 // Cooperative single pass over all n rows with `groups` row groups (every
@@ -85,6 +83,10 @@ int coop_blocks_per_cu(int dp);
 int waves_per_stats_block(int dp);
 hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st,
                            double scale = 1.0);
+// k-means statistics: per (row group, K-tile) sums of x - s and counts of the
+// rows assigned (z) to each centroid, in the statistics partials' layout.
+hipError_t launch_km_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                           const int32_t* z, int acc, hipStream_t st);
 // k-means centroid update from the statistics partials.
 hipError_t launch_kmfinal(const Plan& pl, float* c, hipStream_t st);
 

@@ -296,7 +296,7 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         for (int q = 0; q < 4; ++q) {
             const double l = lp[q] + cp;
             lse_push(m[q], s[q], l);
-            if constexpr (TM > 0) top_push<TM>(tv[q], ti[q], l, pidx);
+            if constexpr (TM > 0) top_push_inc<TM>(tv[q], ti[q], l, pidx);
         }
     };
     // pins the fold's results at this point of the instruction stream (the
@@ -453,17 +453,13 @@ struct StatsGeom {
     static_assert(PER * NT == STATS_ROWS * DP, "every thread stages the same number of values");
 };
 
-// KM (k-means mode): the responsibilities are one-hot, r = [z(row) == slot]
-// with the assignment z of each row from the normaliser pass (zasg), so no
-// E-step runs; the M-step then only touches groups that hold a row assigned
-// to one of the wave's components.
-template <int DP, typename XT, bool KM>
+template <int DP, typename XT>
 __global__ __launch_bounds__(StatsGeom<DP>::NT, 1)
 void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
              const double* __restrict__ Pg, const double* __restrict__ cvec,
              const double* __restrict__ shift, int ntiles, const double* __restrict__ lse,
-             const int32_t* __restrict__ zasg, int64_t rows_per_group,
-             double* __restrict__ part, double* __restrict__ npart, int accumulate) {
+             int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
+             int accumulate) {
     using G = StatsGeom<DP>;
     constexpr int DPH = G::DPH, HS = G::HS, S = G::S, WV = G::WV, NT = G::NT, PER = G::PER;
     constexpr int NJ = DP / 16;  // 16-dim column blocks per power
@@ -489,8 +485,8 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int slot = tile * 16 + ci;
 
     // Stationary coefficients: P[slot][h][t], t = 0..DPH-1.
-    double pr[KM ? 1 : DPH];
-    if constexpr (!KM) {
+    double pr[DPH];
+    {
         const double* src = Pg + (int64_t)slot * 2 * DP + h * DPH;
 #pragma unroll
         for (int t = 0; t < DPH; t += 2) {
@@ -499,7 +495,7 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             pr[t + 1] = v.y;
         }
     }
-    const double cc = KM ? 0.0 : cvec[slot];
+    const double cc = cvec[slot];
 
     f64x4 acc[2 * NJ];
 #pragma unroll
@@ -539,20 +535,12 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             __builtin_amdgcn_make_buffer_rsrc((void*)(x + rbase * ldx), (short)0, xbytes, BUF_RSRC_WORD3);
 #pragma unroll
         for (int i = 0; i < PER; ++i) xv[i] = buf_load_x<XT>(xr, xoff[i]);
-        // normalisers: rows past the row group get +inf (responsibility 0);
-        // k-means mode: the assignment as a double, -1 past the row group
+        // normalisers: rows past the row group get +inf (responsibility 0)
+        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
         const int lrow = tid & (STATS_ROWS - 1);
-        if constexpr (KM) {
-            const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(zasg + rbase), (short)0, (int)(nv * (int64_t)sizeof(int32_t)), BUF_RSRC_WORD3);
-            const int zv = (int)__builtin_amdgcn_raw_buffer_load_b32(zr, lrow * 4, 0, 0);
-            lv = lrow < nv ? (double)zv : -1.0;
-        } else {
-            const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
-            const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
-            lv = lrow < nv ? v : INFINITY;
-        }
+        const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
+        lv = lrow < nv ? v : INFINITY;
     };
     // (several threads write the same normaliser: same value, same slot)
     auto storel = [&](double* lsb) { lsb[tid & (STATS_ROWS - 1)] = lv; };
@@ -602,11 +590,6 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             lsr[1][q] = ls[BUF][16 + 4 * q + h];
         }
         storel(ls[BUF ^ 1]);
-        if constexpr (KM) {
-            // no E-step: only the staging of tile it+1
-#pragma unroll
-            for (int i = 0; i < PER; ++i) store1(fs[BUF ^ 1], i);
-        } else {
         __builtin_amdgcn_sched_group_barrier(0x100, EB + 8, 0);
 #pragma unroll
         for (int bt = 0; bt < NB; ++bt) {
@@ -638,7 +621,6 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
                 if (u % 8 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
         }
-        }
         // the next-but-one tile's values are loaded once this tile's staging
         // registers have been written to LDS
         load(it + 2);
@@ -646,13 +628,8 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         double r[2][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if constexpr (KM) {
-                r[0][q] = lsr[0][q] == (double)slot ? 1.0 : 0.0;
-                r[1][q] = lsr[1][q] == (double)slot ? 1.0 : 0.0;
-            } else {
-                r[0][q] = (double)__expf((float)(e0[q] + cc - lsr[0][q]));
-                r[1][q] = (double)__expf((float)(e1[q] + cc - lsr[1][q]));
-            }
+            r[0][q] = (double)__expf((float)(e0[q] + cc - lsr[0][q]));
+            r[1][q] = (double)__expf((float)(e1[q] + cc - lsr[1][q]));
             n64 += r[0][q];
             n64 += r[1][q];
         }
@@ -1045,6 +1022,96 @@ __global__ void k_ll_final(const double* __restrict__ llpart, int nparts, double
         *out = (status[0] != 0 || status[1] == 0 || status[2] != 0) ? NAN : scale * red[0];
 }
 
+// k-means statistics (one-hot responsibilities from the assignment z): for
+// row group g and K-tile t (16 centroids), the sum of a = x - s over the rows
+// assigned to each centroid of the tile, and their count, in the layout of
+// the statistics pass's partials. The 8 waves of a block take consecutive
+// eighths of the row group; a wave walks its rows 64 at a time, selects the
+// rows assigned to the tile with a ballot, loads up to KMS_BATCH of them at
+// once and adds them, in row order, into its own LDS accumulator (each lane
+// owns two dims, so no two lanes touch one element). The eight accumulators
+// are summed in a fixed order at the end. Every row is read by exactly one
+// block; no MFMA work is needed.
+constexpr int KMS_WAVES = 8;
+constexpr int KMS_BATCH = 8;
+
+template <int DP, typename XT>
+__global__ __launch_bounds__(KMS_WAVES * 64)
+void k_km_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
+                const double* __restrict__ shift, const int32_t* __restrict__ z, int ntiles,
+                int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
+                int accumulate) {
+    static_assert(DP <= 128, "two dims per lane");
+    __shared__ double kacc[KMS_WAVES][16 * DP];
+    __shared__ int kcnt[KMS_WAVES][16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x / ntiles, tile = blockIdx.x - g * ntiles;
+    const int kp = ntiles * 16, c0 = tile * 16;
+    double* my = kacc[wave];
+    for (int i = lane; i < 16 * DP; i += 64) my[i] = 0.0;
+    if (lane < 16) kcnt[wave][lane] = 0;
+    constexpr int DPH = DP / 2;
+    const int dA = lane, dB = lane + 64;
+    const double sA = dA < d ? shift[(dA & 1) * DPH + (dA >> 1)] : 0.0;
+    const double sB = dB < d ? shift[(dB & 1) * DPH + (dB >> 1)] : 0.0;
+    const int64_t r0 = (int64_t)g * rows_per_group;
+    const int64_t r1 = r0 + rows_per_group < n ? r0 + rows_per_group : n;
+    const int64_t span = r1 > r0 ? r1 - r0 : 0;
+    const int64_t per = (span + KMS_WAVES - 1) / KMS_WAVES;
+    const int64_t wa = per * wave < span ? per * wave : span;
+    const int64_t wb = per * (wave + 1) < span ? per * (wave + 1) : span;
+    const int64_t w0 = r0 + wa, w1 = r0 + wb;
+    for (int64_t rb = w0; rb < w1; rb += 64) {
+        const int64_t r = rb + lane;
+        const int zc = (r < w1 ? z[r] : -1) - c0;
+        uint64_t mask = __builtin_amdgcn_ballot_w64((unsigned)zc < 16u);
+        while (mask) {
+            int cb[KMS_BATCH];
+            float xa[KMS_BATCH], xb[KMS_BATCH];
+            int nb = 0;
+#pragma unroll
+            for (int i = 0; i < KMS_BATCH; ++i) {
+                const bool v = mask != 0;  // uniform
+                const int b = v ? __builtin_ctzll(mask) : 0;
+                mask = v ? mask & (mask - 1) : mask;
+                nb += v ? 1 : 0;
+                cb[i] = __builtin_amdgcn_readlane(zc, b);
+                const XT* xr = x + (rb + b) * ldx;
+                xa[i] = (v && dA < d) ? load_x(xr + dA) : 0.0f;
+                xb[i] = (v && dB < d) ? load_x(xr + dB) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < KMS_BATCH; ++i) {
+                if (i < nb) {
+                    double* ar = my + cb[i] * DP;
+                    if (dA < d) ar[dA] += (double)xa[i] - sA;
+                    if (dB < d) ar[dB] += (double)xb[i] - sB;
+                    if (lane == 0) kcnt[wave][cb[i]] += 1;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < 16 * DP; i += KMS_WAVES * 64) {
+        const int cc = i / DP, dd = i - cc * DP;
+        if (dd < d) {
+            double sum = 0.0;
+#pragma unroll
+            for (int w = 0; w < KMS_WAVES; ++w) sum += kacc[w][i];
+            double* p = part + ((int64_t)g * kp + c0 + cc) * 2 * DP + dd;
+            *p = (accumulate ? *p : 0.0) + sum;
+        }
+    }
+    if (tid < 16) {
+        int cnt = 0;
+#pragma unroll
+        for (int w = 0; w < KMS_WAVES; ++w) cnt += kcnt[w][tid];
+        double* np = npart + (int64_t)g * kp + c0 + tid;
+        *np = (accumulate ? *np : 0.0) + (double)cnt;
+    }
+}
+
 // k-means update: c'[k] = s + S1[k] / N[k] for a non-empty cluster (fixed-
 // order fp64 sums over the row groups), the input centroid otherwise.
 __global__ void k_kmfinal(const double* __restrict__ part, const double* __restrict__ npart,
@@ -1086,25 +1153,20 @@ static hipError_t launch_lse_t(const Plan& pl, const void* x, int64_t n, int64_t
                                double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
                                int km, hipStream_t st) {
     if (m <= 0) return launch_lse_tm<DP, XT, 0>(pl, x, n, ldx, lse_out, ll_acc, 0, idx, resp, 0, st);
-    if (m <= 2) return launch_lse_tm<DP, XT, 2>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
+    if (m == 1) return launch_lse_tm<DP, XT, 1>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
+    if (m == 2) return launch_lse_tm<DP, XT, 2>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
     return launch_lse_tm<DP, XT, 4>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
 }
 
 template <int DP, typename XT>
 static hipError_t launch_stats_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
-                                 const double* lse, const int32_t* z, int acc, hipStream_t st) {
+                                 const double* lse, int acc, hipStream_t st) {
     using G = StatsGeom<DP>;
     int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
     if (rpg < STATS_ROWS) rpg = STATS_ROWS;
-    const dim3 grid(pl.ngroups * (pl.ntiles / G::WV));
-    if (z)
-        hipLaunchKernelGGL((k_stats<DP, XT, true>), grid, dim3(G::NT), 0, st, (const XT*)x, n,
-                           pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, z, rpg, pl.part,
-                           pl.npart, acc);
-    else
-        hipLaunchKernelGGL((k_stats<DP, XT, false>), grid, dim3(G::NT), 0, st, (const XT*)x, n,
-                           pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, z, rpg, pl.part,
-                           pl.npart, acc);
+    hipLaunchKernelGGL((k_stats<DP, XT>), dim3(pl.ngroups * (pl.ntiles / G::WV)), dim3(G::NT), 0, st,
+                       (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, rpg,
+                       pl.part, pl.npart, acc);
     return hipGetLastError();
 }
 
@@ -1126,13 +1188,37 @@ hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                        const double* lse, int acc, hipStream_t st, const int32_t* z) {
+template <int DP, typename XT>
+static hipError_t launch_km_stats_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
+                                    const int32_t* z, int acc, hipStream_t st) {
+    int64_t rpg = (n + pl.ngroups - 1) / pl.ngroups;
+    if (rpg < 1) rpg = 1;
+    hipLaunchKernelGGL((k_km_stats<DP, XT>), dim3(pl.ngroups * pl.ntiles), dim3(KMS_WAVES * 64), 0,
+                       st, (const XT*)x, n, pl.d, ldx, pl.shift, z, pl.ntiles, rpg, pl.part,
+                       pl.npart, acc);
+    return hipGetLastError();
+}
+
+hipError_t launch_km_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                           const int32_t* z, int acc, hipStream_t st) {
     switch (pl.dp) {
-#define CASE(DPV)                                                                       \
-    case DPV:                                                                           \
-        return dtype == 0 ? launch_stats_t<DPV, float>(pl, x, n, ldx, lse, z, acc, st) \
-                          : launch_stats_t<DPV, uint16_t>(pl, x, n, ldx, lse, z, acc, st);
+#define CASE(DPV)                                                                      \
+    case DPV:                                                                          \
+        return dtype == 0 ? launch_km_stats_t<DPV, float>(pl, x, n, ldx, z, acc, st) \
+                          : launch_km_stats_t<DPV, uint16_t>(pl, x, n, ldx, z, acc, st);
+        GMM_DP_CASES(CASE)
+#undef CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                        const double* lse, int acc, hipStream_t st) {
+    switch (pl.dp) {
+#define CASE(DPV)                                                                    \
+    case DPV:                                                                        \
+        return dtype == 0 ? launch_stats_t<DPV, float>(pl, x, n, ldx, lse, acc, st) \
+                          : launch_stats_t<DPV, uint16_t>(pl, x, n, ldx, lse, acc, st);
         GMM_DP_CASES(CASE)
 #undef CASE
     }
