@@ -87,7 +87,19 @@ __global__ __launch_bounds__(256) void k_ivf_colscan(int32_t* __restrict__ mat, 
     const int c = blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= k) return;
     int32_t run = 0;
-    for (int64_t t = 0; t < ntiles; ++t) {
+    int64_t t = 0;
+    // eight tiles' counts in flight at a time
+    for (; t + 8 <= ntiles; t += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = mat[(t + u) * k + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            mat[(t + u) * k + c] = run;
+            run += v[u];
+        }
+    }
+    for (; t < ntiles; ++t) {
         const int32_t v = mat[t * k + c];
         mat[t * k + c] = run;
         run += v;

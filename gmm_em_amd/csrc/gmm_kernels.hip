@@ -1026,14 +1026,16 @@ __global__ void k_ll_final(const double* __restrict__ llpart, int nparts, double
 // row group g and K-tile t (16 centroids), the sum of a = x - s over the rows
 // assigned to each centroid of the tile, and their count, in the layout of
 // the statistics pass's partials. The 8 waves of a block take consecutive
-// eighths of the row group; a wave walks its rows 64 at a time, selects the
-// rows assigned to the tile with a ballot, loads up to KMS_BATCH of them at
-// once and adds them, in row order, into its own LDS accumulator (each lane
+// eighths of the row group; a wave walks its rows 64 at a time (the
+// assignments of KMS_ZB such chunks loaded together), selects the rows
+// assigned to the tile with a ballot, loads up to KMS_BATCH of them at once
+// and adds them, in row order, into its own LDS accumulator (each lane
 // owns two dims, so no two lanes touch one element). The eight accumulators
 // are summed in a fixed order at the end. Every row is read by exactly one
 // block; no MFMA work is needed.
 constexpr int KMS_WAVES = 8;
-constexpr int KMS_BATCH = 8;
+constexpr int KMS_BATCH = 16;  // matched rows loaded at once
+constexpr int KMS_ZB = 8;      // 64-row chunks of assignments loaded at once
 
 template <int DP, typename XT>
 __global__ __launch_bounds__(KMS_WAVES * 64)
@@ -1042,19 +1044,24 @@ void k_km_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
                 int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
                 int accumulate) {
     static_assert(DP <= 128, "two dims per lane");
-    __shared__ double kacc[KMS_WAVES][16 * DP];
+    constexpr int KS = 128;  // accumulator row stride: every lane's two dims fit
+    __shared__ double kacc[KMS_WAVES][16 * KS];
     __shared__ int kcnt[KMS_WAVES][16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = blockIdx.x / ntiles, tile = blockIdx.x - g * ntiles;
     const int kp = ntiles * 16, c0 = tile * 16;
     double* my = kacc[wave];
-    for (int i = lane; i < 16 * DP; i += 64) my[i] = 0.0;
+    for (int i = lane; i < 16 * KS; i += 64) my[i] = 0.0;
     if (lane < 16) kcnt[wave][lane] = 0;
     constexpr int DPH = DP / 2;
     const int dA = lane, dB = lane + 64;
     const double sA = dA < d ? shift[(dA & 1) * DPH + (dA >> 1)] : 0.0;
     const double sB = dB < d ? shift[(dB & 1) * DPH + (dB >> 1)] : 0.0;
+    // a row is read through a buffer resource that ends after its d values:
+    // lanes past d read 0 (and add 0 to accumulator padding), no branches
+    const uint32_t oA = (uint32_t)(dA * sizeof(XT)), oB = (uint32_t)(dB * sizeof(XT));
+    const int rbytes = (int)(d * sizeof(XT));
     const int64_t r0 = (int64_t)g * rows_per_group;
     const int64_t r1 = r0 + rows_per_group < n ? r0 + rows_per_group : n;
     const int64_t span = r1 > r0 ? r1 - r0 : 0;
@@ -1062,39 +1069,51 @@ void k_km_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int64_t wa = per * wave < span ? per * wave : span;
     const int64_t wb = per * (wave + 1) < span ? per * (wave + 1) : span;
     const int64_t w0 = r0 + wa, w1 = r0 + wb;
-    for (int64_t rb = w0; rb < w1; rb += 64) {
-        const int64_t r = rb + lane;
-        const int zc = (r < w1 ? z[r] : -1) - c0;
-        uint64_t mask = __builtin_amdgcn_ballot_w64((unsigned)zc < 16u);
-        while (mask) {
-            int cb[KMS_BATCH];
-            float xa[KMS_BATCH], xb[KMS_BATCH];
-            int nb = 0;
+    // the assignments of KMS_ZB chunks of 64 rows are loaded at once
+    for (int64_t rz = w0; rz < w1; rz += 64 * KMS_ZB) {
+        int zc[KMS_ZB];
 #pragma unroll
-            for (int i = 0; i < KMS_BATCH; ++i) {
-                const bool v = mask != 0;  // uniform
-                const int b = v ? __builtin_ctzll(mask) : 0;
-                mask = v ? mask & (mask - 1) : mask;
-                nb += v ? 1 : 0;
-                cb[i] = __builtin_amdgcn_readlane(zc, b);
-                const XT* xr = x + (rb + b) * ldx;
-                xa[i] = (v && dA < d) ? load_x(xr + dA) : 0.0f;
-                xb[i] = (v && dB < d) ? load_x(xr + dB) : 0.0f;
-            }
+        for (int u = 0; u < KMS_ZB; ++u) {
+            const int64_t r = rz + 64 * u + lane;
+            zc[u] = (r < w1 ? z[r] : -1) - c0;
+        }
 #pragma unroll
-            for (int i = 0; i < KMS_BATCH; ++i) {
-                if (i < nb) {
-                    double* ar = my + cb[i] * DP;
-                    if (dA < d) ar[dA] += (double)xa[i] - sA;
-                    if (dB < d) ar[dB] += (double)xb[i] - sB;
-                    if (lane == 0) kcnt[wave][cb[i]] += 1;
+        for (int u = 0; u < KMS_ZB; ++u) {
+            const int64_t rb = rz + 64 * u;
+            uint64_t mask = __builtin_amdgcn_ballot_w64((unsigned)zc[u] < 16u);
+            while (mask) {
+                int cb[KMS_BATCH];
+                float xa[KMS_BATCH], xb[KMS_BATCH];
+                int nb = 0;
+#pragma unroll
+                for (int i = 0; i < KMS_BATCH; ++i) {
+                    // past the last selected row: row rb again (its values
+                    // are loaded but not added)
+                    const bool v = mask != 0;  // uniform
+                    const int b = v ? __builtin_ctzll(mask) : 0;
+                    mask = v ? mask & (mask - 1) : mask;
+                    nb += v ? 1 : 0;
+                    cb[i] = __builtin_amdgcn_readlane(zc[u], b);
+                    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                        (void*)(x + (rb + b) * ldx), (short)0, rbytes, BUF_RSRC_WORD3);
+                    xa[i] = buf_load_x<XT>(xr, oA);
+                    xb[i] = buf_load_x<XT>(xr, oB);
+                }
+#pragma unroll
+                for (int i = 0; i < KMS_BATCH; ++i) {
+                    if (i < nb) {
+                        double* ar = my + cb[i] * KS;
+                        ar[dA] += (double)xa[i] - sA;
+                        ar[dB] += (double)xb[i] - sB;
+                        if (lane == 0) kcnt[wave][cb[i]] += 1;
+                    }
                 }
             }
         }
     }
     __syncthreads();
-    for (int i = tid; i < 16 * DP; i += KMS_WAVES * 64) {
-        const int cc = i / DP, dd = i - cc * DP;
+    for (int i = tid; i < 16 * KS; i += KMS_WAVES * 64) {
+        const int cc = i / KS, dd = i - cc * KS;
         if (dd < d) {
             double sum = 0.0;
 #pragma unroll
