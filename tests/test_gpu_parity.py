@@ -162,6 +162,16 @@ def test_embed_prefix_per_step(ops):
     print("embed per-step worst", worst)
 
 
+def test_embed_full_per_step(ops):
+    # the embedding-like workload at its full size (N = 1,000,000, D = 128,
+    # K = 256), three EM steps from the seeded initial parameters
+    W = dg.WORKLOADS["embed"]
+    x = dg.rows(W)
+    w0, m0, v0 = dg.init_params(W, x)
+    worst = _per_step(ops, x, w0, m0, v0, 3, W.var_floor, label="embed full")
+    print("embed full-size per-step worst", worst)
+
+
 def test_descriptor_prefix_per_step(ops):
     # integer descriptor data: after one step some components sit at the
     # variance floor in some dims (w = 1e6), the hardest case for the
