@@ -251,7 +251,7 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 
     // Above D = 96 (or with the longer top-m lists) the register budget is
     // spent: tile t+2 is loaded and stored at the top of iteration t.
-    constexpr bool AHEAD = DP <= 96 && TM <= 2;
+    constexpr bool AHEAD = DP <= 128 && TM <= 2;
     auto stage_now = [&](int tile, int buf) {
         const double* src = Pg + (int64_t)tile * 16 * 2 * DP;
         for (int i = tid; i < 16 * DP; i += NT) {  // pairs of doubles
