@@ -126,8 +126,14 @@ __device__ __forceinline__ void wide_coefs(double (&pr)[DS / 2], const double* P
 // (h, ci) -> row 4q + h, component ci): one chain of DS/2 MFMAs; the A
 // values stream from LDS through a two-batch register ring of EB dim groups
 // (the scheduling barrier keeps the compiler from hoisting further reads).
-template <int DS>
-__device__ __forceinline__ f64x4 wide_estep(const double* pa, const double (&pr)[DS / 2]) {
+// hook(bt) runs after batch bt's MFMAs are issued: independent work placed
+// there overlaps the MFMA chain.
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+template <int DS, typename Hook = NoHook>
+__device__ __forceinline__ f64x4 wide_estep(const double* pa, const double (&pr)[DS / 2],
+                                            Hook&& hook = Hook()) {
     constexpr int T1 = DS / 4, EB = 4;
     static_assert(T1 % EB == 0, "whole E batches");
     f64x4 e = {0.0, 0.0, 0.0, 0.0};
@@ -148,6 +154,7 @@ __device__ __forceinline__ f64x4 wide_estep(const double* pa, const double (&pr)
             e = mfma4d(v, pr[2 * j], e);
             e = mfma4d(v * v, pr[2 * j + 1], e);
         }
+        hook(bt);
         __builtin_amdgcn_sched_barrier(0);
     }
     return e;
@@ -165,11 +172,13 @@ void k_wlse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             const double* __restrict__ Pg, const double* __restrict__ cvec,
             const double* __restrict__ shift, int ntiles, int64_t rows_per_group,
             double2* __restrict__ lpart, double* __restrict__ tval, int32_t* __restrict__ tidx) {
-    constexpr int NW = 8, NT = 512, DS = DP / NW, RS = DP + 4;
+    // RS (tile row stride, doubles) is odd: the 16 lanes of an E-step read
+    // (16 rows, one dim) then hit 16 distinct pairs of the 32 LDS banks
+    constexpr int NW = 8, NT = 512, DS = DP / NW, RS = DP + 1;
     constexpr int TMA = TM > 0 ? TM : 1;
     __shared__ __attribute__((aligned(16))) double fa[WROWS * RS];
     __shared__ double shl[DP];
-    __shared__ __attribute__((aligned(16))) f64x4 xb[NW][64];
+    __shared__ __attribute__((aligned(16))) f64x4 xb[2][NW][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -191,47 +200,80 @@ void k_wlse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     WideStage<DP, NT, XT> stg(x, ldx, d, gr0, gr1, tid);
     const double* pa = fa + ci * RS + w * DS + h;
 
+    // Waves 0-3 fold tile it's partials (row 4q + h, q = wave) into per
+    // (row, K-tile) results while tile it+1's E-step runs: the reduction is
+    // split into steps placed after the E-step's MFMA batches. The partials
+    // alternate between two buffers, so a tile's are read one iteration
+    // after they were written, with the tile's barriers in between.
+    const int wq = __builtin_amdgcn_readfirstlane(w);
+    double rl = 0.0, rm = -1.0e300, rs = 0.0;
+    double tv[TMA];
+    int ti[TMA];
+    auto red_start = [&](int buf) {
+        const int q = wq;
+        double l = xb[buf][0][lane][q];
+#pragma unroll
+        for (int v = 1; v < NW; ++v) l += xb[buf][v][lane][q];
+        rl = l + cc;
+        rm = rl > -1.0e300 ? rl : -1.0e300;
+        rs = rl > -1.0e300 ? 1.0 : 0.0;
+#pragma unroll
+        for (int j = 0; j < TMA; ++j) { tv[j] = -INFINITY; ti[j] = 0x7fffffff; }
+        if constexpr (TM > 0) top_push<TM>(tv, ti, rl, slot);
+    };
+    auto red_round = [&](int off) {
+        const double m2 = shfl_xor_d(rm, off);
+        const double s2 = shfl_xor_d(rs, off);
+        const double mn = fmax(rm, m2);
+        rs = rs * (double)__expf((float)(rm - mn)) + s2 * (double)__expf((float)(m2 - mn));
+        rm = mn;
+        if constexpr (TM > 0) top_merge<TM>(tv, ti, off);
+    };
+    auto red_store = [&](int64_t rt) {
+        const int64_t row = gr0 + rt * WROWS + 4 * wq + h;
+        if (ci == 0 && row < gr1) {
+            lpart[row * ntiles + kt] = double2{rm, rs};
+            if constexpr (TM > 0) {
+#pragma unroll
+                for (int j = 0; j < TM; ++j) {
+                    tval[(row * ntiles + kt) * TM + j] = tv[j];
+                    tidx[(row * ntiles + kt) * TM + j] = ti[j];
+                }
+            }
+        }
+    };
+    // the reduction's six steps (start, four butterfly rounds, store) spread
+    // evenly over the E-step's NB batches
+    constexpr int NB = DS / 16;
+
     if (ntr > 0) stg.load(0);
     for (int64_t it = 0; it < ntr; ++it) {
         __syncthreads();  // every wave is done with the previous tile's LDS
         stg.template store<RS>(fa, shl, tid);
         __syncthreads();
         if (it + 1 < ntr) stg.load(it + 1);
-        xb[w][lane] = wide_estep<DS>(pa, pr);
+        const int cur = (int)(it & 1);
+        const bool red = wq < 4 && it > 0;  // wave-uniform
+        auto hook = [&](int bt) {
+            if (!red) return;
+#pragma unroll
+            for (int k = 0; k < 6; ++k) {
+                if (k * NB / 6 != bt) continue;
+                if (k == 0) red_start(cur ^ 1);
+                else if (k <= 4) red_round(1 << (k - 1));
+                else red_store(it - 1);
+            }
+        };
+        xb[cur][w][lane] = wide_estep<DS>(pa, pr, hook);
+    }
+    if (ntr > 0) {
         __syncthreads();
-        if (w < 4) {
-            const int q = w;
-            double l = xb[0][lane][q];
-#pragma unroll
-            for (int v = 1; v < NW; ++v) l += xb[v][lane][q];
-            l += cc;
-            double m = l > -1.0e300 ? l : -1.0e300;
-            double sm = l > -1.0e300 ? 1.0 : 0.0;
-            double tv[TMA];
-            int ti[TMA];
-#pragma unroll
-            for (int j = 0; j < TMA; ++j) { tv[j] = -INFINITY; ti[j] = 0x7fffffff; }
-            if constexpr (TM > 0) top_push<TM>(tv, ti, l, slot);
+        if (wq < 4) {
+            const int last = (int)((ntr - 1) & 1);
+            red_start(last);
 #pragma unroll 1
-            for (int off = 1; off < 16; off <<= 1) {
-                const double m2 = shfl_xor_d(m, off);
-                const double s2 = shfl_xor_d(sm, off);
-                const double mn = fmax(m, m2);
-                sm = sm * (double)__expf((float)(m - mn)) + s2 * (double)__expf((float)(m2 - mn));
-                m = mn;
-                if constexpr (TM > 0) top_merge<TM>(tv, ti, off);
-            }
-            const int64_t row = gr0 + it * WROWS + 4 * q + h;
-            if (ci == 0 && row < gr1) {
-                lpart[row * ntiles + kt] = double2{m, sm};
-                if constexpr (TM > 0) {
-#pragma unroll
-                    for (int j = 0; j < TM; ++j) {
-                        tval[(row * ntiles + kt) * TM + j] = tv[j];
-                        tidx[(row * ntiles + kt) * TM + j] = ti[j];
-                    }
-                }
-            }
+            for (int off = 1; off < 16; off <<= 1) red_round(off);
+            red_store(ntr - 1);
         }
     }
 }
@@ -254,7 +296,8 @@ void k_wstats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
               const double* __restrict__ shift, int ntiles, int64_t rows_per_group,
               const double* __restrict__ lse, double* __restrict__ part,
               double* __restrict__ npart, int accumulate) {
-    constexpr int NT = 512, NS = 4, DS = DP / NS, RS = DP + 4, NJ = DS / 16;
+    // odd tile row stride: conflict-free E-step reads (see k_wlse)
+    constexpr int NT = 512, NS = 4, DS = DP / NS, RS = DP + 1, NJ = DS / 16;
     // fp32 rows: the M waves copy the next tile's raw values into LDS with
     // buffer-to-LDS loads during the E phase, so no thread holds them in
     // registers (one dword per lane: the LDS copy has the rows' own layout).
