@@ -216,19 +216,18 @@ void k_wlse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         for (int v = 1; v < NW; ++v) l += xb[buf][v][lane][q];
         rl = l + cc;
         rm = rl > -1.0e300 ? rl : -1.0e300;
-        rs = rl > -1.0e300 ? 1.0 : 0.0;
 #pragma unroll
         for (int j = 0; j < TMA; ++j) { tv[j] = -INFINITY; ti[j] = 0x7fffffff; }
         if constexpr (TM > 0) top_push<TM>(tv, ti, rl, slot);
     };
-    auto red_round = [&](int off) {
-        const double m2 = shfl_xor_d(rm, off);
-        const double s2 = shfl_xor_d(rs, off);
-        const double mn = fmax(rm, m2);
-        rs = rs * (double)__expf((float)(rm - mn)) + s2 * (double)__expf((float)(m2 - mn));
-        rm = mn;
+    // the tile's 16 components: max over the 16 lanes, then one exponential
+    // per lane and a sum over the 16 lanes (fixed butterfly orders)
+    auto red_max = [&](int off) {
+        rm = fmax(rm, shfl_xor_d(rm, off));
         if constexpr (TM > 0) top_merge<TM>(tv, ti, off);
     };
+    auto red_exp = [&]() { rs = (double)__expf((float)(rl - rm)); };
+    auto red_sum = [&](int off) { rs += shfl_xor_d(rs, off); };
     auto red_store = [&](int64_t rt) {
         const int64_t row = gr0 + rt * WROWS + 4 * wq + h;
         if (ci == 0 && row < gr1) {
@@ -242,9 +241,17 @@ void k_wlse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             }
         }
     };
-    // the reduction's six steps (start, four butterfly rounds, store) spread
-    // evenly over the E-step's NB batches
+    // the reduction's eleven steps (start, four max rounds, exponential, four
+    // sum rounds, store) spread evenly over the E-step's NB batches
     constexpr int NB = DS / 16;
+    constexpr int NSTEP = 11;
+    auto red_step = [&](int k, int buf, int64_t rt) {
+        if (k == 0) red_start(buf);
+        else if (k <= 4) red_max(1 << (k - 1));
+        else if (k == 5) red_exp();
+        else if (k <= 9) red_sum(1 << (k - 6));
+        else red_store(rt);
+    };
 
     if (ntr > 0) stg.load(0);
     for (int64_t it = 0; it < ntr; ++it) {
@@ -257,23 +264,16 @@ void k_wlse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         auto hook = [&](int bt) {
             if (!red) return;
 #pragma unroll
-            for (int k = 0; k < 6; ++k) {
-                if (k * NB / 6 != bt) continue;
-                if (k == 0) red_start(cur ^ 1);
-                else if (k <= 4) red_round(1 << (k - 1));
-                else red_store(it - 1);
-            }
+            for (int k = 0; k < NSTEP; ++k)
+                if (k * NB / NSTEP == bt) red_step(k, cur ^ 1, it - 1);
         };
         xb[cur][w][lane] = wide_estep<DS>(pa, pr, hook);
     }
     if (ntr > 0) {
         __syncthreads();
         if (wq < 4) {
-            const int last = (int)((ntr - 1) & 1);
-            red_start(last);
-#pragma unroll 1
-            for (int off = 1; off < 16; off <<= 1) red_round(off);
-            red_store(ntr - 1);
+#pragma unroll
+            for (int k = 0; k < NSTEP; ++k) red_step(k, (int)((ntr - 1) & 1), ntr - 1);
         }
     }
 }
@@ -359,11 +359,19 @@ void k_wstats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         double* dst = fa + sr * RS + sl;
         const float* src = xraw + sr * DP + sl;
         // (a few values at a time: the M waves hold their accumulators here)
+        if (d == DP) {  // (uniform) no padding dims: no select
 #pragma unroll
-        for (int u = 0; u < PR; ++u) {
-            const float v = u < nvalid ? src[TPR * u] : 0.0f;
-            dst[TPR * u] = (double)v - shl[sl + TPR * u];
-            if (u % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            for (int u = 0; u < PR; ++u) {
+                dst[TPR * u] = (double)src[TPR * u] - shl[sl + TPR * u];
+                if (u % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < PR; ++u) {
+                const float v = u < nvalid ? src[TPR * u] : 0.0f;
+                dst[TPR * u] = (double)v - shl[sl + TPR * u];
+                if (u % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
     auto stage = [&](int64_t it) {
