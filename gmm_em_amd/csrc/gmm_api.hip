@@ -308,7 +308,6 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
     int rc = check_common(x, n, d, ldx, x_dtype, centroids, centroids, centroids, k, workspace,
                           workspace_bytes, &pl);
     if (rc) return rc;
-    if (pl.wide) return GMM_E_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
     // weights and variances null: the k-means coefficients (2c, -1, -|c|^2)
     hipError_t e = launch_prologue(pl, nullptr, centroids, nullptr, st);
@@ -320,11 +319,13 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
         // normaliser scratch (CHUNK_ROWS doubles hold CHUNK_ROWS int32)
         int32_t* zc = assign_dev ? assign_dev + c0 : (int32_t*)pl.lse;
         prof_mark(1, true, st);
-        e = launch_lse(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, 1, zc, nullptr, st, 1);
+        e = pl.wide ? launch_wide_lse(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, 1, zc, nullptr, st, 1)
+                    : launch_lse(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, 1, zc, nullptr, st, 1);
         prof_mark(1, false, st);
         if (e != hipSuccess) break;
         prof_mark(2, true, st);
-        e = launch_km_stats(pl, xc, cn, ldx, x_dtype, zc, ci > 0, st);
+        e = pl.wide ? launch_wide_km_stats(pl, xc, cn, ldx, x_dtype, zc, ci > 0, st)
+                    : launch_km_stats(pl, xc, cn, ldx, x_dtype, zc, ci > 0, st);
         prof_mark(2, false, st);
     }
     if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), inertia_dev ? inertia_dev : pl.ll_tmp, st, -1.0);

@@ -76,9 +76,12 @@ hipError_t launch_coop(const Plan& pl, const void* x, int64_t n, int64_t ldx, in
 // statistics pass.
 hipError_t launch_wide_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                            double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                           hipStream_t st);
+                           hipStream_t st, int km = 0);
 hipError_t launch_wide_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                              const double* lse, int acc, hipStream_t st);
+// k-means statistics of the wide path (one dim slice per wave)
+hipError_t launch_wide_km_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                                const int32_t* z, int acc, hipStream_t st);
 int coop_blocks_per_cu(int dp);
 int waves_per_stats_block(int dp);
 hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st,

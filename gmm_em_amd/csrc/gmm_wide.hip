@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256)
 void k_wmerge(const double2* __restrict__ lpart, const double* __restrict__ tval,
               const int32_t* __restrict__ tidx, int ntiles, int64_t n, int k,
               double* __restrict__ lse_out, double* __restrict__ llpart, int ll_accumulate,
-              int m_out, int32_t* __restrict__ idx_out, float* __restrict__ resp_out) {
+              int m_out, int32_t* __restrict__ idx_out, float* __restrict__ resp_out, int km) {
     constexpr int TMA = TM > 0 ? TM : 1;
     __shared__ double rowll[LL_ROWS];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -526,14 +526,17 @@ void k_wmerge(const double2* __restrict__ lpart, const double* __restrict__ tval
                 m = mn;
                 if constexpr (TM > 0) top_merge<TM>(tv, ti, off);
             }
+            // k-means mode: the row's value is its best log-density,
+            // -|x - c_z|^2 (the row's contribution to -inertia)
             v = m + log(s);
+            if constexpr (TM > 0) v = km ? tv[0] : v;
             if (lane == 0) {
                 if (lse_out) lse_out[row] = v;
                 if constexpr (TM > 0) {
                     for (int q = 0; q < m_out; ++q) {
                         const int sl = ti[q];
                         idx_out[row * m_out + q] = sl < k ? sl : -1;
-                        resp_out[row * m_out + q] = __expf((float)(tv[q] - v));
+                        if (resp_out) resp_out[row * m_out + q] = __expf((float)(tv[q] - v));
                     }
                 }
             }
@@ -546,6 +549,99 @@ void k_wmerge(const double2* __restrict__ lpart, const double* __restrict__ tval
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) tot += shfl_xor_d(tot, off);
         if (lane == 0) llpart[blockIdx.x] = (ll_accumulate ? llpart[blockIdx.x] : 0.0) + tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k-means statistics (wide): the one-hot counterpart of the statistics pass.
+// A block owns (row group, 16-centroid K-tile); wave w owns dim slice w (of
+// 8, DP/8 dims) and walks all the group's rows in order: it selects the rows
+// assigned to the tile with a ballot, loads the slice of up to KMW_BATCH of
+// them at once (per-row buffer resources: dims past d or past the slice read
+// 0) and adds them, in row order, into its LDS accumulator (a lane owns one
+// or two dims). Each (centroid, dim) has one owner, so no cross-wave sum.
+// ---------------------------------------------------------------------------
+constexpr int KMW_BATCH = 16;
+constexpr int KMW_ZB = 8;
+
+template <int DP, typename XT>
+__global__ __launch_bounds__(512)
+void k_km_wstats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
+                 const double* __restrict__ shift, const int32_t* __restrict__ z, int ntiles,
+                 int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
+                 int accumulate) {
+    constexpr int NW = 8, DPW = DP / NW, KS = 128;
+    static_assert(DPW <= 128, "two dims per lane");
+    __shared__ double kacc[NW][16 * KS];
+    __shared__ int kcnt[16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x / ntiles, tile = blockIdx.x - g * ntiles;
+    const int kp = ntiles * 16, c0 = tile * 16;
+    double* my = kacc[w];
+    for (int i = lane; i < 16 * KS; i += 64) my[i] = 0.0;
+    if (tid < 16) kcnt[tid] = 0;
+    const int d0 = w * DPW;  // first dim of the slice
+    const int dA = lane, dB = lane + 64;  // slice-relative dims of this lane
+    const double sA = (dA < DPW && d0 + dA < d) ? shift[((d0 + dA) & 1) * (DP / 2) + ((d0 + dA) >> 1)] : 0.0;
+    const double sB = (dB < DPW && d0 + dB < d) ? shift[((d0 + dB) & 1) * (DP / 2) + ((d0 + dB) >> 1)] : 0.0;
+    int sbytes = d - d0;
+    sbytes = sbytes < 0 ? 0 : (sbytes > DPW ? DPW : sbytes);
+    sbytes *= (int)sizeof(XT);
+    const uint32_t oA = (uint32_t)(dA * sizeof(XT)), oB = (uint32_t)(dB * sizeof(XT));
+    const int64_t r0 = (int64_t)g * rows_per_group;
+    const int64_t r1 = r0 + rows_per_group < n ? r0 + rows_per_group : n;
+    __syncthreads();
+    for (int64_t rz = r0; rz < r1; rz += 64 * KMW_ZB) {
+        int zc[KMW_ZB];
+#pragma unroll
+        for (int u = 0; u < KMW_ZB; ++u) {
+            const int64_t r = rz + 64 * u + lane;
+            zc[u] = (r < r1 ? z[r] : -1) - c0;
+        }
+#pragma unroll
+        for (int u = 0; u < KMW_ZB; ++u) {
+            const int64_t rb = rz + 64 * u;
+            uint64_t mask = __builtin_amdgcn_ballot_w64((unsigned)zc[u] < 16u);
+            while (mask) {
+                int cb[KMW_BATCH];
+                float xa[KMW_BATCH], xb[KMW_BATCH];
+                int nb = 0;
+#pragma unroll
+                for (int i = 0; i < KMW_BATCH; ++i) {
+                    const bool v = mask != 0;  // uniform
+                    const int b = v ? __builtin_ctzll(mask) : 0;
+                    mask = v ? mask & (mask - 1) : mask;
+                    nb += v ? 1 : 0;
+                    cb[i] = __builtin_amdgcn_readlane(zc[u], b);
+                    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                        (void*)(x + (rb + b) * ldx + d0), (short)0, sbytes, BUF_RSRC_WORD3);
+                    xa[i] = buf_load_x<XT>(xr, oA);
+                    xb[i] = buf_load_x<XT>(xr, oB);
+                }
+#pragma unroll
+                for (int i = 0; i < KMW_BATCH; ++i) {
+                    if (i < nb) {
+                        double* ar = my + cb[i] * KS;
+                        ar[dA] += (double)xa[i] - sA;
+                        ar[dB] += (double)xb[i] - sB;
+                        if (w == 0 && lane == 0) kcnt[cb[i]] += 1;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = lane; i < 16 * DPW; i += 64) {
+        const int cc = i / DPW, j = i - cc * DPW;
+        if (d0 + j < d) {
+            double* p = part + ((int64_t)g * kp + c0 + cc) * 2 * DP + d0 + j;
+            *p = (accumulate ? *p : 0.0) + my[cc * KS + j];
+        }
+    }
+    if (tid < 16) {
+        double* np = npart + (int64_t)g * kp + c0 + tid;
+        *np = (accumulate ? *np : 0.0) + (double)kcnt[tid];
     }
 }
 
@@ -570,11 +666,11 @@ static hipError_t launch_wlse_t(const Plan& pl, const void* x, int64_t n, int64_
 
 template <int TM>
 static hipError_t launch_wmerge_t(const Plan& pl, int64_t n, double* lse_out, int ll_acc, int m,
-                                  int32_t* idx, float* resp, hipStream_t st) {
+                                  int32_t* idx, float* resp, int km, hipStream_t st) {
     const int64_t blocks = (n + LL_ROWS - 1) / LL_ROWS;
     hipLaunchKernelGGL((k_wmerge<TM>), dim3((unsigned)blocks), dim3(256), 0, st, pl.wlpart,
                        pl.wtval, pl.wtidx, pl.ntiles, n, pl.k, lse_out, pl.llpart, ll_acc, m, idx,
-                       resp);
+                       resp, km);
     return hipGetLastError();
 }
 
@@ -593,7 +689,7 @@ static hipError_t launch_wstats_t(const Plan& pl, const void* x, int64_t n, int6
 
 hipError_t launch_wide_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                            double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                           hipStream_t st) {
+                           hipStream_t st, int km) {
     if (n <= 0) return hipSuccess;
     hipError_t e = hipErrorInvalidValue;
     const int tm = m <= 0 ? 0 : (m <= 2 ? 2 : 4);
@@ -614,9 +710,33 @@ hipError_t launch_wide_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx
 #undef CASE
     }
     if (e != hipSuccess) return e;
-    if (tm == 0) return launch_wmerge_t<0>(pl, n, lse_out, ll_acc, 0, nullptr, nullptr, st);
-    if (tm == 2) return launch_wmerge_t<2>(pl, n, lse_out, ll_acc, m, idx, resp, st);
-    return launch_wmerge_t<4>(pl, n, lse_out, ll_acc, m, idx, resp, st);
+    if (tm == 0) return launch_wmerge_t<0>(pl, n, lse_out, ll_acc, 0, nullptr, nullptr, 0, st);
+    if (tm == 2) return launch_wmerge_t<2>(pl, n, lse_out, ll_acc, m, idx, resp, km, st);
+    return launch_wmerge_t<4>(pl, n, lse_out, ll_acc, m, idx, resp, km, st);
+}
+
+template <int DP, typename XT>
+static hipError_t launch_km_wstats_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
+                                     const int32_t* z, int acc, hipStream_t st) {
+    int64_t rpg = (n + pl.ngroups - 1) / pl.ngroups;
+    if (rpg < 1) rpg = 1;
+    hipLaunchKernelGGL((k_km_wstats<DP, XT>), dim3(pl.ngroups * pl.ntiles), dim3(512), 0, st,
+                       (const XT*)x, n, pl.d, ldx, pl.shift, z, pl.ntiles, rpg, pl.part, pl.npart,
+                       acc);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide_km_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                                const int32_t* z, int acc, hipStream_t st) {
+    switch (pl.dp) {
+#define CASE(DPV)                                                                          \
+    case DPV:                                                                              \
+        return dtype == 0 ? launch_km_wstats_t<DPV, float>(pl, x, n, ldx, z, acc, st)    \
+                          : launch_km_wstats_t<DPV, uint16_t>(pl, x, n, ldx, z, acc, st);
+        GMM_WIDE_CASES(CASE)
+#undef CASE
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_wide_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,

@@ -132,7 +132,7 @@ int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
  * centroids. The distances use the expanded form 2 a.b - a.a - b.b about a
  * per-dimension shift (exact up to fp64 rounding), so rows whose two nearest
  * centroids are within rounding of each other may be assigned either one.
- * The workspace is the one for (d, k). n >= 1; d <= 128 (GMM_E_UNSUPPORTED
+ * The workspace is the one for (d, k). n >= 1; d <= 768 (GMM_E_UNSUPPORTED
  * otherwise). A non-finite centroid is reported by gmm_device_status and
  * turns the outputs into NaN. */
 int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,

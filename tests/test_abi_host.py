@@ -97,8 +97,7 @@ def test_kmeans_argument_checks(ops):
     assert km(1, 10, 4, 3, 0, 1, 2, None, None, 256, need, None) == ops.GMM_E_INVALID  # ldx < d
     assert km(1, 10, 4, 4, 7, 1, 2, None, None, 256, need, None) == ops.GMM_E_DTYPE
     assert km(1, 10, 4, 4, 0, 1, 2, None, None, 256, need - 1, None) == ops.GMM_E_WORKSPACE
-    wide = ops.workspace_bytes(300, 2)
-    assert km(1, 10, 300, 300, 0, 1, 2, None, None, 256, wide, None) == ops.GMM_E_UNSUPPORTED
+    assert km(1, 10, 800, 800, 0, 1, 2, None, None, 256, need, None) == ops.GMM_E_UNSUPPORTED
 
 
 def test_ivf_workspace_and_argument_checks(ops):

@@ -201,3 +201,33 @@ def test_kmeans_descriptor_full_size(ops):
     print(f"kmeans descriptor full: centroid err {worst:.2e}, inertia {I:.9e} vs {total:.9e}")
     assert worst <= 1e-4
     assert rel(I, total) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# Wide rows (padded dimension 256..768): the wide distance pass and the
+# per-slice k-means statistics.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,d,k,seed", [(3000, 300, 40, 21),    # padded 384
+                                         (5000, 768, 24, 22),    # padded 768, two row chunks
+                                         (2500, 513, 70, 23)])   # padded 640, ragged dims
+def test_kmeans_wide_per_step(ops, n, d, k, seed):
+    x, _, _ = dg.custom(n, d, k, seed=seed)
+    rng = np.random.default_rng(seed)
+    c0 = x[rng.choice(n, k, replace=False)].astype(np.float32)
+    _run(ops, x, c0, 3, f"kmeans wide n={n} d={d} k={k}")
+
+
+def test_kmeans_wide_bf16(ops):
+    x, _, _ = dg.custom(2000, 256, 30, seed=24, dtype="bf16")
+    xf = dg.as_f32(x)
+    c0 = xf[np.random.default_rng(24).choice(2000, 30, replace=False)]
+    _run(ops, x, c0, 2, "kmeans wide bf16")
+
+
+def test_kmeans_wide_workload_prefix(ops):
+    # the wide many-component workload (D = 768, K = 16384) on a 20,000-row
+    # prefix, from its seeded initial means
+    W = dg.WORKLOADS["wide"]
+    x = dg.rows(W, 20_000)
+    _, m0, _ = dg.init_params(W, x)
+    _run(ops, x, m0, 1, "kmeans wide workload prefix")
