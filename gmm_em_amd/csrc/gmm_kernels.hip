@@ -44,6 +44,12 @@
 //                     log-densities.
 // Partials are summed in a fixed order in fp64 by k_finalize: no atomics on
 // floating-point data, bitwise reproducible results.
+//
+// k-means (Lloyd) step, the quantizer the pages' GMM replaces (same source,
+// section 3): k_params without weights or variances gives coefficients with
+// l = -|x - c|^2; k_lse with a top-1 list yields the assignment and sums the
+// best l (minus the inertia); k_km_stats adds each row, one-hot, into its
+// centroid's sums (no MFMA needed); k_kmfinal divides.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -161,7 +167,8 @@ __global__ void k_params(const float* __restrict__ w, const float* __restrict__ 
 // Block: 8 waves x 16 rows. Each lane holds the fp64 features of its row in
 // E-operand order (feature (dim 2t + (h>>1), power 1 + (h&1)) for t = 0..
 // DP/2-1), computed once; the K-tiles' coefficient rows and constants stream
-// through double-buffered LDS shared by the 8 waves.
+// through three LDS buffers shared by the 8 waves. In k-means mode (km, with
+// the k-means coefficients) the row's value is its best log-density.
 // ---------------------------------------------------------------------------
 constexpr int LSE_WAVES = 8;
 constexpr int LSE_ROWS = LSE_WAVES * 16;
