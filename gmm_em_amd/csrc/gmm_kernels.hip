@@ -452,8 +452,15 @@ constexpr int STATS_ROWS = 32;  // two 16-row MFMA blocks per staged tile
 template <int DP>
 struct StatsGeom {
     static constexpr int DPH = DP / 2;
-    static constexpr int HS = DPH;           // stride of one (parity, power) section
-    static constexpr int S = 4 * DPH + 10;   // row stride (doubles); see bank analysis
+    // LDS strides (doubles) chosen so that neither pass's reads conflict on
+    // the 32 four-byte banks:
+    // * HS, one (parity, power) section, is 4 mod 8: an M-step read (16
+    //   lanes: dims 16J + ci of one row, even ci in section 0 and odd ci in
+    //   section 2, 8 doubles each) covers banks 2k and 2k + 4*HS = 2k + 16;
+    // * S, one row, is 2 mod 4: an E-step 16-byte read (8 lanes: rows ci of
+    //   one section) starts at bank 2*S*ci = 4*ci mod 32.
+    static constexpr int HS = DPH + 4;
+    static constexpr int S = 4 * HS + 2;
     static constexpr int WV = DP <= 64 ? 8 : 4;  // 8 waves fit 256 registers each only up to 64
     static constexpr int NT = WV * 64;
     static constexpr int PER = (STATS_ROWS * DP + NT - 1) / NT;  // x values per thread
