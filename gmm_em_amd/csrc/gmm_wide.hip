@@ -89,6 +89,28 @@ struct WideStage {
             xv[u] = u < nvalid ? v : 0.0f;
         }
     }
+    // load() without the padding select, for d == DP (every dim is data)
+    __device__ __forceinline__ void load_full(int64_t it) {
+        const int64_t rbase = gr0 + it * WROWS;
+        int64_t nv = gr1 - rbase;
+        nv = nv < 0 ? 0 : (nv > WROWS ? WROWS : nv);
+        const int xbytes = nv > 0 ? (int)(((nv - 1) * ldx + d) * (int64_t)sizeof(XT)) : 0;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(x + rbase * ldx), (short)0, xbytes, BUF_RSRC_WORD3);
+#pragma unroll
+        for (int u = 0; u < PR; ++u)
+            xv[u] = buf_load_x<XT>(xr, xoff + (uint32_t)(TPR * u * (int)sizeof(XT)));
+    }
+    // store() with this thread's shifts in registers (shr[u]: dim sl + TPR*u)
+    template <int RS>
+    __device__ __forceinline__ void store_r(double* fa, const double (&shr)[PR], int tid) const {
+        double* dst = fa + (tid / TPR) * RS + sl;
+#pragma unroll
+        for (int u = 0; u < PR; ++u) {
+            dst[TPR * u] = (double)xv[u] - shr[u];
+            if (u % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
     // fa: the tile in LDS (row stride RS, natural dim order); shl: shifts
     template <int RS>
     __device__ __forceinline__ void store(double* fa, const double* shl, int tid) const {
@@ -177,7 +199,6 @@ void k_wlse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     constexpr int NW = 8, NT = 512, DS = DP / NW, RS = DP + 1;
     constexpr int TMA = TM > 0 ? TM : 1;
     __shared__ __attribute__((aligned(16))) double fa[WROWS * RS];
-    __shared__ double shl[DP];
     __shared__ __attribute__((aligned(16))) f64x4 xb[2][NW][64];
 
     const int tid = threadIdx.x;
@@ -191,7 +212,6 @@ void k_wlse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     double pr[DS / 2];
     wide_coefs<DP, DS>(pr, Pg, slot, w, h);
     const double cc = cvec[slot];
-    for (int i = tid; i < DP; i += NT) shl[i] = shift[(i & 1) * (DP / 2) + (i >> 1)];
 
     const int64_t gr0 = (int64_t)g * rows_per_group;
     int64_t gr1 = gr0 + rows_per_group;
@@ -253,12 +273,26 @@ void k_wlse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         else red_store(rt);
     };
 
-    if (ntr > 0) stg.load(0);
+    // the shifts of the dims this thread stages, in registers; rows without
+    // padding dims skip the padding select
+    using Stage = WideStage<DP, NT, XT>;
+    double shr[Stage::PR];
+#pragma unroll
+    for (int u = 0; u < Stage::PR; ++u) {
+        const int dim = stg.sl + Stage::TPR * u;
+        shr[u] = shift[(dim & 1) * (DP / 2) + (dim >> 1)];
+    }
+    const bool full = d == DP;
+    auto load = [&](int64_t it) {
+        if (full) stg.load_full(it);
+        else stg.load(it);
+    };
+    if (ntr > 0) load(0);
     for (int64_t it = 0; it < ntr; ++it) {
         __syncthreads();  // every wave is done with the previous tile's LDS
-        stg.template store<RS>(fa, shl, tid);
+        stg.template store_r<RS>(fa, shr, tid);
         __syncthreads();
-        if (it + 1 < ntr) stg.load(it + 1);
+        if (it + 1 < ntr) load(it + 1);
         const int cur = (int)(it & 1);
         const bool red = wq < 4 && it > 0;  // wave-uniform
         auto hook = [&](int bt) {
