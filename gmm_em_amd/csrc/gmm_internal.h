@@ -23,7 +23,7 @@ constexpr int64_t CHUNK_ROWS = (int64_t)1 << 22;
 // fewer than 2^31 bytes (the statistics pass's per-tile buffer offsets).
 constexpr int64_t MAX_LDX = ((int64_t)1 << 24) - 1;
 // Rows per normaliser-pass block (one log-likelihood partial each).
-constexpr int LL_ROWS = 128;
+constexpr int LL_ROWS = 64;
 
 // Workspace layout and launch geometry for one (d, k).
 struct Plan {

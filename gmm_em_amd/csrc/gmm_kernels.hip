@@ -167,16 +167,22 @@ __global__ void k_params(const float* __restrict__ w, const float* __restrict__ 
 // Block: 8 waves x 16 rows. Each lane holds the fp64 features of its row in
 // E-operand order (feature (dim 2t + (h>>1), power 1 + (h&1)) for t = 0..
 // DP/2-1), computed once; the K-tiles' coefficient rows and constants stream
-// through three LDS buffers shared by the 8 waves. In k-means mode (km, with
-// the k-means coefficients) the row's value is its best log-density.
+// through three LDS buffers shared by the block's waves. Up to D = 96 a block
+// has 4 waves (64 rows) and two blocks share a CU, so one block's prologue
+// and epilogue overlap the other's MFMAs; above, 8 waves (128 rows; three
+// buffers of 128-dim tiles leave LDS for one block). In k-means mode (km,
+// with the k-means coefficients) the row's value is its best log-density.
 // ---------------------------------------------------------------------------
-constexpr int LSE_WAVES = 8;
-constexpr int LSE_ROWS = LSE_WAVES * 16;
-static_assert(LSE_ROWS == 128, "the block's log-likelihood sum reads two rows per lane");
-static_assert(LSE_ROWS == LL_ROWS, "one log-likelihood partial per normaliser block");
+template <int DP>
+struct LseGeom {
+    static constexpr int WAVES = DP <= 96 ? 4 : 8;
+    static constexpr int ROWS = WAVES * 16;
+    static constexpr int NT = WAVES * 64;
+    static_assert(ROWS % LL_ROWS == 0 && LL_ROWS == 64, "one partial per 64 rows");
+};
 
 template <int DP, typename XT, int TM>
-__global__ __launch_bounds__(LSE_WAVES * 64, 1)
+__global__ __launch_bounds__(LseGeom<DP>::NT, 8 / LseGeom<DP>::WAVES)
 void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
            const double* __restrict__ Pg, const double* __restrict__ cvec,
            const double* __restrict__ shift, int ntiles, double* __restrict__ lse_out,
@@ -185,7 +191,8 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     constexpr int DPH = DP / 2;
     constexpr int PSTR = 2 * DP + 2;  // LDS stride of one component (doubles)
     constexpr int TMA = TM > 0 ? TM : 1;
-    constexpr int NT = LSE_WAVES * 64;
+    constexpr int NT = LseGeom<DP>::NT;
+    constexpr int LSE_ROWS = LseGeom<DP>::ROWS;
     __shared__ __attribute__((aligned(16))) double Pt[3][16 * PSTR];
     __shared__ double Ct[3][16];
     __shared__ double rowll[LSE_ROWS];
@@ -420,13 +427,14 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
         }
     }
     __syncthreads();
-    // Fixed-order sum of the block's rows: lane l of wave 0 adds rows l and
-    // l + 64, then a butterfly over the 64 lanes.
-    if (wave == 0) {
-        double tot = rowll[lane] + rowll[lane + 64];
+    // Fixed-order sums of the block's rows, one partial per 64 rows: wave w
+    // (w < rows / 64) takes rows 64w + lane, then a butterfly over the lanes.
+    if (wave < LSE_ROWS / LL_ROWS) {
+        double tot = rowll[wave * 64 + lane];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) tot += shfl_xor_d(tot, off);
-        if (lane == 0) llpart[blockIdx.x] = (ll_accumulate ? llpart[blockIdx.x] : 0.0) + tot;
+        const int64_t pi = (int64_t)blockIdx.x * (LSE_ROWS / LL_ROWS) + wave;
+        if (lane == 0) llpart[pi] = (ll_accumulate ? llpart[pi] : 0.0) + tot;
     }
 }
 
@@ -1173,9 +1181,10 @@ template <int DP, typename XT, int TM>
 static hipError_t launch_lse_tm(const Plan& pl, const void* x, int64_t n, int64_t ldx,
                                 double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
                                 int km, hipStream_t st) {
-    const int64_t blocks = (n + LSE_ROWS - 1) / LSE_ROWS;
+    using G = LseGeom<DP>;
+    const int64_t blocks = (n + G::ROWS - 1) / G::ROWS;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_lse<DP, XT, TM>), dim3((unsigned)blocks), dim3(LSE_WAVES * 64), 0, st,
+    hipLaunchKernelGGL((k_lse<DP, XT, TM>), dim3((unsigned)blocks), dim3(G::NT), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse_out,
                        pl.llpart, ll_acc, pl.k, m, idx, resp, km);
     return hipGetLastError();

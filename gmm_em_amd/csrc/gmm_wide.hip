@@ -579,7 +579,9 @@ void k_wmerge(const double2* __restrict__ lpart, const double* __restrict__ tval
     }
     __syncthreads();
     if (w == 0) {
-        double tot = rowll[lane] + rowll[lane + 64];
+        double tot = 0.0;
+#pragma unroll
+        for (int r = 0; r < LL_ROWS; r += 64) tot += rowll[r + lane];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) tot += shfl_xor_d(tot, off);
         if (lane == 0) llpart[blockIdx.x] = (ll_accumulate ? llpart[blockIdx.x] : 0.0) + tot;
