@@ -333,6 +333,42 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
     return hip_status(e);
 }
 
+int gmm_kmeans_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                   float* centroids, int32_t k, int32_t max_iter, double tol,
+                   double* inertia_hist_dev, int32_t* iters_done, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    if (max_iter < 0 || !(tol >= 0.0) || !isfinite(tol)) return GMM_E_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    double prev = 0.0;
+    int done = 0, rc = GMM_OK;
+    for (int it = 0; it < max_iter; ++it) {
+        double* in = inertia_hist_dev ? inertia_hist_dev + it : nullptr;
+        double* tmp = nullptr;
+        if (!in && tol > 0.0) {
+            Plan pl;
+            if (!make_plan(d, k, workspace, &pl)) return GMM_E_UNSUPPORTED;
+            tmp = pl.ll_tmp;  // (checked by gmm_kmeans_step below)
+        }
+        rc = gmm_kmeans_step(x, n, d, ldx, x_dtype, centroids, k, nullptr, in ? in : tmp,
+                             workspace, workspace_bytes, stream);
+        if (rc) break;
+        ++done;
+        if (tol > 0.0) {
+            double cur = 0.0;
+            if (hipMemcpyAsync(&cur, in ? in : tmp, sizeof(double), hipMemcpyDeviceToHost, st) !=
+                    hipSuccess ||
+                hipStreamSynchronize(st) != hipSuccess) {
+                rc = GMM_E_HIP;
+                break;
+            }
+            if (it > 0 && prev - cur < tol * cur) break;
+            prev = cur;
+        }
+    }
+    if (iters_done) *iters_done = done;
+    return rc;
+}
+
 int gmm_device_status(const void* workspace, void* stream) {
     if (!workspace) return GMM_E_INVALID;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GMM_E_HIP;

@@ -29,6 +29,8 @@ lib.gmm_loglik.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _i32, _vp
 lib.gmm_assign_topm.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp,
                                 _vp, _sz, _vp]
 lib.gmm_kmeans_step.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+lib.gmm_kmeans_fit.argtypes = [_vp, _i64, _i32, _i64, _i32, _vp, _i32, _i32, _f64, _vp,
+                               ctypes.POINTER(_i32), _vp, _sz, _vp]
 lib.gmm_ivf_workspace_bytes.argtypes = [_i64, _i32, _i32]
 lib.gmm_ivf_workspace_bytes.restype = _sz
 lib.gmm_ivf_build.argtypes = [_vp, _vp, _i64, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -40,7 +42,8 @@ lib.gmm_profile_begin.argtypes = [_i32]
 lib.gmm_profile_end.argtypes = [ctypes.POINTER(_f64), ctypes.POINTER(_i32), ctypes.POINTER(_f64),
                                 ctypes.POINTER(_i32)]
 for _f in (lib.gmm_em_step, lib.gmm_fit, lib.gmm_loglik, lib.gmm_assign_topm, lib.gmm_kmeans_step,
-           lib.gmm_ivf_build, lib.gmm_device_status, lib.gmm_profile_begin, lib.gmm_profile_end):
+           lib.gmm_kmeans_fit, lib.gmm_ivf_build, lib.gmm_device_status, lib.gmm_profile_begin,
+           lib.gmm_profile_end):
     _f.restype = ctypes.c_int
 
 (GMM_OK, GMM_E_INVALID, GMM_E_DTYPE, GMM_E_WORKSPACE, GMM_E_PARAMS, GMM_E_HIP, GMM_E_UNSUPPORTED,
@@ -178,6 +181,23 @@ def kmeans_step(x, centroids, ws=None, assign: bool = True):
     _check(lib.gmm_kmeans_step(_ptr(x), x.shape[0], d, ldx, dt, _ptr(centroids), k, _ptr(z),
                                _ptr(inertia), _ptr(ws), ws.numel(), _stream(x.device)))
     return inertia, z
+
+
+def kmeans_fit(x, centroids, max_iter: int = 10, tol: float = 0.0, ws=None):
+    """Lloyd steps in place; returns (inertia history float64 tensor, steps taken)."""
+    dt, ldx = _data(x)
+    if centroids.dtype != torch.float32 or not centroids.is_contiguous() or centroids.dim() != 2:
+        raise ValueError("centroids must be a contiguous float32 (K, D) tensor")
+    if centroids.device != x.device or centroids.shape[1] != x.shape[1]:
+        raise ValueError("centroids must be on the device of x and match its D")
+    k, d = centroids.shape
+    ws = _ws(ws, d, k, x.device)
+    hist = torch.full((max(max_iter, 1),), float("nan"), dtype=torch.float64, device=x.device)
+    done = _i32(0)
+    _check(lib.gmm_kmeans_fit(_ptr(x), x.shape[0], d, ldx, dt, _ptr(centroids), k, max_iter, tol,
+                              _ptr(hist), ctypes.byref(done), _ptr(ws), ws.numel(),
+                              _stream(x.device)))
+    return hist[: done.value], done.value
 
 
 def ivf_build(idx, resp, k: int, min_resp: float = 0.0, values: bool = True):

@@ -160,6 +160,17 @@ int gmm_ivf_build(const int32_t* idx_dev, const float* resp_dev, int64_t n, int3
                   float min_resp, int64_t* offsets_dev, int32_t* rows_dev, float* values_dev,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* max_iter Lloyd steps (gmm_kmeans_step repeated) on the centroids in place.
+ * inertia_hist_dev (device, max_iter doubles, may be NULL) receives the
+ * inertia of the centroids entering step t, t = 0, 1, ... When tol > 0 the
+ * host reads each inertia after its step (one synchronisation per step) and
+ * stops once I_{t-1} - I_t < tol * I_t. iters_done (host pointer, may be
+ * NULL) receives the number of steps taken. */
+int gmm_kmeans_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                   float* centroids, int32_t k, int32_t max_iter, double tol,
+                   double* inertia_hist_dev, int32_t* iters_done, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Synchronises the stream and returns GMM_E_PARAMS if the last call that used
  * this workspace found invalid parameter values, GMM_E_SYNC if its
  * cooperative exchange timed out, GMM_OK otherwise, or GMM_E_HIP if the

@@ -118,3 +118,15 @@ def test_ivf_workspace_and_argument_checks(ops):
     assert b(1, 1, 100, 2, 8, 0.0, 1, 1, None, 257, need, None) == ops.GMM_E_WORKSPACE
     assert b(1, 1, 100, 2, 20000, 0.0, 1, 1, None, 256, need, None) == ops.GMM_E_UNSUPPORTED
     assert b(1, 1, -5, 2, 8, 0.0, 1, 1, None, 256, need, None) == ops.GMM_E_INVALID
+
+
+def test_kmeans_fit_argument_checks(ops):
+    f = ops.lib.gmm_kmeans_fit
+    need = ops.workspace_bytes(4, 2)
+    assert f(1, 10, 4, 4, 0, 1, 2, -1, 0.0, None, None, 256, need, None) == ops.GMM_E_INVALID
+    assert f(1, 10, 4, 4, 0, 1, 2, 3, -1.0, None, None, 256, need, None) == ops.GMM_E_INVALID
+    assert f(1, 10, 4, 4, 0, 1, 2, 3, float("inf"), None, None, 256, need, None) == ops.GMM_E_INVALID
+    # zero steps: nothing runs, nothing is touched
+    done = ops._i32(7)
+    assert f(1, 10, 4, 4, 0, 1, 2, 0, 0.0, None, ops.ctypes.byref(done), 256, need, None) == ops.GMM_OK
+    assert done.value == 0

@@ -231,3 +231,27 @@ def test_kmeans_wide_workload_prefix(ops):
     x = dg.rows(W, 20_000)
     _, m0, _ = dg.init_params(W, x)
     _run(ops, x, m0, 1, "kmeans wide workload prefix")
+
+
+def test_kmeans_fit_matches_chained_oracle_steps(ops):
+    # five Lloyd steps end to end from the same centroids on both sides, and
+    # the early stop on the relative inertia decrease
+    x, _, _ = dg.custom(4000, 12, 10, seed=31)
+    c0 = x[np.random.default_rng(31).choice(4000, 10, replace=False)].astype(np.float32)
+    c = torch.from_numpy(c0.copy()).to(DEV)
+    hist, done = ops.kmeans_fit(_xt(x), c, max_iter=5)
+    torch.cuda.synchronize()
+    assert done == 5
+    ref = c0.astype(np.float64)
+    rhist = []
+    for _ in range(5):
+        ref, _, inertia, _ = oracle.kmeans_step(x, ref.astype(np.float32).astype(np.float64))
+        rhist.append(inertia)
+    h = hist.cpu().numpy()
+    assert np.all(np.abs(h - rhist) / np.array(rhist) <= 1e-5), (h, rhist)
+    g = c.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(g - ref) / np.maximum(np.abs(ref).max(axis=1, keepdims=True), 1.0)) <= 1e-4
+    # with a tolerance the loop stops once the inertia stops improving
+    c2 = torch.from_numpy(c0.copy()).to(DEV)
+    _, done2 = ops.kmeans_fit(_xt(x), c2, max_iter=200, tol=1e-9)
+    assert 1 <= done2 < 200
