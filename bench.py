@@ -39,8 +39,8 @@ PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (the contractions
 # Keyed by a hash of the kernel sources: a changed kernel reports null until
 # it is profiled again.
 MEASURED_TRAFFIC = {
-    "454f6430b8493d20": {"workload": "descriptor", "kernel": "k_stats (pass 2)",
-                         "bytes_per_launch": 1.6790e9},
+    "45f21e27e4ec1449": {"workload": "descriptor", "kernel": "k_stats (pass 2)",
+                         "bytes_per_launch": 1.6817e9},
 }
 
 
