@@ -130,3 +130,15 @@ def test_kmeans_fit_argument_checks(ops):
     done = ops._i32(7)
     assert f(1, 10, 4, 4, 0, 1, 2, 0, 0.0, None, ops.ctypes.byref(done), 256, need, None) == ops.GMM_OK
     assert done.value == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the bench measures one GPU; asking for more exits with a message
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
