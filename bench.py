@@ -6,7 +6,13 @@ synthetic data matrix, which is resident in HBM before timing starts. The
 default workload is the headline one: N = 10,000,000 rows, D = 96, K = 1024,
 fp32, non-negative integer descriptor-like data (planted means U[0,100]^D,
 sd U[2,10], Zipf(1.1) weights), EM started from K seeded rows with unit
-variances. Prints one JSON line.
+variances. The W warm-up steps are the first EM iterations (the first one is
+sparse: each row has about one nonzero responsibility); the K timed steps
+continue from there, so every timed step is a dense iteration. Prints one
+JSON line, with the dominant kernel's roofline (HIP events around its
+launches, on the stream they run on) and the fp64 oracle timed on the host
+on a bounded row prefix from the same parameters, next to the GPU's step on
+that prefix (the "parity_sample" errors).
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--cpu-rows R] [--rows R]
@@ -65,7 +71,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="descriptor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3_000_000)
@@ -113,16 +119,19 @@ def main() -> int:
     ws = ops.workspace(W.d, W.k, dev)
     if args.mode != "em":
         return _other_mode(args, W, x, xt, w0, m0, v0, ws, n_rows)
-    th0 = [torch.from_numpy(a).to(dev) for a in (w0, m0, v0)]
-    w, mu, var = (t.clone() for t in th0)
-    ll = torch.empty(max(args.steps, 1), dtype=torch.float64, device=dev)
+    w, mu, var = (torch.from_numpy(a).to(dev) for a in (w0, m0, v0))
+    ll = torch.empty(max(args.steps + args.warmup, 1), dtype=torch.float64, device=dev)
 
-    for _ in range(args.warmup):
-        ops.em_step(xt, w, mu, var, W.var_floor, ws=ws, loglik=ll[0])
+    # Warm-up steps are the first EM iterations from the seeded initial
+    # parameters (the first one is the sparse iteration: a row has about one
+    # nonzero responsibility); the timed steps continue from there, so every
+    # timed step is a dense iteration.
+    for i in range(args.warmup):
+        ops.em_step(xt, w, mu, var, W.var_floor, ws=ws, loglik=ll[i])
     torch.cuda.synchronize()
-    for t, s in zip((w, mu, var), th0):
-        t.copy_(s)
-    torch.cuda.synchronize()
+    theta_w = [t.cpu().numpy() for t in (w, mu, var)]  # parameters entering the timed steps
+    torch.cuda.reset_peak_memory_stats(dev)
+    free_before, total_mem = torch.cuda.mem_get_info(dev)
 
     chunk = 4096 if W.d > 128 else (1 << 22)  # rows per launch of each pass
     ops.profile_begin(args.steps * (-(-n_rows // chunk)) + 8)
@@ -132,11 +141,12 @@ def main() -> int:
     wall0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        ops.em_step(xt, w, mu, var, W.var_floor, ws=ws, loglik=ll[i])
+        ops.em_step(xt, w, mu, var, W.var_floor, ws=ws, loglik=ll[args.warmup + i])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     prof = ops.profile_end()
+    free_after, _ = torch.cuda.mem_get_info(dev)
     status = ops.device_status(ws, dev)
     if status != ops.GMM_OK:
         print(f"device status {status}", file=sys.stderr)
@@ -146,23 +156,27 @@ def main() -> int:
     its = 1000.0 / ms_step
     flops_step = 8.0 * n_rows * W.d * W.k
     tflops = flops_step * its / 1e12
-    hist = ll[: args.steps].cpu().numpy()
+    hist = ll[: args.warmup + args.steps].cpu().numpy()
+    x_bytes = xt.numel() * xt.element_size()
 
-    # dominant kernel: the pass with the larger summed time (in the
-    # cooperative single-pass schedule there is no pass 1 and the one kernel
-    # does both contractions)
+    # Dominant kernel, credited with the method's own work only: the
+    # normaliser pass does the E-step contraction (4 D K flop per row); the
+    # statistics pass is credited with the M-step contraction alone (4 D K
+    # flop per row: [r, r a, r a^2] against the row), not with the E-step it
+    # recomputes to form responsibilities, and its skipped all-zero groups
+    # count as work. One launch processes one row chunk.
     (ms1, n1), (ms2, n2) = prof["pass1"], prof["pass2"]
     wide = W.d > 128  # rows past 128 dims run the D-sliced wide kernels
     if ms2 >= ms1:
-        kname = ("k_wide statistics (pass 2)" if wide else "k_stats (pass 2)") if n1 > 0 \
-            else "k_coop (single pass)"
-        kms, kn, kflops = ms2, n2, 8.0 * W.d * W.k
+        kname = "k_wide statistics (pass 2)" if wide else "k_stats (pass 2)"
+        kms, kn, alg_row, exec_row = ms2, n2, 4.0 * W.d * W.k, 8.0 * W.d * W.k
     else:
         kname = "k_wide normaliser + k_wmerge (pass 1)" if wide else "k_lse (pass 1)"
-        kms, kn, kflops = ms1, n1, 4.0 * W.d * W.k
+        kms, kn, alg_row, exec_row = ms1, n1, 4.0 * W.d * W.k, 4.0 * W.d * W.k
     launches_per_step = kn / args.steps
     avg_ms = kms / kn
-    alg_flops_launch = kflops * n_rows / launches_per_step
+    rows_per_launch = n_rows / launches_per_step
+    alg_flops_launch = alg_row * rows_per_launch
     achieved = alg_flops_launch / (avg_ms * 1e-3) / 1e12
     roofline = {
         "kernel": kname,
@@ -171,32 +185,53 @@ def main() -> int:
         "peak": PEAK_FP64_MFMA_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP64_MFMA_TFLOPS, 4),
+        "frac_of_fp32_mfma_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
         "traffic": _traffic(W.key, kname),
-        "schedule": "two-pass" if n1 > 0 else "cooperative single pass",
         "avg_launch_ms": round(avg_ms, 4),
         "launches_per_step": launches_per_step,
+        "rows_per_launch": rows_per_launch,
+        "alg_flops_per_row": alg_row,
         "alg_flops_per_launch": alg_flops_launch,
+        # what the kernel issues (the recomputed E-step included), as a
+        # utilisation figure beside the algorithmic one
+        "executed_flops_per_row": exec_row,
+        "executed_frac": round(exec_row * rows_per_launch / (avg_ms * 1e-3) / 1e12
+                               / PEAK_FP64_MFMA_TFLOPS, 4),
         "pass1_ms_per_step": round(ms1 / args.steps, 3),
         "pass2_ms_per_step": round(ms2 / args.steps, 3),
     }
 
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         from oracle import oracle
+        from tests.parity import param_errors
 
+        # The oracle's step from the parameters that entered the timed steps
+        # (a dense iteration), on a bounded row prefix, scaled to all rows.
         nr = min(args.cpu_rows, n_rows)
         xs = x[:nr]
         t1 = time.perf_counter()
-        oracle.em_step(xs, w0, m0, v0, W.var_floor)
+        rw, rmu, rv, rL, rnk = oracle.em_step(xs, *theta_w, W.var_floor)
         dt = time.perf_counter() - t1
         cpu = {
             "value": round(1.0 / (dt * n_rows / nr), 6),
             "unit": "EM it/s",
             "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"one EM step from the initial parameters on the first {nr} of {n_rows} rows "
-                      f"({dt:.2f} s), scaled linearly to all rows",
+            "sample": f"one dense EM step (from the parameters after {args.warmup} warm-up "
+                      f"iterations) on the first {nr} of {n_rows} rows ({dt:.2f} s), scaled "
+                      f"linearly to all rows",
+            "cpu_model": _cpu_model(),
         }
+        # the GPU's step on the same prefix from the same parameters
+        gw, gmu, gv = (torch.from_numpy(a).to(dev) for a in theta_w)
+        gL = ops.em_step(xt[:nr], gw, gmu, gv, W.var_floor, ws=ws)
+        torch.cuda.synchronize()
+        e = param_errors([t.cpu().numpy() for t in (gw, gmu, gv)], (rw, rmu, rv), rnk, nr)
+        parity = {"rows": nr, "mu": e["mu"], "var": e["var"], "w": e["w"],
+                  "loglik": abs(gL.item() - rL) / abs(rL), "tiny_components": e["n_tiny"],
+                  "killed": e["killed"]}
 
     headline = W.key == "descriptor" and n_rows == W.n
     out = {
@@ -213,7 +248,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": f"{W.key}: N={n_rows} D={W.d} K={W.k} {W.dtype}, EM from seeded init"
+        "config": {"workload": f"{W.key}: N={n_rows} D={W.d} K={W.k} {W.dtype}, EM iterations "
+                               f"{args.warmup}..{args.warmup + args.steps - 1} from seeded init"
                                + ("" if n_rows == W.n else f" (row prefix of N={W.n})"),
                    "n": n_rows, "d": W.d, "k": W.k, "x_dtype": W.dtype, "var_floor": W.var_floor},
         "x_dtype": W.dtype,
@@ -223,13 +259,46 @@ def main() -> int:
         "pct_mfma_roofline": round(100.0 * tflops / PEAK_FP32_MFMA_TFLOPS, 2),
         # the same flops against the fp64 MFMA peak the contractions run on
         "pct_fp64_mfma_roofline": round(100.0 * tflops / PEAK_FP64_MFMA_TFLOPS, 2),
+        # the data matrix is read once per pass, two passes per step
+        "hbm_gbs_data_reads": round(2.0 * x_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "device_memory": {
+            "data_bytes": x_bytes,
+            "workspace_bytes": ws.numel(),
+            "torch_peak_bytes": torch.cuda.max_memory_allocated(dev),
+            "free_delta_over_timed_steps": free_before - free_after,
+            "total_bytes": total_mem,
+        },
         "loglik_first_last": [float(hist[0]), float(hist[-1])],
         "wall_s": round(wall, 3),
+        "git_revision": _git_revision(),
         "roofline": roofline,
+        "parity_sample": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _git_revision():
+    import subprocess
+
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"],
+                           capture_output=True, text=True, timeout=10)
+        return r.stdout.strip() or None
+    except Exception:
+        return None
 
 
 def _other_mode(args, W, x, xt, w0, m0, v0, ws, n_rows) -> int:

@@ -4,9 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <new>
-#include <stdlib.h>
-#include <string.h>
 
 #include "gmm_em.h"
 #include "gmm_internal.h"
@@ -50,8 +49,6 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     const size_t o_np = take((size_t)p.ngroups * p.kp * sizeof(double));
     const size_t o_part = take((size_t)p.ngroups * p.kp * 2 * p.dp * sizeof(double));
     const size_t o_lt = take(sizeof(double));
-    const size_t o_xb = take((size_t)p.ngroups * 4 * kgroups * 32 * sizeof(double2));
-    const size_t o_cnt = take((size_t)p.ngroups * kgroups * sizeof(unsigned));
     const size_t wpart = p.wide ? (size_t)WIDE_CHUNK_ROWS * p.ntiles : 0;
     const size_t o_wl = take(wpart * sizeof(double2));
     const size_t o_wv = take(wpart * WIDE_TM * sizeof(double));
@@ -68,8 +65,6 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
         p.npart = (double*)(b + o_np);
         p.part = (double*)(b + o_part);
         p.ll_tmp = (double*)(b + o_lt);
-        p.xbuf = (double2*)(b + o_xb);
-        p.counters = (unsigned*)(b + o_cnt);
         if (p.wide) {
             p.wlpart = (double2*)(b + o_wl);
             p.wtval = (double*)(b + o_wv);
@@ -103,6 +98,9 @@ static int check_common(const void* x, int64_t n, int32_t d, int64_t ldx, int32_
 static int hip_status(hipError_t e) { return e == hipSuccess ? GMM_OK : GMM_E_HIP; }
 
 // Optional event recording around the two passes (gmm_profile_begin/end).
+// This is the library's only process-wide state: a measurement aid outside
+// the compute calls' re-entrancy promise. A mutex keeps concurrent calls from
+// corrupting it; the events exist only between begin and end.
 struct Prof {
     bool on = false;
     int cap = 0;
@@ -111,8 +109,20 @@ struct Prof {
     hipEvent_t* ev2 = nullptr;  // [2*cap] pass 2
 };
 static Prof g_prof;
+static std::mutex g_prof_mu;
+
+static void prof_release() {
+    for (int i = 0; i < 2 * g_prof.cap; ++i) {
+        if (g_prof.ev1 && g_prof.ev1[i]) (void)hipEventDestroy(g_prof.ev1[i]);
+        if (g_prof.ev2 && g_prof.ev2[i]) (void)hipEventDestroy(g_prof.ev2[i]);
+    }
+    delete[] g_prof.ev1;
+    delete[] g_prof.ev2;
+    g_prof = Prof();
+}
 
 static void prof_mark(int pass, bool start, hipStream_t st) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof.on) return;
     int& cnt = pass == 1 ? g_prof.n1 : g_prof.n2;
     hipEvent_t* ev = pass == 1 ? g_prof.ev1 : g_prof.ev2;
@@ -152,42 +162,6 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
     return hipSuccess;
 }
 
-// Schedule of the EM step. The default is the two-pass schedule; the
-// cooperative single pass (GMM_EM_SCHEDULE=coop) removes the normaliser
-// pass but pays a cross-workgroup exchange per 32-row tile, which measured
-// slower on MI355X at the headline shape (321 vs 217 ms per step at N=1e7,
-// D=96, K=1024). coop fails with GMM_E_UNSUPPORTED where the grid cannot be
-// co-resident.
-enum { SCHED_TWO_PASS = 1, SCHED_COOP = 2 };
-
-static int schedule_choice() {
-    const char* v = getenv("GMM_EM_SCHEDULE");
-    if (v && !strcmp(v, "coop")) return SCHED_COOP;
-    return SCHED_TWO_PASS;
-}
-
-// Row groups of the cooperative pass for the current device, or 0 if it
-// cannot run: every block must be co-resident, and each XCD (8 of them,
-// workgroups dispatched round-robin) must hold whole row groups.
-static int coop_groups(const Plan& pl) {
-    static int cached_dev = -1, cached_cus = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev != cached_dev) {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess || !prop.cooperativeLaunch) return 0;
-        cached_cus = prop.multiProcessorCount;
-        cached_dev = dev;
-    }
-    if (pl.wide) return 0;  // the cooperative kernel holds a K-group's rows in registers
-    const int bpc = coop_blocks_per_cu(pl.dp);
-    if (bpc < 1 || pl.kgroups < 1 || pl.kgroups > 64) return 0;  // one wave watches the flags
-    int groups = (cached_cus * bpc) / pl.kgroups;
-    groups = groups / 8 * 8;
-    if (groups > pl.ngroups) groups = pl.ngroups / 8 * 8;
-    return groups >= 8 ? groups : 0;
-}
-
 static int ll_parts(const Plan& pl, int64_t n) {
     const int64_t first = n < pl.chunk ? n : pl.chunk;
     return (int)((first + LL_ROWS - 1) / LL_ROWS);
@@ -209,24 +183,9 @@ int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtyp
     if (rc) return rc;
     if (n < 1 || !(var_floor >= 0.0f) || !isfinite(var_floor)) return GMM_E_INVALID;
     hipStream_t st = (hipStream_t)stream;
-    const int sched = schedule_choice();
-    const int cg = sched == SCHED_TWO_PASS ? 0 : coop_groups(pl);
-    if (sched == SCHED_COOP && cg == 0) return GMM_E_UNSUPPORTED;
     double* ll_out = loglik_dev ? loglik_dev : pl.ll_tmp;
     hipError_t e = launch_prologue(pl, weights, means, variances, st);
     if (e != hipSuccess) return GMM_E_HIP;
-    if (cg > 0) {
-        prof_mark(2, true, st);
-        e = launch_coop(pl, x, n, ldx, x_dtype, cg, st);
-        prof_mark(2, false, st);
-        if (e == hipSuccess) {
-            e = launch_ll_final(pl, cg, ll_out, st);
-            if (e == hipSuccess) e = launch_finalize(pl, cg, n, var_floor, weights, means, variances, st);
-            return hip_status(e);
-        }
-        if (sched == SCHED_COOP) return GMM_E_HIP;
-        (void)hipGetLastError();  // fall back to the two-pass schedule
-    }
     e = run_passes(pl, x, n, ldx, x_dtype, true, st);
     if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), ll_out, st);
     if (e == hipSuccess) e = launch_finalize(pl, pl.ngroups, n, var_floor, weights, means, variances, st);
@@ -374,7 +333,6 @@ int gmm_device_status(const void* workspace, void* stream) {
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GMM_E_HIP;
     int st2[4] = {0, 0, 0, 0};
     if (hipMemcpy(st2, workspace, sizeof(st2), hipMemcpyDeviceToHost) != hipSuccess) return GMM_E_HIP;
-    if (st2[2] != 0) return GMM_E_SYNC;
     return (st2[0] != 0 || st2[1] == 0) ? GMM_E_PARAMS : GMM_OK;
 }
 
@@ -386,65 +344,60 @@ const char* gmm_status_string(int status) {
         case GMM_E_WORKSPACE: return "workspace missing, misaligned or too small";
         case GMM_E_PARAMS: return "invalid parameter values";
         case GMM_E_HIP: return "HIP runtime error";
-        case GMM_E_UNSUPPORTED: return "shape or schedule not supported by this build or device";
-        case GMM_E_SYNC: return "cooperative exchange between workgroups timed out";
+        case GMM_E_UNSUPPORTED: return "shape not supported by this build";
         default: return "unknown status";
     }
 }
 
 int gmm_profile_begin(int32_t max_launches) {
     if (max_launches < 1 || max_launches > (1 << 16)) return GMM_E_INVALID;
-    if (g_prof.cap < max_launches) {
-        hipEvent_t* e1 = new (std::nothrow) hipEvent_t[2 * max_launches];
-        hipEvent_t* e2 = new (std::nothrow) hipEvent_t[2 * max_launches];
-        if (!e1 || !e2) {
-            delete[] e1;
-            delete[] e2;
-            return GMM_E_INVALID;
-        }
-        for (int i = 0; i < 2 * g_prof.cap; ++i) {
-            (void)hipEventDestroy(g_prof.ev1[i]);
-            (void)hipEventDestroy(g_prof.ev2[i]);
-        }
-        delete[] g_prof.ev1;
-        delete[] g_prof.ev2;
-        g_prof.ev1 = e1;
-        g_prof.ev2 = e2;
-        for (int i = 0; i < 2 * max_launches; ++i) {
-            if (hipEventCreate(&e1[i]) != hipSuccess || hipEventCreate(&e2[i]) != hipSuccess) {
-                g_prof.cap = 0;
-                return GMM_E_HIP;
-            }
-        }
-        g_prof.cap = max_launches;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    prof_release();
+    g_prof.ev1 = new (std::nothrow) hipEvent_t[2 * max_launches]();
+    g_prof.ev2 = new (std::nothrow) hipEvent_t[2 * max_launches]();
+    g_prof.cap = max_launches;
+    if (!g_prof.ev1 || !g_prof.ev2) {
+        prof_release();
+        return GMM_E_INVALID;
     }
-    g_prof.n1 = g_prof.n2 = 0;
+    for (int i = 0; i < 2 * max_launches; ++i) {
+        if (hipEventCreate(&g_prof.ev1[i]) != hipSuccess ||
+            hipEventCreate(&g_prof.ev2[i]) != hipSuccess) {
+            prof_release();
+            return GMM_E_HIP;
+        }
+    }
     g_prof.on = true;
     return GMM_OK;
 }
 
 int gmm_profile_end(double* ms1, int32_t* n1, double* ms2, int32_t* n2) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof.on) return GMM_E_INVALID;
     g_prof.on = false;
-    double t1 = 0.0, t2 = 0.0;
-    for (int i = 0; i < g_prof.n1; ++i) {
-        float ms = 0.0f;
-        if (hipEventSynchronize(g_prof.ev1[2 * i + 1]) != hipSuccess ||
-            hipEventElapsedTime(&ms, g_prof.ev1[2 * i], g_prof.ev1[2 * i + 1]) != hipSuccess)
-            return GMM_E_HIP;
-        t1 += ms;
+    double t[2] = {0.0, 0.0};
+    int rc = GMM_OK;
+    for (int pass = 0; pass < 2 && rc == GMM_OK; ++pass) {
+        hipEvent_t* ev = pass == 0 ? g_prof.ev1 : g_prof.ev2;
+        const int cnt = pass == 0 ? g_prof.n1 : g_prof.n2;
+        for (int i = 0; i < cnt; ++i) {
+            float ms = 0.0f;
+            if (hipEventSynchronize(ev[2 * i + 1]) != hipSuccess ||
+                hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess) {
+                rc = GMM_E_HIP;
+                break;
+            }
+            t[pass] += ms;
+        }
     }
-    for (int i = 0; i < g_prof.n2; ++i) {
-        float ms = 0.0f;
-        if (hipEventSynchronize(g_prof.ev2[2 * i + 1]) != hipSuccess ||
-            hipEventElapsedTime(&ms, g_prof.ev2[2 * i], g_prof.ev2[2 * i + 1]) != hipSuccess)
-            return GMM_E_HIP;
-        t2 += ms;
+    if (rc == GMM_OK) {
+        if (ms1) *ms1 = t[0];
+        if (n1) *n1 = g_prof.n1;
+        if (ms2) *ms2 = t[1];
+        if (n2) *n2 = g_prof.n2;
     }
-    if (ms1) *ms1 = t1;
-    if (n1) *n1 = g_prof.n1;
-    if (ms2) *ms2 = t2;
-    if (n2) *n2 = g_prof.n2;
-    return GMM_OK;
+    prof_release();
+    return rc;
 }
 
 int32_t gmm_version(void) { return 100; }

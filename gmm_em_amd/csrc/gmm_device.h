@@ -62,6 +62,19 @@ __device__ __forceinline__ void lse_merge(double& m, float& s, double m2, float 
     m = mn;
 }
 
+// exp(t) for t <= 0 with fp32-level relative accuracy over the whole fp64
+// range: exp(t) = 2^j * 2^f with j = rint(t log2 e) and |f| <= 1/2, the
+// fraction through the hardware base-2 exponential (fp32) and the power of two
+// through ldexp (fp64, gradual underflow, exactly 0 below 2^-1075). A
+// responsibility therefore vanishes where exp underflows in fp64, not where it
+// underflows in fp32 (about exp(-104)). t = -inf (padding) gives 0.
+__device__ __forceinline__ double exp_f64range(double t) {
+    const double y = fmax(t, -1100.0) * 1.4426950408889634074;
+    const double j = rint(y);
+    const float f = (float)(y - j);
+    return ldexp((double)__builtin_amdgcn_exp2f(f), (int)j);
+}
+
 __device__ __forceinline__ double shfl_xor_d(double v, int off) {
     return __shfl_xor(v, off);
 }

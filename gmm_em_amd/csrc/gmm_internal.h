@@ -42,8 +42,6 @@ struct Plan {
     double* npart = nullptr;   // [ngroups][kp] responsibility mass partials
     double* part = nullptr;    // [ngroups][kp][2*dp] first/second moment partials
     double* ll_tmp = nullptr;  // [1] scratch total
-    double2* xbuf = nullptr;   // [ngroups][4][kgroups][32] cooperative exchange slots
-    unsigned* counters = nullptr;  // [ngroups][kgroups] cooperative progress flags
     int kgroups = 0;           // K-groups of the statistics pass (blocks per row group)
     bool wide = false;         // dp > MAX_DP: the D-sliced wide kernels
     int64_t chunk = 0;         // rows per chunk (CHUNK_ROWS or WIDE_CHUNK_ROWS)
@@ -67,10 +65,6 @@ hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, i
                         const double* lse, int acc, hipStream_t st);
 hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floor, float* w,
                            float* mu, float* var, hipStream_t st);
-// Cooperative single pass over all n rows with `groups` row groups (every
-// block co-resident); fails if the grid cannot be co-resident.
-hipError_t launch_coop(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                       int groups, hipStream_t st);
 // Wide path (pl.wide): normaliser partials + merge (writes lse_out, the
 // log-likelihood partials and, with m > 0, the top-m outputs), and the
 // statistics pass.
@@ -82,7 +76,6 @@ hipError_t launch_wide_stats(const Plan& pl, const void* x, int64_t n, int64_t l
 // k-means statistics of the wide path (one dim slice per wave)
 hipError_t launch_wide_km_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                                 const int32_t* z, int acc, hipStream_t st);
-int coop_blocks_per_cu(int dp);
 int waves_per_stats_block(int dp);
 hipError_t launch_ll_final(const Plan& pl, int nparts, double* out, hipStream_t st,
                            double scale = 1.0);

@@ -468,7 +468,7 @@ void k_wstats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             bool any = false;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                r[q] = (double)__expf((float)(l[q] + cc - ls[4 * q + h]));
+                r[q] = exp_f64range(l[q] + cc - ls[4 * q + h]);
                 n64 += r[q];
                 any = any || r[q] != 0.0;
             }

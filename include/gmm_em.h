@@ -56,8 +56,7 @@ typedef enum {
     GMM_E_WORKSPACE = 3, /* workspace missing or too small */
     GMM_E_PARAMS = 4,    /* invalid parameter values (reported by gmm_device_status) */
     GMM_E_HIP = 5,       /* a HIP runtime call failed */
-    GMM_E_UNSUPPORTED = 6, /* shape outside what this build supports */
-    GMM_E_SYNC = 7       /* cooperative exchange timed out (reported by gmm_device_status) */
+    GMM_E_UNSUPPORTED = 6  /* shape outside what this build supports */
 } gmm_status;
 
 typedef enum { GMM_F32 = 0, GMM_BF16 = 1 } gmm_dtype;
@@ -80,10 +79,11 @@ size_t gmm_workspace_bytes(int32_t d, int32_t k);
  *   w'[k] = N[k]/n, mu'[k] = S1[k]/N[k], var'[k] = max(S2[k]/N[k] - mu'[k]^2, var_floor)
  * (a component with N[k] == 0 keeps its mean and variance and gets weight 0).
  * r is never stored: it lives in registers between the two contractions.
- * Schedule: two passes over the rows (normalisers, then statistics) by
- * default; GMM_EM_SCHEDULE=coop selects a single cooperative pass in which
- * the workgroups of a row group exchange per-row partial normalisers through
- * L2 (it returns GMM_E_UNSUPPORTED where the grid cannot be co-resident).
+ * Schedule: two passes over the rows (normalisers, then statistics); the
+ * second recomputes the log-densities instead of storing them.
+ * Responsibilities keep the fp64 exponent range: a component whose
+ * responsibilities are all below fp32's smallest value but above fp64's
+ * still gets a nonzero N[k].
  * loglik_dev (device, 1 double, may be NULL) receives sum_n lse[n] for the
  * INPUT parameters. var_floor must be finite and >= 0. n >= 1. */
 int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
@@ -172,22 +172,24 @@ int gmm_kmeans_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_d
                    size_t workspace_bytes, void* stream);
 
 /* Synchronises the stream and returns GMM_E_PARAMS if the last call that used
- * this workspace found invalid parameter values, GMM_E_SYNC if its
- * cooperative exchange timed out, GMM_OK otherwise, or GMM_E_HIP if the
- * synchronisation failed. */
+ * this workspace found invalid parameter values, GMM_OK otherwise, or
+ * GMM_E_HIP if the synchronisation failed. */
 int gmm_device_status(const void* workspace, void* stream);
 
 /* Static description of a status code. */
 const char* gmm_status_string(int status);
 
-/* Measurement hook. gmm_profile_begin(max_launches) starts recording HIP
- * events on the caller's stream around every normaliser-pass (pass 1) and
- * statistics-pass (pass 2: the two-pass schedule's statistics kernel, or the
- * single cooperative kernel) launch of the following calls, up to
- * max_launches of each (events are created on first use; no device memory is
- * allocated). gmm_profile_end() synchronises those events and returns the
- * summed milliseconds and launch counts of each pass, then stops recording.
- * Not thread-safe; meant for benchmarks. */
+/* Measurement hook (not part of the method). gmm_profile_begin(max_launches)
+ * creates 4 * max_launches HIP events (host objects; no device memory) and
+ * starts recording them on the calling entry point's stream around every
+ * normaliser-pass (pass 1) and statistics-pass (pass 2) launch of the calls
+ * that follow, up to max_launches of each. gmm_profile_end() synchronises
+ * those events, returns the summed milliseconds and launch counts of each
+ * pass, stops recording and destroys the events (GMM_E_INVALID if no
+ * recording is active). This recording is the library's only process-wide
+ * state: it is guarded by a mutex, but it is outside the re-entrancy promise
+ * above (calls on several streams between begin and end are all recorded
+ * into the same totals). Meant for benchmarks. */
 int gmm_profile_begin(int32_t max_launches);
 int gmm_profile_end(double* ms_pass1, int32_t* launches_pass1, double* ms_pass2,
                     int32_t* launches_pass2);

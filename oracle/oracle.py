@@ -201,17 +201,26 @@ def topm(x, w, mu, var, m: int):
     return idx, resp, gap
 
 
-def fit(x, w, mu, var, var_floor: float = 1e-6, iters: int = 10, tol: float = 0.0):
+def fit(x, w, mu, var, var_floor: float = 1e-6, iters: int = 10, tol: float = 0.0,
+        param_dtype=np.float64):
     """Run EM. Returns (w, mu, var, history) with history[t] = L(theta_t).
 
     Stops early only when tol > 0 and L(theta_t) - L(theta_{t-1}) <
     tol * |L(theta_t)|; the parameters returned are those after the last
     step taken.
+
+    ``param_dtype=np.float32`` rounds the parameters to fp32 after every step
+    (the precision in which a caller that stores fp32 parameters carries them
+    from one step to the next); each step's arithmetic stays fp64. Comparing
+    that trajectory with the fp64 one measures how much EM's own dynamics
+    amplify a one-ulp perturbation of the parameters over the iterations.
     """
     hist = []
     for _ in range(iters):
         w2, mu2, v2, L, _ = em_step(x, w, mu, var, var_floor)
         hist.append(L)
+        if param_dtype is not np.float64:
+            w2, mu2, v2 = (np.asarray(a, dtype=param_dtype).astype(np.float64) for a in (w2, mu2, v2))
         w, mu, var = w2, mu2, v2
         if tol > 0 and len(hist) >= 2 and hist[-1] - hist[-2] < tol * abs(hist[-1]):
             break

@@ -142,3 +142,23 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_no_hidden_run_time_switches():
+    # the library's behaviour is set by its arguments only: no environment
+    # variable is read anywhere in its sources
+    csrc = os.path.join(ROOT, "gmm_em_amd", "csrc")
+    for name in os.listdir(csrc):
+        src = open(os.path.join(csrc, name)).read()
+        assert "getenv" not in src and "secure_getenv" not in src, name
+
+
+def test_profile_hook_states(ops):
+    # end without begin is an error; begin validates its size; begin/end with
+    # no launch in between returns zero counts and releases its events
+    f, i = ctypes.c_double, ctypes.c_int32
+    a, b, na, nb = f(0), f(0), i(0), i(0)
+    refs = (ctypes.byref(a), ctypes.byref(na), ctypes.byref(b), ctypes.byref(nb))
+    assert ops.lib.gmm_profile_end(*refs) == ops.GMM_E_INVALID
+    assert ops.lib.gmm_profile_begin(0) == ops.GMM_E_INVALID
+    assert ops.lib.gmm_profile_begin(1 << 20) == ops.GMM_E_INVALID

@@ -230,6 +230,92 @@ def test_affine_equivariance():
     assert r1[3] == pytest.approx(r0[3] - len(x) * np.log(np.abs(a)).sum(), rel=1e-13)
 
 
+def test_fit_tol_rule_on_a_scripted_history(monkeypatch):
+    # The stopping rule of fit: after step t >= 1, stop when
+    # L_t - L_{t-1} < tol * |L_t| (strict). Scripted log-likelihoods (exact
+    # binary fractions) place one step just above the threshold and the next
+    # below it, so an off-by-one, a sign slip, a non-strict comparison or a
+    # threshold relative to the wrong L fails.
+    script = iter([-1024.0, -512.0, -511.5, -511.25, -100.0, -50.0])
+    calls = []
+
+    def fake_step(x, w, mu, var, floor):
+        calls.append(1)
+        n = len(calls)
+        return (np.full(1, float(n)), np.full((1, 1), float(n)), np.ones((1, 1)),
+                next(script), np.ones(1))
+
+    monkeypatch.setattr(oracle, "em_step", fake_step)
+    tol = 2.0 ** -10
+    # t=1: 512 >= tol*512; t=2: 0.5 >= tol*511.5 (= 0.4995...); t=3: 0.25 < tol*511.25
+    w, mu, var, hist = oracle.fit(None, [1.0], [[0.0]], [[1.0]], 0.0, iters=6, tol=tol)
+    assert len(calls) == 4
+    np.testing.assert_array_equal(hist, [-1024.0, -512.0, -511.5, -511.25])
+    assert w[0] == 4.0 and mu[0, 0] == 4.0  # parameters of the last step taken
+    # a decrease stops at once; tol = 0 never stops early
+    script2 = iter([-10.0, -11.0, -5.0])
+    monkeypatch.setattr(oracle, "em_step", lambda *a: (np.ones(1), np.ones((1, 1)), np.ones((1, 1)),
+                                                        next(script2), np.ones(1)))
+    *_, h2 = oracle.fit(None, [1.0], [[0.0]], [[1.0]], 0.0, iters=3, tol=1e-9)
+    np.testing.assert_array_equal(h2, [-10.0, -11.0])
+    script3 = iter([-10.0, -10.0, -10.0])
+    monkeypatch.setattr(oracle, "em_step", lambda *a: (np.ones(1), np.ones((1, 1)), np.ones((1, 1)),
+                                                        next(script3), np.ones(1)))
+    *_, h3 = oracle.fit(None, [1.0], [[0.0]], [[1.0]], 0.0, iters=3, tol=0.0)
+    assert len(h3) == 3
+
+
+def test_fit_tol_stops_at_the_single_component_fixed_point():
+    # K = 1 reaches its closed form in one step and is a fixed point after
+    # that: L(theta_2) equals L(theta_1) to rounding, so any tol above the
+    # rounding level stops after exactly three steps, while the first
+    # improvement (from the initial parameters) is large.
+    rng = np.random.default_rng(31)
+    x = rng.normal(1.0, 2.0, size=(4000, 3)).astype(np.float32)
+    X = x.astype(np.float64)
+    w, mu, var, hist = oracle.fit(x, [1.0], [[5.0, -5.0, 0.0]], [[1.0, 1.0, 1.0]], 1e-6,
+                                  iters=10, tol=1e-12)
+    assert len(hist) == 3
+    want = -0.5 * len(x) * np.sum(np.log(2 * np.pi * X.var(axis=0)) + 1)
+    assert hist[1] == pytest.approx(want, rel=1e-12)
+    assert hist[2] == pytest.approx(want, rel=1e-12)
+    assert hist[1] - hist[0] > 1e-3 * abs(hist[1])
+
+
+def test_fit_fp32_parameter_rounding():
+    # Rows at 0 and 2 (half each): one component reaches mean 1 and
+    # variance 1 in one step, values exact in fp32, so rounding the
+    # parameters to fp32 between steps changes nothing; with rows at 0, 0.1
+    # and 0.7 the fitted mean is not exact in fp32, the rounded trajectory returns
+    # fp32 values and differs from the fp64 one by at most their rounding.
+    x = np.array([[0.0], [2.0]] * 50, dtype=np.float32)
+    a = oracle.fit(x, [1.0], [[5.0]], [[3.0]], 1e-6, iters=3)
+    b = oracle.fit(x, [1.0], [[5.0]], [[3.0]], 1e-6, iters=3, param_dtype=np.float32)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    assert a[1][0, 0] == 1.0 and a[2][0, 0] == 1.0
+    x2 = np.array([[0.0], [0.1], [0.7]] * 30, dtype=np.float32)
+    a2 = oracle.fit(x2, [1.0], [[5.0]], [[3.0]], 1e-6, iters=2)
+    b2 = oracle.fit(x2, [1.0], [[5.0]], [[3.0]], 1e-6, iters=2, param_dtype=np.float32)
+    assert np.float32(b2[1][0, 0]) == b2[1][0, 0] and np.float32(b2[2][0, 0]) == b2[2][0, 0]
+    assert a2[1][0, 0] != b2[1][0, 0]
+    assert abs(a2[1][0, 0] - b2[1][0, 0]) <= 2.0 ** -24 * abs(a2[1][0, 0])
+
+
+def test_tiny_mass_below_fp32_range_is_kept():
+    # Rows at 0, a unit-variance component at 0 and one at 20: every row has
+    # l_1 - l_0 = -200, so r_1 = exp(-200) / (1 + exp(-200)) ~ 1.4e-87, far
+    # below the smallest fp32 value but well inside fp64's range. The mass
+    # N_1 = N r_1 is kept, the component stays alive (weight > 0) and its
+    # mean moves onto the rows.
+    n = 1000
+    x = np.zeros((n, 1), dtype=np.float32)
+    w1, mu1, v1, L, nk = oracle.em_step(x, [0.5, 0.5], [[0.0], [20.0]], [[1.0], [1.0]], 1e-6)
+    r1 = np.exp(-200.0) / (1.0 + np.exp(-200.0))
+    assert nk[1] == pytest.approx(n * r1, rel=1e-12)
+    assert w1[1] > 0.0 and abs(mu1[1, 0]) < 1e-10 and v1[1, 0] == 1e-6
+
+
 def test_zero_weight_component_is_frozen():
     rng = np.random.default_rng(21)
     x = rng.normal(0, 1, size=(500, 3)).astype(np.float32)
