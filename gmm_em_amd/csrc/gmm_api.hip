@@ -14,7 +14,7 @@ namespace gmm {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-bool make_plan(int d, int k, void* ws, Plan* pl) {
+bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows, int max_groups) {
     if (d < 1 || k < 1 || k > (1 << 22)) return false;
     Plan p;
     p.d = d;
@@ -32,8 +32,10 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     const int kgroups = p.wide ? p.ntiles : p.ntiles / waves_per_stats_block(p.dp);
     p.kgroups = kgroups;
     int g = (1024 + kgroups - 1) / kgroups;
-    p.ngroups = g < 1 ? 1 : (g > 512 ? 512 : g);
-    p.chunk = p.wide ? WIDE_CHUNK_ROWS : CHUNK_ROWS;
+    p.ngroups = g < 1 ? 1 : (g > max_groups ? max_groups : g);
+    p.chunk = p.wide ? WIDE_CHUNK_ROWS : chunk_rows;
+    // per-row scratch: the narrow chunk, and at least the wide chunk
+    const int64_t srows = chunk_rows > WIDE_CHUNK_ROWS ? chunk_rows : WIDE_CHUNK_ROWS;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -44,11 +46,22 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
     const size_t o_shift = take((size_t)p.dp * sizeof(double));
     const size_t o_pg = take((size_t)p.kp * 2 * p.dp * sizeof(double));
     const size_t o_c = take((size_t)p.kp * sizeof(double));
-    const size_t o_lse = take((size_t)CHUNK_ROWS * sizeof(double));
-    const size_t o_ll = take((size_t)(CHUNK_ROWS / LL_ROWS) * sizeof(double));
+    const size_t o_lse = take((size_t)srows * sizeof(double));
+    const size_t o_ll = take((size_t)(srows / LL_ROWS) * sizeof(double));
     const size_t o_np = take((size_t)p.ngroups * p.kp * sizeof(double));
     const size_t o_part = take((size_t)p.ngroups * p.kp * 2 * p.dp * sizeof(double));
     const size_t o_lt = take(sizeof(double));
+    const bool i8 = !p.wide;  // the int8-slice E-step serves the narrow path
+    const size_t o_ia = take(i8 ? MAX_DP * sizeof(unsigned long long) : 0);
+    const size_t o_il = take(i8 ? MAX_DP * sizeof(int) : 0);
+    const size_t o_ip = take(i8 ? I8P_SIZE * sizeof(int) : 0);
+    const size_t o_id = take(i8 ? sizeof(double) : 0);
+    const size_t o_ic = take(i8 ? (size_t)p.ntiles * I8_MAX_LEV * I8_MAX_NC * 1024 : 0);
+    const size_t o_ie = take(i8 ? (size_t)p.kp * sizeof(int) : 0);
+    const size_t o_it = take(i8 ? (size_t)p.ntiles * I8_TINFO * sizeof(int) : 0);
+    p.i8_nc = i8 ? i8_nc_for(d) : 0;
+    p.i8_stats = i8 && i8_stats_for(p.dp);
+    const size_t o_ir = take(p.i8_stats ? (size_t)chunk_rows * S8_FLG : 0);
     const size_t wpart = p.wide ? (size_t)WIDE_CHUNK_ROWS * p.ntiles : 0;
     const size_t o_wl = take(wpart * sizeof(double2));
     const size_t o_wv = take(wpart * WIDE_TM * sizeof(double));
@@ -65,6 +78,16 @@ bool make_plan(int d, int k, void* ws, Plan* pl) {
         p.npart = (double*)(b + o_np);
         p.part = (double*)(b + o_part);
         p.ll_tmp = (double*)(b + o_lt);
+        if (i8) {
+            p.i8_amax = (unsigned long long*)(b + o_ia);
+            p.i8_lsb = (int*)(b + o_il);
+            p.i8_plan = (int*)(b + o_ip);
+            p.i8_dbl = (double*)(b + o_id);
+            p.i8_coef = (int8_t*)(b + o_ic);
+            p.i8_ek = (int*)(b + o_ie);
+            p.i8_tinfo = (int*)(b + o_it);
+            if (p.i8_stats) p.i8_rows = (int8_t*)(b + o_ir);
+        }
         if (p.wide) {
             p.wlpart = (double2*)(b + o_wl);
             p.wtval = (double*)(b + o_wv);
@@ -135,10 +158,13 @@ static void prof_mark(int pass, bool start, hipStream_t st) {
 // workspace scratch and the log-likelihood partials; with `stats`, each
 // chunk's statistics pass follows its normaliser pass; with m > 0, the top-m
 // components of each row are written to idx/resp; lse_rows, if given,
-// receives every row's normaliser instead of the chunk scratch.
+// receives every row's normaliser instead of the chunk scratch. With i8 (the
+// int8-slice prologue has run), pass 1 is the int8-slice kernel when the
+// prologue selected it.
 static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                              bool stats, hipStream_t st, int m = 0, int32_t* idx = nullptr,
-                             float* resp = nullptr, double* lse_rows = nullptr) {
+                             float* resp = nullptr, double* lse_rows = nullptr,
+                             bool i8 = false) {
     const size_t esz = dtype == GMM_BF16 ? 2 : 4;
     for (int64_t c0 = 0, ci = 0; c0 < n; c0 += pl.chunk, ++ci) {
         const int64_t cn = n - c0 < pl.chunk ? n - c0 : pl.chunk;
@@ -147,14 +173,33 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
         int32_t* ic = m > 0 ? idx + c0 * m : nullptr;
         float* rc = m > 0 ? resp + c0 * m : nullptr;
         prof_mark(1, true, st);
-        hipError_t e = pl.wide ? launch_wide_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st)
-                               : launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st);
+        hipError_t e = hipSuccess;
+        if (pl.wide) {
+            e = launch_wide_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st);
+        } else if (i8) {
+            // both variants are launched; the mode flag the prologue wrote
+            // lets exactly one of them do the work
+            e = launch_lse8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+            if (e == hipSuccess)
+                e = launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st, 0,
+                               pl.status + I8S_MODE);
+        } else {
+            e = launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st);
+        }
         prof_mark(1, false, st);
         if (e != hipSuccess) return e;
         if (stats) {
             prof_mark(2, true, st);
-            e = pl.wide ? launch_wide_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st)
-                        : launch_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+            if (pl.wide) {
+                e = launch_wide_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+            } else if (i8 && pl.i8_stats) {
+                // as for pass 1: the mode flag lets one of the two work
+                e = launch_stats8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+                if (e == hipSuccess)
+                    e = launch_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st, pl.status + I8S_MODE2);
+            } else {
+                e = launch_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+            }
             prof_mark(2, false, st);
             if (e != hipSuccess) return e;
         }
@@ -165,6 +210,21 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
 static int ll_parts(const Plan& pl, int64_t n) {
     const int64_t first = n < pl.chunk ? n : pl.chunk;
     return (int)((first + LL_ROWS - 1) / LL_ROWS);
+}
+
+// The launch sequence of one EM step on a planned workspace.
+static int em_step_planned(const Plan& pl, const void* x, int64_t n, int64_t ldx, int x_dtype,
+                           float* weights, float* means, float* variances, float var_floor,
+                           double* loglik_dev, hipStream_t st) {
+    double* ll_out = loglik_dev ? loglik_dev : pl.ll_tmp;
+    hipError_t e = launch_prologue(pl, weights, means, variances, st);
+    if (e == hipSuccess && !pl.wide)
+        e = launch_i8_prologue(pl, weights, means, variances, x, n, ldx, x_dtype, st);
+    if (e != hipSuccess) return GMM_E_HIP;
+    e = run_passes(pl, x, n, ldx, x_dtype, true, st, 0, nullptr, nullptr, nullptr, !pl.wide);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), ll_out, st);
+    if (e == hipSuccess) e = launch_finalize(pl, pl.ngroups, n, var_floor, weights, means, variances, st);
+    return hip_status(e);
 }
 
 extern "C" {
@@ -182,14 +242,8 @@ int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtyp
                           workspace_bytes, &pl);
     if (rc) return rc;
     if (n < 1 || !(var_floor >= 0.0f) || !isfinite(var_floor)) return GMM_E_INVALID;
-    hipStream_t st = (hipStream_t)stream;
-    double* ll_out = loglik_dev ? loglik_dev : pl.ll_tmp;
-    hipError_t e = launch_prologue(pl, weights, means, variances, st);
-    if (e != hipSuccess) return GMM_E_HIP;
-    e = run_passes(pl, x, n, ldx, x_dtype, true, st);
-    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), ll_out, st);
-    if (e == hipSuccess) e = launch_finalize(pl, pl.ngroups, n, var_floor, weights, means, variances, st);
-    return hip_status(e);
+    return em_step_planned(pl, x, n, ldx, x_dtype, weights, means, variances, var_floor, loglik_dev,
+                           (hipStream_t)stream);
 }
 
 int gmm_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype, float* weights,
@@ -237,8 +291,11 @@ int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype
     if (!total_dev) return GMM_E_INVALID;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_prologue(pl, weights, means, variances, st);
+    if (e == hipSuccess && !pl.wide)
+        e = launch_i8_prologue(pl, weights, means, variances, x, n, ldx, x_dtype, st);
     if (e == hipSuccess)
-        e = run_passes(pl, x, n, ldx, x_dtype, false, st, 0, nullptr, nullptr, per_row_dev);
+        e = run_passes(pl, x, n, ldx, x_dtype, false, st, 0, nullptr, nullptr, per_row_dev,
+                       !pl.wide);
     if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), total_dev, st);
     return hip_status(e);
 }
@@ -334,6 +391,15 @@ int gmm_device_status(const void* workspace, void* stream) {
     int st2[4] = {0, 0, 0, 0};
     if (hipMemcpy(st2, workspace, sizeof(st2), hipMemcpyDeviceToHost) != hipSuccess) return GMM_E_HIP;
     return (st2[0] != 0 || st2[1] == 0) ? GMM_E_PARAMS : GMM_OK;
+}
+
+int gmm_estep_arithmetic(const void* workspace, void* stream) {
+    if (!workspace) return -1;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return -1;
+    int st2[16] = {0};
+    if (hipMemcpy(st2, workspace, sizeof(st2), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+    if (st2[I8S_MODE] != 1) return GMM_ESTEP_FP64;
+    return st2[I8S_MODE2] == 1 ? GMM_ESTEP_INT8_SLICES_BOTH : GMM_ESTEP_INT8_SLICES;
 }
 
 const char* gmm_status_string(int status) {

@@ -1,0 +1,851 @@
+// gmm_i8.hip - the E-step contraction on exact int8 slices (v_mfma_i32_16x16x64_i8).
+//
+// The E-step log-density of the fused EM step ("Flash-GMM: A Memory-Efficient
+// Kernel for Scalable Soft Clustering", section 3: a tiled E-step whose
+// responsibilities never reach HBM) is the contraction
+//   l[n][k] = sum_f F[n][f] P[k][f] + c_k,   F = [a^2, a] (a = x - s),
+//                                            P = [-w/2, w b] (w = 1/var, b = mu - s),
+// whose terms cancel to a few nats while each is as large as w a^2 (up to
+// ~1e10 for a component at the variance floor). fp32 cannot hold that; fp64
+// MFMA can but runs at 1/64 of the int8 MFMA rate. Here the contraction is
+// computed exactly on int8 MFMA (the Ozaki splitting of a floating-point
+// product into exactly representable slices, Ozaki, Ogita, Oishi and Rump
+// 2012; on integer matrix units, Ootomo, Ozaki and Yokota 2024):
+//
+//  * every feature column is scaled by a power of two 2^G (per dimension and
+//    power, from the data's largest |a|) and written as digits of 7 bits:
+//    F = 2^G sum_i phi_i 128^-i, phi_1 in [-127, 127], phi_i in [-64, 64];
+//    integer data (the descriptor workload) needs 1 digit for a and 2 for a^2
+//    and is represented exactly;
+//  * every coefficient row, with the feature scales folded in, is scaled by a
+//    power of two 2^E_k per component and written as J digits q_j in
+//    [-64, 64]; 8 digits hold an fp64 coefficient exactly, and J is the
+//    smallest count whose truncation error is below 2^-20 nats for every row;
+//  * products of digits are exact, and so are their int32 sums (|sum| <
+//    2^23), so level L = i + j contributes 2^(E_k - 7L) * sum_f phi_i q_j
+//    exactly; the levels are added in fp64.
+// The result equals the fp64 contraction up to the 2^-20 truncation bound and
+// fp64 rounding of the level sum. Where the features are not exact in 3
+// digits and the truncation of the data cannot be bounded below 2^-20 nats,
+// the prologue selects the fp64 kernels instead (a flag in the workspace that
+// both kernel variants read; no host synchronisation).
+//
+// MFMA layout (16x16x64 i8, wave64, measured on gfx950): lane l = 16h + i
+// holds A[i][16h .. 16h+15] and B[16h .. 16h+15][i]; register q of the result
+// is C[4h + q][i]. Here A = feature digits of 16 rows, B = coefficient digits
+// of 16 components: lane (h, i) ends with l[row 4h + q][component i].
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "gmm_device.h"
+#include "gmm_internal.h"
+
+namespace gmm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Layout of the packed feature row (bytes): digit blocks i = 1 .. max(Ia, Ib),
+// each [a^2 digit i (d bytes) if i <= Ib][a digit i (d bytes) if i <= Ia],
+// zero padding up to a multiple of 64 (one MFMA chunk).
+struct I8Layout {
+    int ia, ib, fl0, nc;  // digit counts, used bytes, 64-byte chunks
+    int off_b[I8_MAX_DIGITS + 1], off_a[I8_MAX_DIGITS + 1];  // block offsets, -1 if absent
+};
+
+__device__ __forceinline__ I8Layout i8_layout(const int* plan, int d) {
+    I8Layout L;
+    L.ia = plan[I8P_IA];
+    L.ib = plan[I8P_IB];
+    int off = 0;
+    const int im = L.ia > L.ib ? L.ia : L.ib;
+    for (int i = 1; i <= I8_MAX_DIGITS; ++i) {
+        L.off_b[i] = -1;
+        L.off_a[i] = -1;
+        if (i <= im) {
+            if (i <= L.ib) { L.off_b[i] = off; off += d; }
+            if (i <= L.ia) { L.off_a[i] = off; off += d; }
+        }
+    }
+    L.fl0 = off;
+    L.nc = (off + 63) / 64;
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// Data pass: per dimension, the largest |a| (a = x - s) and the lowest set bit
+// over all rows. a is formed in fp64 exactly (fp32 data minus an integer).
+// ---------------------------------------------------------------------------
+__global__ void k_i8_reset(unsigned long long* amax, int* lsb, int dp) {
+    for (int i = threadIdx.x; i < dp; i += blockDim.x) {
+        amax[i] = 0ull;
+        lsb[i] = 0x7fffffff;
+    }
+}
+
+__device__ __forceinline__ int lowest_bit_exponent(double a) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(a);
+    const int be = (int)((u >> 52) & 0x7ff);
+    const unsigned long long frac = u & ((1ull << 52) - 1);
+    if (be == 0) return -1074 + __builtin_ctzll(frac);  // subnormal (a != 0)
+    return be - 1075 + __builtin_ctzll(frac | (1ull << 52));
+}
+
+template <typename XT>
+__global__ __launch_bounds__(256) void k_i8_xstats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
+                                                   int dp, const double* __restrict__ shift,
+                                                   unsigned long long* __restrict__ amax,
+                                                   int* __restrict__ lsb, int* __restrict__ status) {
+    __shared__ unsigned long long sm[256];
+    __shared__ int sl[256];
+    const int dd = threadIdx.x & 127, r0 = threadIdx.x >> 7;  // two rows per sweep, 128 dims
+    const bool live = dd < d;
+    const double s = live ? shift[(dd & 1) * (dp >> 1) + (dd >> 1)] : 0.0;
+    unsigned long long mx = 0ull;
+    int lo = 0x7fffffff, bad = 0;
+    if (live) {
+        // 8 rows per thread and sweep, loaded together
+        constexpr int U = 8;
+        const int64_t stride = (int64_t)gridDim.x * 2 * U;
+        for (int64_t base = (int64_t)blockIdx.x * 2 * U + r0; base < n; base += stride) {
+            float xv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t row = base + 2 * u;
+                xv[u] = row < n ? load_x(x + row * ldx + dd) : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (base + 2 * u >= n) continue;
+                const double a = (double)xv[u] - s;
+                if (!isfinite(a)) { bad = 1; continue; }
+                if (a != 0.0) {
+                    const unsigned long long b = (unsigned long long)__double_as_longlong(fabs(a));
+                    mx = b > mx ? b : mx;
+                    const int e = lowest_bit_exponent(a);
+                    lo = e < lo ? e : lo;
+                }
+            }
+        }
+    }
+    sm[threadIdx.x] = mx;
+    sl[threadIdx.x] = lo;
+    __syncthreads();
+    if (threadIdx.x < 128 && live) {
+        const unsigned long long m2 = sm[threadIdx.x + 128];
+        const int l2 = sl[threadIdx.x + 128];
+        mx = mx > m2 ? mx : m2;
+        lo = lo < l2 ? lo : l2;
+        if (mx) atomicMax(&amax[dd], mx);
+        if (lo != 0x7fffffff) atomicMin(&lsb[dd], lo);
+    }
+    if (bad) atomicOr(&status[I8S_NONFINITE], 1);
+}
+
+// Smallest g with v <= 127/128 * 2^g (v >= 0; v = 0 gives 0).
+__device__ __forceinline__ int scale_exp(double v) {
+    if (!(v > 0.0)) return 0;
+    int g = ilogb(v) + 1;  // v < 2^g
+    if (ldexp(v, -g) > 127.0 / 128.0) ++g;
+    return g;
+}
+
+// ---------------------------------------------------------------------------
+// Plan: per-dimension scales, digit counts and the bound inputs (one block).
+// plan[I8P_GA + d], plan[I8P_GB + d]: exponents G of the a and a^2 columns;
+// plan[I8P_IA / I8P_IB]: digits per column kind; plan[I8P_TRUNC_A / _B]: 1 if
+// that kind is not exact in its digits; dbl[0] = sum over columns of the
+// largest scaled |feature| (bounds the coefficient truncation error).
+// ---------------------------------------------------------------------------
+__global__ void k_i8_plan(const unsigned long long* __restrict__ amax, const int* __restrict__ lsb,
+                          int d, int* __restrict__ plan, double* __restrict__ dbl,
+                          int* __restrict__ status) {
+    __shared__ int s_ia[128], s_ib[128];
+    __shared__ double s_sf[128];
+    const int dd = threadIdx.x;
+    int ia = 1, ib = 1;
+    double sf = 0.0;
+    if (dd < d) {
+        const double am = __longlong_as_double((long long)amax[dd]);
+        const double bm = am * am;
+        const int ga = scale_exp(am), gb = scale_exp(bm);
+        plan[I8P_GA + dd] = ga;
+        plan[I8P_GB + dd] = gb;
+        if (am > 0.0) {
+            const int lo = lsb[dd];
+            // digits i cover down to 2^(g - 7i): exact once g - 7i <= lowest bit
+            ia = (ga - lo + 6) / 7;
+            ib = (gb - 2 * lo + 6) / 7;
+            ia = ia < 1 ? 1 : ia;
+            ib = ib < 1 ? 1 : ib;
+        }
+        sf = ldexp(am, -ga) + ldexp(bm, -gb);
+    }
+    s_ia[dd] = ia;
+    s_ib[dd] = ib;
+    s_sf[dd] = sf;
+    __syncthreads();
+    if (dd == 0) {
+        int ma = 1, mb = 1;
+        double tot = 0.0;
+        for (int j = 0; j < d; ++j) {
+            ma = s_ia[j] > ma ? s_ia[j] : ma;
+            mb = s_ib[j] > mb ? s_ib[j] : mb;
+            tot += s_sf[j];
+        }
+        plan[I8P_TRUNC_A] = ma > I8_MAX_DIGITS;
+        plan[I8P_TRUNC_B] = mb > I8_MAX_DIGITS;
+        ma = ma > I8_MAX_DIGITS ? I8_MAX_DIGITS : ma;
+        mb = mb > I8_MAX_DIGITS ? I8_MAX_DIGITS : mb;
+        plan[I8P_IA] = ma;
+        plan[I8P_IB] = mb;
+        dbl[0] = tot;
+        const int fl0 = d * (ma + mb);
+        if ((fl0 + 63) / 64 > I8_MAX_NC) atomicOr(&status[I8S_FAIL], 1);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Coefficient digits, one block per 16-component K-tile (256 threads: 16 per
+// component). Writes, for each level L = 2 .. Imax + J_t (lev = L - 2), the
+// digit vector matched position by position to the packed feature row
+// (feature digit i meets coefficient digit L - i), in MFMA B-operand order,
+// as consecutive 1 KB pieces (a tile is one contiguous copy). Also E_k and
+// the tile's level count.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_i8_coef(const float* __restrict__ w, const float* __restrict__ mu,
+                                                 const float* __restrict__ var, int k, int d, int dp,
+                                                 const double* __restrict__ shift,
+                                                 const int* __restrict__ plan,
+                                                 const double* __restrict__ dbl,
+                                                 int8_t* __restrict__ coef8, int* __restrict__ ek,
+                                                 int* __restrict__ tinfo, int* __restrict__ status) {
+    __shared__ int8_t dig[16][2 * MAX_DP][I8_MAX_J];  // [comp][column][digit]
+    __shared__ double red[256];
+    __shared__ int s_e[16], s_j[16];
+    const int tile = blockIdx.x;
+    const int c = threadIdx.x >> 4, sub = threadIdx.x & 15;
+    const int slot = tile * 16 + c;
+    const bool live = slot < k;
+    const I8Layout L = i8_layout(plan, d);
+    // a layout wider than the kernels' chunk budget: k_i8_plan has already
+    // marked the int8 path inapplicable, and nothing is written
+    if (L.nc > I8_MAX_NC) return;
+    const int dph = dp >> 1;
+    // columns: 0 .. d-1 the a^2 coefficients (-w/2), d .. 2d-1 the a coefficients (w b)
+    auto coef_u = [&](int col) -> double {
+        const int dd = col < d ? col : col - d;
+        const double s = shift[(dd & 1) * dph + (dd >> 1)];
+        const double v = (double)var[(int64_t)slot * d + dd];
+        const double iw = 1.0 / v;
+        if (col < d) return ldexp(-0.5 * iw, plan[I8P_GB + dd]);
+        return ldexp(iw * ((double)mu[(int64_t)slot * d + dd] - s), plan[I8P_GA + dd]);
+    };
+    double um = 0.0;
+    if (live)
+        for (int col = sub; col < 2 * d; col += 16) um = fmax(um, fabs(coef_u(col)));
+    red[threadIdx.x] = um;
+    __syncthreads();
+    if (sub == 0) {
+        double m = 0.0;
+        for (int j = 0; j < 16; ++j) m = fmax(m, red[threadIdx.x + j]);
+        // |coefficient| * 2^-E <= 1/2, so the first digit lies in [-64, 64]
+        const int e = m > 0.0 ? ilogb(m) + 2 : 0;
+        // coefficient truncation after J digits: 2^E * 2^(-7J-1) * sum_f max|F_f|
+        int J = 1;
+        while (J < I8_MAX_J && ldexp(dbl[0], e - 7 * J - 1) > I8_DELTA) ++J;
+        s_e[c] = e;
+        s_j[c] = live ? J : 1;
+        if (live) ek[slot] = e;
+        else ek[slot] = 0;
+    }
+    __syncthreads();
+    const int e = s_e[c];
+    int jt = 1;
+    for (int j = 0; j < 16; ++j) jt = s_j[j] > jt ? s_j[j] : jt;
+    // digits (and the feature-truncation bound for inexact data)
+    double tb = 0.0;
+    for (int col = sub; col < 2 * MAX_DP; col += 16) {
+        double r = (live && col < 2 * d) ? ldexp(coef_u(col), -e) : 0.0;
+        if (live && col < 2 * d) {
+            const bool trunc = col < d ? plan[I8P_TRUNC_B] : plan[I8P_TRUNC_A];
+            const int id = col < d ? L.ib : L.ia;
+            if (trunc) tb += fabs(r) * ldexp(1.0, e - 7 * id - 1);
+        }
+        for (int j = 0; j < I8_MAX_J; ++j) {
+            const double t = r * 128.0;
+            const double q = rint(t);
+            dig[c][col][j] = (int8_t)q;
+            r = t - q;
+        }
+    }
+    red[threadIdx.x] = tb;
+    __syncthreads();
+    if (sub == 0 && live) {
+        double t = 0.0;
+        for (int j = 0; j < 16; ++j) t += red[threadIdx.x + j];
+        if (t > I8_DELTA) atomicOr(&status[I8S_FAIL], 1);
+    }
+    const int im = L.ia > L.ib ? L.ia : L.ib;
+    const int nlev = im + jt - 1;
+    if (threadIdx.x == 0) {
+        tinfo[tile * I8_TINFO] = nlev;
+        atomicMax(&status[I8S_MAXLEV], nlev);
+    }
+    // level vectors in B-operand order, every chunk of the packed row (zero
+    // where the level pairs no digits): piece (lev * nc + chunk) holds, at
+    // [lane 16h + c][16 bytes], positions 64 chunk + 16h .. +15 of component c
+    const int nc = L.nc;
+    int8_t* dst = coef8 + (int64_t)tile * I8_MAX_LEV * I8_MAX_NC * 1024;
+    for (int lev = 0; lev < nlev; ++lev) {
+        const int Lv = lev + 2;
+        for (int pos = sub; pos < nc * 64; pos += 16) {
+            int v = 0;
+            for (int i = 1; i <= im; ++i) {
+                const int j = Lv - i;
+                if (j < 1 || j > jt) continue;
+                if (L.off_b[i] >= 0 && pos >= L.off_b[i] && pos < L.off_b[i] + d) v = dig[c][pos - L.off_b[i]][j - 1];
+                if (L.off_a[i] >= 0 && pos >= L.off_a[i] && pos < L.off_a[i] + d) v = dig[c][d + pos - L.off_a[i]][j - 1];
+            }
+            const int ch = pos >> 6, h = (pos >> 4) & 3, u = pos & 15;
+            dst[(int64_t)(lev * nc + ch) * 1024 + (16 * h + c) * 16 + u] = (int8_t)v;
+        }
+    }
+}
+
+// Mode: the int8 normaliser pass runs when no check failed and the data is
+// finite; the int8 statistics pass as well when a tile's digit levels fit
+// its registers (stats_ok: the kernel exists for this dimension).
+__global__ void k_i8_mode(int* status, const int* plan, int d, int stats_ok) {
+    if (threadIdx.x == 0) {
+        const int m1 = (status[I8S_FAIL] == 0 && status[I8S_NONFINITE] == 0) ? 1 : 0;
+        const I8Layout L = i8_layout(plan, d);
+        status[I8S_MODE] = m1;
+        status[I8S_MODE2] =
+            (m1 && stats_ok && L.nc <= S8_NC && status[I8S_MAXLEV] <= S8_LV) ? 1 : 0;
+    }
+}
+
+// One fold of the level sums: a pair of consecutive levels L, L+1 is first
+// combined exactly in int32 (128 acc_L + acc_{L+1}: |acc| < 2^22, so no
+// overflow), then added in fp64 with its power-of-two scale (a lone last
+// level comes with acc_{L+1} = 0). Both passes fold in the same order, so
+// they produce bitwise identical log-densities.
+__device__ __forceinline__ void fold_pair(double& l, int a, int b, double sc) {
+    l = fma((double)(a * 128 + b), sc, l);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1 on int8 slices: per-row logsumexp over all components.
+// Block = 8 waves, 64 rows per wave (four 16-row MFMA tiles), 512 rows. Each
+// wave packs the digit rows of its 64 rows once (through LDS) and keeps them
+// in registers as A operands; the K-tiles' level vectors stream through two
+// LDS buffers (tile t+1 is copied while tile t is contracted). Per tile and
+// level: the chunks holding nonzero digits, one int32 accumulator per row
+// tile, then l += acc * 2^(E_k - 7L) in fp64. The finished tile's values go
+// into the online logsumexp (fp64 running maximum, fp32 scaled sum).
+// ---------------------------------------------------------------------------
+constexpr int L8_WAVES = 8;
+constexpr int L8_RT = 4;  // 16-row tiles per wave
+constexpr int L8_ROWS = L8_WAVES * L8_RT * 16;
+
+template <int NC, typename XT>
+__global__ __launch_bounds__(L8_WAVES * 64, 1)
+void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
+            const double* __restrict__ shift, const int* __restrict__ plan,
+            const int8_t* __restrict__ coef8, const int* __restrict__ ek,
+            const int* __restrict__ tinfo, const double* __restrict__ cvec, int ntiles,
+            double* __restrict__ lse_out, double* __restrict__ llpart, int ll_accumulate,
+            int8_t* __restrict__ drows, const int* __restrict__ status) {
+    constexpr int FLS = NC * 64 + 16;            // LDS stride of a packed row (conflict-free b128 reads)
+    constexpr int TB = I8_MAX_LEV * NC * 1024;   // bytes of one tile's level vectors
+    constexpr int STG = L8_WAVES * 16 * FLS;     // staging of 16 rows per wave
+    static_assert(STG <= TB, "row staging aliases the second coefficient buffer");
+    __shared__ __attribute__((aligned(16))) int8_t cbuf[2][TB];
+    __shared__ double rowll[L8_ROWS];
+    if (status[I8S_MODE] != 1) return;  // the fp64 kernels run instead
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = lane & 15, h = lane >> 4;
+    const int64_t wrow = (int64_t)blockIdx.x * L8_ROWS + wave * (L8_RT * 16);
+    const I8Layout LY = i8_layout(plan, d);
+    const int dph = dp >> 1;
+    const bool hand_off = status[I8S_MODE2] == 1;
+
+    // ---- pack the wave's rows: digits of a^2 and a, through LDS
+    v4i A[L8_RT][NC];
+    {
+        int8_t* stg = &cbuf[1][wave * 16 * FLS];
+        for (int rt = 0; rt < L8_RT; ++rt) {
+            for (int e = lane; e < 16 * FLS / 16; e += 64) ((v4i*)stg)[e] = v4i{0, 0, 0, 0};
+            __syncthreads();
+            for (int e = lane; e < 16 * d; e += 64) {
+                const int r = e / d, dd = e - r * d;
+                const int64_t row = wrow + rt * 16 + r;
+                const double s = shift[(dd & 1) * dph + (dd >> 1)];
+                const double a = row < n ? (double)load_x(x + row * ldx + dd) - s : 0.0;
+                int8_t* pr = stg + r * FLS;
+                double va = ldexp(a, -plan[I8P_GA + dd]), vb = ldexp(a * a, -plan[I8P_GB + dd]);
+                for (int i = 1; i <= I8_MAX_DIGITS; ++i) {
+                    const double ta = va * 128.0, tb = vb * 128.0;
+                    const double qa = rint(ta), qb = rint(tb);
+                    va = ta - qa;
+                    vb = tb - qb;
+                    if (LY.off_a[i] >= 0) pr[LY.off_a[i] + dd] = (int8_t)qa;
+                    if (LY.off_b[i] >= 0) pr[LY.off_b[i] + dd] = (int8_t)qb;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < NC; ++c) A[rt][c] = *(const v4i*)(stg + ci * FLS + 64 * c + 16 * h);
+            // hand the packed rows to the statistics pass (row stride S8_FLG)
+            if (hand_off) {
+                const int per_row = LY.nc * 4;  // 16-byte pieces
+                for (int e = lane; e < 16 * per_row; e += 64) {
+                    const int r = e / per_row, u = e - r * per_row;
+                    const int64_t row = wrow + rt * 16 + r;
+                    if (row < n)
+                        *(v4i*)(drows + row * S8_FLG + u * 16) = *(const v4i*)(stg + r * FLS + u * 16);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- stream the K-tiles: tile t+1's level vectors are copied into the
+    // other buffer by buffer-to-LDS loads (one 1 KB operand piece per wave
+    // instruction, no registers held) while tile t is contracted
+    constexpr int TSTRIDE = I8_MAX_LEV * I8_MAX_NC * 1024;
+    const int nc = LY.nc;  // chunks of this call's packed rows (<= NC)
+    auto issue_tile = [&](int t, int buf) {
+        const int pieces = tinfo[t * I8_TINFO] * nc;
+        const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(coef8 + (int64_t)t * TSTRIDE), (short)0, TSTRIDE, BUF_RSRC_WORD3);
+        for (int p = wave; p < pieces; p += L8_WAVES)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                cr, (__attribute__((address_space(3))) void*)(cbuf[buf] + p * 1024), 16, lane * 16,
+                p * 1024, 0, 0);
+    };
+    double m[L8_RT][4];
+    float s[L8_RT][4];
+#pragma unroll
+    for (int rt = 0; rt < L8_RT; ++rt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            m[rt][q] = -1.0e300;
+            s[rt][q] = 0.0f;
+        }
+    issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+        const int nl = tinfo[t * I8_TINFO];
+        const int slot = t * 16 + ci;
+        const double scale = ldexp(1.0, ek[slot] - 14);  // level 2
+        const double cc = cvec[slot];
+        double l[L8_RT][4];
+#pragma unroll
+        for (int rt = 0; rt < L8_RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) l[rt][q] = 0.0;
+        const int8_t* cb = cbuf[buf] + lane * 16;
+        // one level: every chunk of the row (chunk NC-1 only when the rows
+        // use it), one int32 accumulator per row tile
+        auto mfma_level = [&](int lev, v4i (&acc)[L8_RT]) {
+            const int8_t* bl = cb + lev * nc * 1024;
+#pragma unroll
+            for (int rt = 0; rt < L8_RT; ++rt) acc[rt] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if (c < NC - 1 || nc == NC) {
+                    const v4i b = *(const v4i*)(bl + c * 1024);
+#pragma unroll
+                    for (int rt = 0; rt < L8_RT; ++rt) acc[rt] = mfma_i8(A[rt][c], b, acc[rt]);
+                }
+            }
+        };
+        v4i acc0[L8_RT], acc1[L8_RT];
+        double sc = scale * (1.0 / 128.0);  // a pair starting at level 2
+        for (int lev = 0; lev < nl; lev += 2) {
+            const bool two = lev + 1 < nl;
+            mfma_level(lev, acc0);
+            if (two) mfma_level(lev + 1, acc1);
+#pragma unroll
+            for (int rt = 0; rt < L8_RT; ++rt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) fold_pair(l[rt][q], acc0[rt][q], two ? acc1[rt][q] : 0, sc);
+            sc *= 1.0 / 16384.0;
+        }
+#pragma unroll
+        for (int rt = 0; rt < L8_RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) lse_push(m[rt][q], s[rt][q], l[rt][q] + cc);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t+1 have landed
+        __syncthreads();                // ... and every wave's; tile t's buffer is free
+    }
+
+    // ---- merge the 16 lanes holding the same rows (fixed butterfly order)
+#pragma unroll
+    for (int rt = 0; rt < L8_RT; ++rt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll 1
+            for (int off = 1; off < 16; off <<= 1) {
+                const double m2 = shfl_xor_d(m[rt][q], off);
+                const float s2 = __shfl_xor(s[rt][q], off);
+                lse_merge(m[rt][q], s[rt][q], m2, s2);
+            }
+        }
+    if (ci == 0) {
+#pragma unroll
+        for (int rt = 0; rt < L8_RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int lr = wave * (L8_RT * 16) + rt * 16 + 4 * h + q;
+                const int64_t row = (int64_t)blockIdx.x * L8_ROWS + lr;
+                double v = 0.0;
+                if (row < n) {
+                    v = m[rt][q] + log((double)s[rt][q]);
+                    if (lse_out) lse_out[row] = v;
+                }
+                rowll[lr] = v;
+            }
+    }
+    __syncthreads();
+    // one partial per 64 rows: wave w sums its own rows (fixed order)
+    {
+        double tot = rowll[wave * 64 + lane];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) tot += shfl_xor_d(tot, off);
+        const int64_t pi = (int64_t)blockIdx.x * (L8_ROWS / LL_ROWS) + wave;
+        if (lane == 0 && wrow < n) llpart[pi] = (ll_accumulate ? llpart[pi] : 0.0) + tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2 on int8 slices: statistics. Same organisation as the fp64
+// statistics pass (a block of 4 waves, wave w owning K-tile kg*4 + w, the
+// block walking its row group in 32-row tiles): the wave's coefficient digit
+// levels stay in registers, the row tiles' packed digit rows (written by the
+// normaliser pass) arrive by buffer-to-LDS copies, and the E-step is the int8
+// contraction with the normaliser pass's fold, so both passes see the same
+// log-densities bit for bit. The M-step is unchanged: fp64 MFMA of
+// r = exp(l - lse) against the rows' fp64 [a, a^2] (staged in LDS), with
+// register statistics over the row group. The int8 result layout gives lane
+// (h, i) rows 4h + q of a 16-row tile; the M-step takes its 4-row groups in
+// that order (row 16 rb + 4h + q for step (rb, q)), so responsibilities
+// still go from the E-step accumulators to the M-step operand in registers.
+// ---------------------------------------------------------------------------
+template <int DP, typename XT>
+__global__ __launch_bounds__(256, 1)
+void k_stats8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
+              const int8_t* __restrict__ drows, const int8_t* __restrict__ coef8,
+              const int* __restrict__ ek, const int* __restrict__ tinfo,
+              const double* __restrict__ cvec, const double* __restrict__ shift,
+              const int* __restrict__ plan, int ntiles, const double* __restrict__ lse,
+              int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
+              int accumulate, const int* __restrict__ status) {
+    constexpr int WV = 4, NT = 256;
+    constexpr int DPH = DP / 2, HS = DPH + 4, S = 4 * HS + 2;  // fp64 feature tile layout
+    constexpr int PER = STATS_ROWS * DP / NT;
+    constexpr int NJ = DP / 16;
+    constexpr int DGB = STATS_ROWS * S8_FLG;      // digit bytes of a 32-row tile
+    constexpr int DGP = (DGB + 1023) / 1024;      // 1 KB copy pieces
+    static_assert(PER * NT == STATS_ROWS * DP, "every thread stages the same number of values");
+    __shared__ __attribute__((aligned(16))) double fs[2][STATS_ROWS * S];
+    __shared__ double ls[2][STATS_ROWS];
+    __shared__ __attribute__((aligned(16))) int8_t dg[2][DGP * 1024];
+    if (status[I8S_MODE2] != 1) return;  // the fp64 statistics pass runs instead
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = lane & 15, h = lane >> 4;
+    const int kgroups = ntiles / WV;
+    const int nb = gridDim.x;
+    const int o = (nb % 8 == 0) ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int g = o / kgroups;
+    const int tile = (o % kgroups) * WV + wave;
+    const int slot = tile * 16 + ci;
+    const I8Layout LY = i8_layout(plan, d);
+    const int nc = LY.nc;
+    const int nl = tinfo[tile * I8_TINFO];
+
+    // the K-tile's digit levels (B operands), resident for the whole pass
+    v4i qd[S8_LV][S8_NC];
+    {
+        const int8_t* cp = coef8 + (int64_t)tile * (I8_MAX_LEV * I8_MAX_NC * 1024) + lane * 16;
+#pragma unroll
+        for (int lev = 0; lev < S8_LV; ++lev)
+#pragma unroll
+            for (int c = 0; c < S8_NC; ++c)
+                qd[lev][c] = (lev < nl && c < nc) ? *(const v4i*)(cp + (lev * nc + c) * 1024)
+                                                  : v4i{0, 0, 0, 0};
+    }
+    const double scale = ldexp(1.0, ek[slot] - 14);
+    const double cc = cvec[slot];
+
+    f64x4 acc[2 * NJ];
+#pragma unroll
+    for (int j = 0; j < 2 * NJ; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    double n64 = 0.0;
+
+    const int64_t gr0 = (int64_t)g * rows_per_group;
+    int64_t gr1 = gr0 + rows_per_group;
+    if (gr1 > n) gr1 = n;
+    const int64_t ntile_rows = gr1 > gr0 ? (gr1 - gr0 + STATS_ROWS - 1) / STATS_ROWS : 0;
+
+    // fp64 features for the M-step, staged as in the fp64 statistics pass
+    float xv[PER];
+    double lv = 0.0;
+    double shv[PER];
+    uint32_t xoff[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = tid + NT * i;
+        const int r = e / DP, dd = e % DP;
+        shv[i] = shift[(dd & 1) * DPH + (dd >> 1)];
+        xoff[i] = dd < d ? (uint32_t)(((int64_t)r * ldx + dd) * (int64_t)sizeof(XT)) : 0xFFFFFFF0u;
+    }
+    auto load = [&](int64_t it) {
+        const int64_t rbase = gr0 + it * STATS_ROWS;
+        int64_t nv = gr1 - rbase;
+        nv = nv < 0 ? 0 : (nv > STATS_ROWS ? STATS_ROWS : nv);
+        const int xbytes = nv > 0 ? (int)(((nv - 1) * ldx + d) * (int64_t)sizeof(XT)) : 0;
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + rbase * ldx), (short)0, xbytes, BUF_RSRC_WORD3);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) xv[i] = buf_load_x<XT>(xr, xoff[i]);
+        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
+        const int lrow = tid & (STATS_ROWS - 1);
+        const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
+        lv = lrow < nv ? v : INFINITY;  // rows past the row group: responsibility 0
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + NT * i;
+            const int r = e / DP, dd = e % DP;
+            const int pp = 2 * (dd & 1), t = dd >> 1;
+            const double a = (double)xv[i] - shv[i];
+            fs[buf][r * S + pp * HS + t] = a;
+            fs[buf][r * S + (pp + 1) * HS + t] = a * a;
+        }
+        ls[buf][tid & (STATS_ROWS - 1)] = lv;
+    };
+    // digit rows of tile it: contiguous in the workspace (stride S8_FLG), so
+    // the copy is DGP pieces of 1 KB; rows past the row group read as 0
+    auto issue_dg = [&](int64_t it, int buf) {
+        const int64_t rbase = gr0 + it * STATS_ROWS;
+        int64_t nv = gr1 - rbase;
+        nv = nv < 0 ? 0 : (nv > STATS_ROWS ? STATS_ROWS : nv);
+        const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(drows + rbase * S8_FLG), (short)0, (int)(nv * S8_FLG), BUF_RSRC_WORD3);
+        for (int p = wave; p < DGP; p += WV)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                dr, (__attribute__((address_space(3))) void*)(dg[buf] + p * 1024), 16, lane * 16,
+                p * 1024, 0, 0);
+    };
+
+    if (ntile_rows > 0) {
+        load(0);
+        issue_dg(0, 0);
+        store(0);
+        if (ntile_rows > 1) load(1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int64_t it = 0; it < ntile_rows; ++it) {
+        const int buf = (int)(it & 1);
+        // next tile's digit rows (its buffer was last read before the
+        // previous iteration's closing barrier)
+        if (it + 1 < ntile_rows) issue_dg(it + 1, buf ^ 1);
+        // E-step: two 16-row tiles, all levels, the normaliser pass's fold.
+        // Every chunk is contracted: a chunk past the rows' digits has zero
+        // coefficients (its digit bytes are not written and read as anything),
+        // and a missing second level of the last pair has zero coefficients.
+        const int8_t* db = dg[buf];
+        v4i A[2][S8_NC];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int c = 0; c < S8_NC; ++c)
+                A[rb][c] = *(const v4i*)(db + (16 * rb + ci) * S8_FLG + 64 * c + 16 * h);
+        double l[2][4];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) l[rb][q] = 0.0;
+        double sc = scale * (1.0 / 128.0);
+#pragma unroll
+        for (int lev = 0; lev < S8_LV; lev += 2) {
+            if (lev < nl) {
+                v4i a0[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+                v4i a1[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+#pragma unroll
+                for (int c = 0; c < S8_NC; ++c) {
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) a0[rb] = mfma_i8(A[rb][c], qd[lev][c], a0[rb]);
+                    if (lev + 1 < S8_LV) {
+#pragma unroll
+                        for (int rb = 0; rb < 2; ++rb)
+                            a1[rb] = mfma_i8(A[rb][c], qd[lev + 1 < S8_LV ? lev + 1 : lev][c], a1[rb]);
+                    }
+                }
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) fold_pair(l[rb][q], a0[rb][q], a1[rb][q], sc);
+                sc *= 1.0 / 16384.0;
+            }
+        }
+        // responsibilities of rows 16 rb + 4h + q
+        double r[2][4];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                r[rb][q] = exp_f64range(l[rb][q] + cc - ls[buf][16 * rb + 4 * h + q]);
+                n64 += r[rb][q];
+            }
+        // stage the next tile's fp64 features (buffer buf^1 was last read
+        // before the previous iteration's closing barrier)
+        if (it + 1 < ntile_rows) {
+            store(buf ^ 1);
+            if (it + 2 < ntile_rows) load(it + 2);
+        }
+        // M-step: step (rb, q) contracts r[row 16 rb + 4h + q][comp ci] with
+        // feature column 16j + ci of that row; a step whose 64
+        // responsibilities are all exactly zero adds nothing and is skipped
+        const double* fb = fs[buf];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double rv = r[rb][q];
+                if (__builtin_amdgcn_ballot_w64(rv != 0.0) == 0) continue;
+                const double* fm = fb + (16 * rb + 4 * h + q) * S;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int dd = 16 * j + ci;
+                    acc[j] = mfma4d(rv, fm[2 * (dd & 1) * HS + (dd >> 1)], acc[j]);
+                    acc[NJ + j] = mfma4d(rv, fm[(2 * (dd & 1) + 1) * HS + (dd >> 1)], acc[NJ + j]);
+                }
+            }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's digit copies of the next tile have landed
+        __syncthreads();
+    }
+
+    // responsibility mass: lanes ci, ci+16, ci+32, ci+48 hold disjoint rows
+    n64 += shfl_xor_d(n64, 16);
+    n64 += shfl_xor_d(n64, 32);
+    const int64_t gbase = (int64_t)g * ntiles * 16;
+    if (h == 0) {
+        double* np = npart + gbase + slot;
+        *np = (accumulate ? *np : 0.0) + n64;
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int comp = tile * 16 + 4 * q + h;
+            double* p2 = part + (gbase + comp) * (2 * DP) + 16 * j + ci;
+            *p2 = (accumulate ? *p2 : 0.0) + acc[j][q];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers.
+// ---------------------------------------------------------------------------
+hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
+                              const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st) {
+    hipLaunchKernelGGL(k_i8_reset, dim3(1), dim3(128), 0, st, pl.i8_amax, pl.i8_lsb, pl.dp);
+    if (n > 0) {
+        int64_t b = (n + 2047) / 2048;
+        const unsigned blocks = (unsigned)(b > 8192 ? 8192 : (b < 1 ? 1 : b));
+        if (dtype == 0)
+            hipLaunchKernelGGL(k_i8_xstats<float>, dim3(blocks), dim3(256), 0, st, (const float*)x, n,
+                               pl.d, ldx, pl.dp, pl.shift, pl.i8_amax, pl.i8_lsb, pl.status);
+        else
+            hipLaunchKernelGGL(k_i8_xstats<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t*)x,
+                               n, pl.d, ldx, pl.dp, pl.shift, pl.i8_amax, pl.i8_lsb, pl.status);
+    }
+    hipLaunchKernelGGL(k_i8_plan, dim3(1), dim3(128), 0, st, pl.i8_amax, pl.i8_lsb, pl.d, pl.i8_plan,
+                       pl.i8_dbl, pl.status);
+    hipLaunchKernelGGL(k_i8_coef, dim3(pl.ntiles), dim3(256), 0, st, w, mu, var, pl.k, pl.d, pl.dp,
+                       pl.shift, pl.i8_plan, pl.i8_dbl, pl.i8_coef, pl.i8_ek, pl.i8_tinfo, pl.status);
+    hipLaunchKernelGGL(k_i8_mode, dim3(1), dim3(64), 0, st, pl.status, pl.i8_plan, pl.d,
+                       pl.i8_stats ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <int NC, typename XT>
+static hipError_t launch_lse8_t(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
+                                int ll_acc, hipStream_t st) {
+    const int64_t blocks = (n + L8_ROWS - 1) / L8_ROWS;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_lse8<NC, XT>), dim3((unsigned)blocks), dim3(L8_WAVES * 64), 0, st,
+                       (const XT*)x, n, pl.d, ldx, pl.dp, pl.shift, pl.i8_plan, pl.i8_coef, pl.i8_ek,
+                       pl.i8_tinfo, pl.cvec, pl.ntiles, lse_out, pl.llpart, ll_acc, pl.i8_rows,
+                       pl.status);
+    return hipGetLastError();
+}
+
+// The kernel is instantiated for the largest chunk count the layout can need
+// at this dimension (unused chunks of a row hold zeros and are skipped by the
+// per-level chunk ranges).
+int i8_nc_for(int d) {
+    // digits: up to 3 for a and 3 for a^2, but at most I8_MAX_NC chunks
+    const int nc = (d * 2 * I8_MAX_DIGITS + 63) / 64;
+    return nc > I8_MAX_NC ? I8_MAX_NC : (nc < 2 ? 2 : nc);
+}
+
+hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                       double* lse_out, int ll_acc, hipStream_t st) {
+    switch (pl.i8_nc) {
+#define CASE(NCV)                                                                              \
+    case NCV:                                                                                  \
+        return dtype == 0 ? launch_lse8_t<NCV, float>(pl, x, n, ldx, lse_out, ll_acc, st)      \
+                          : launch_lse8_t<NCV, uint16_t>(pl, x, n, ldx, lse_out, ll_acc, st);
+        CASE(2) CASE(3) CASE(4) CASE(5) CASE(6)
+#undef CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DP, typename XT>
+static hipError_t launch_stats8_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
+                                  const double* lse, int acc, hipStream_t st) {
+    int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
+    if (rpg < STATS_ROWS) rpg = STATS_ROWS;
+    hipLaunchKernelGGL((k_stats8<DP, XT>), dim3(pl.ngroups * (pl.ntiles / 4)), dim3(256), 0, st,
+                       (const XT*)x, n, pl.d, ldx, pl.i8_rows, pl.i8_coef, pl.i8_ek, pl.i8_tinfo,
+                       pl.cvec, pl.shift, pl.i8_plan, pl.ntiles, lse, rpg, pl.part, pl.npart, acc,
+                       pl.status);
+    return hipGetLastError();
+}
+
+bool i8_stats_for(int dp) { return dp <= S8_MAX_DP; }
+
+hipError_t launch_stats8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                         const double* lse, int acc, hipStream_t st) {
+    switch (pl.dp) {
+#define CASE(DPV)                                                                          \
+    case DPV:                                                                              \
+        return dtype == 0 ? launch_stats8_t<DPV, float>(pl, x, n, ldx, lse, acc, st)      \
+                          : launch_stats8_t<DPV, uint16_t>(pl, x, n, ldx, lse, acc, st);
+        CASE(16) CASE(32) CASE(48) CASE(64) CASE(80) CASE(96) CASE(112)
+#undef CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gmm

@@ -24,6 +24,36 @@ constexpr int64_t CHUNK_ROWS = (int64_t)1 << 22;
 constexpr int64_t MAX_LDX = ((int64_t)1 << 24) - 1;
 // Rows per normaliser-pass block (one log-likelihood partial each).
 constexpr int LL_ROWS = 64;
+// Rows per staged tile of the statistics passes (two 16-row MFMA blocks).
+constexpr int STATS_ROWS = 32;
+
+// E-step on exact int8 slices (gmm_i8.hip). Digits per feature column kind
+// (a, a^2), coefficient digits (8 hold an fp64 value exactly), levels
+// i + j = 2 .. I + J, 64-byte chunks per packed row, truncation bound (nats).
+constexpr int I8_MAX_DIGITS = 3;
+constexpr int I8_MAX_J = 8;
+constexpr int I8_MAX_LEV = I8_MAX_DIGITS + I8_MAX_J - 1;
+constexpr int I8_MAX_NC = 6;
+constexpr double I8_DELTA = 9.5367431640625e-07;  // 2^-20
+// per tile: the number of levels (a tile's operands are levels x chunks
+// pieces of 1 KB)
+constexpr int I8_TINFO = 1;
+// plan[] indices: digit counts, truncation flags, per-dim scale exponents
+constexpr int I8P_IA = 0, I8P_IB = 1, I8P_TRUNC_A = 2, I8P_TRUNC_B = 3, I8P_GA = 8,
+              I8P_GB = 8 + MAX_DP, I8P_SIZE = 8 + 2 * MAX_DP;
+// status word slots: [0] invalid parameters, [1] some weight > 0,
+// [4] int8 path selected for this call, [5] int8 path not applicable,
+// [6] non-finite data value seen by the data pass
+constexpr int I8S_MODE = 4, I8S_FAIL = 5, I8S_NONFINITE = 6;
+// [7] int8 statistics pass selected, [8] largest level count over the tiles
+constexpr int I8S_MODE2 = 7, I8S_MAXLEV = 8;
+// The statistics pass keeps a K-tile's digit levels in registers: at most
+// S8_LV levels of S8_NC chunks; rows of packed digits are handed from the
+// normaliser pass through the workspace with this stride (bytes), and the
+// statistics pass runs for padded dimensions up to S8_MAX_DP (LDS).
+constexpr int S8_NC = 5, S8_LV = 9;
+constexpr int S8_FLG = S8_NC * 64 + 16;
+constexpr int S8_MAX_DP = 112;
 
 // Workspace layout and launch geometry for one (d, k).
 struct Plan {
@@ -45,12 +75,27 @@ struct Plan {
     int kgroups = 0;           // K-groups of the statistics pass (blocks per row group)
     bool wide = false;         // dp > MAX_DP: the D-sliced wide kernels
     int64_t chunk = 0;         // rows per chunk (CHUNK_ROWS or WIDE_CHUNK_ROWS)
+    // int8-slice E-step (narrow path only)
+    unsigned long long* i8_amax = nullptr;  // [MAX_DP] largest |x - s| per dim (fp64 bits)
+    int* i8_lsb = nullptr;     // [MAX_DP] lowest set bit exponent of x - s per dim
+    int* i8_plan = nullptr;    // [I8P_SIZE] digit counts and scale exponents
+    double* i8_dbl = nullptr;  // [1] sum of the largest scaled features
+    int8_t* i8_coef = nullptr; // [ntiles][I8_MAX_LEV][chunks][1024] level digit pieces
+    int* i8_ek = nullptr;      // [kp] per-component scale exponent
+    int* i8_tinfo = nullptr;   // [ntiles][I8_TINFO] levels per tile
+    int8_t* i8_rows = nullptr; // [CHUNK_ROWS][S8_FLG] packed digit rows of the current chunk
+    int i8_nc = 0;             // chunks per packed row the pass-1 kernel is built for
+    bool i8_stats = false;     // the int8 statistics pass exists for this dp
     double2* wlpart = nullptr; // wide: [chunk][ntiles] per-(row, K-tile) (max, sum)
     double* wtval = nullptr;   // wide: [chunk][ntiles][WIDE_TM] top-m candidate values
     int32_t* wtidx = nullptr;  // wide: [chunk][ntiles][WIDE_TM] candidate components
 };
 
-bool make_plan(int d, int k, void* ws, Plan* pl);
+// Workspace layout for (d, k). chunk_rows: rows per launch of the narrow
+// passes (sizes the per-row scratch); max_groups: cap on the statistics
+// pass's row groups (sizes the partials).
+bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows = CHUNK_ROWS,
+               int max_groups = 512);
 
 hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
                            hipStream_t st);
@@ -58,11 +103,25 @@ hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, cons
 // components (idx, resp, row-major n x m) of each row.
 // km (k-means mode, with m = 1): the row value summed into the partials is
 // the best log-density instead of the normaliser.
+// skip (device, may be null): the kernel does nothing when *skip == 1 (the
+// int8-slice pass runs instead).
 hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                       double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                      hipStream_t st, int km = 0);
+                      hipStream_t st, int km = 0, const int* skip = nullptr);
+// int8-slice E-step: data pass, digit plan and coefficient digits, then the
+// mode flag (status[I8S_MODE]) that selects the int8 or the fp64 pass 1.
+hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
+                              const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st);
+hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                       double* lse_out, int ll_acc, hipStream_t st);
+// int8-slice statistics pass (runs when status[I8S_MODE2] == 1; the fp64
+// statistics kernel is then told to skip through the same flag)
+hipError_t launch_stats8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                         const double* lse, int acc, hipStream_t st);
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                        const double* lse, int acc, hipStream_t st);
+                        const double* lse, int acc, hipStream_t st, const int* skip = nullptr);
+int i8_nc_for(int d);
+bool i8_stats_for(int dp);
 hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floor, float* w,
                            float* mu, float* var, hipStream_t st);
 // Wide path (pl.wide): normaliser partials + merge (writes lse_out, the

@@ -65,7 +65,7 @@ namespace gmm {
 // Prologue: parameter checks, shift, coefficient rows and constants.
 // ---------------------------------------------------------------------------
 __global__ void k_status_reset(int* status) {
-    if (threadIdx.x < 4) status[threadIdx.x] = 0;
+    if (threadIdx.x < 16) status[threadIdx.x] = 0;
 }
 
 // (w and var null: k-means mode, centroids only; every weight counts as 1)
@@ -187,7 +187,9 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
            const double* __restrict__ Pg, const double* __restrict__ cvec,
            const double* __restrict__ shift, int ntiles, double* __restrict__ lse_out,
            double* __restrict__ llpart, int ll_accumulate, int k, int m_out,
-           int32_t* __restrict__ idx_out, float* __restrict__ resp_out, int km) {
+           int32_t* __restrict__ idx_out, float* __restrict__ resp_out, int km,
+           const int* __restrict__ skip) {
+    if (skip && *skip == 1) return;  // the int8-slice pass runs instead
     constexpr int DPH = DP / 2;
     constexpr int PSTR = 2 * DP + 2;  // LDS stride of one component (doubles)
     constexpr int TMA = TM > 0 ? TM : 1;
@@ -455,7 +457,6 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 // indices are clamped instead of branched on so that the staging stays in
 // the E-step's basic block; values of rows outside the row group are zeroed.
 // ---------------------------------------------------------------------------
-constexpr int STATS_ROWS = 32;  // two 16-row MFMA blocks per staged tile
 
 template <int DP>
 struct StatsGeom {
@@ -481,7 +482,8 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
              const double* __restrict__ Pg, const double* __restrict__ cvec,
              const double* __restrict__ shift, int ntiles, const double* __restrict__ lse,
              int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
-             int accumulate) {
+             int accumulate, const int* __restrict__ skip) {
+    if (skip && *skip == 1) return;  // the int8-slice statistics pass runs instead
     using G = StatsGeom<DP>;
     constexpr int DPH = G::DPH, HS = G::HS, S = G::S, WV = G::WV, NT = G::NT, PER = G::PER;
     constexpr int NJ = DP / 16;  // 16-dim column blocks per power
@@ -915,35 +917,35 @@ __global__ void k_kmfinal(const double* __restrict__ part, const double* __restr
 template <int DP, typename XT, int TM>
 static hipError_t launch_lse_tm(const Plan& pl, const void* x, int64_t n, int64_t ldx,
                                 double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                                int km, hipStream_t st) {
+                                int km, hipStream_t st, const int* skip) {
     using G = LseGeom<DP>;
     const int64_t blocks = (n + G::ROWS - 1) / G::ROWS;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((k_lse<DP, XT, TM>), dim3((unsigned)blocks), dim3(G::NT), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse_out,
-                       pl.llpart, ll_acc, pl.k, m, idx, resp, km);
+                       pl.llpart, ll_acc, pl.k, m, idx, resp, km, skip);
     return hipGetLastError();
 }
 
 template <int DP, typename XT>
 static hipError_t launch_lse_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
                                double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                               int km, hipStream_t st) {
-    if (m <= 0) return launch_lse_tm<DP, XT, 0>(pl, x, n, ldx, lse_out, ll_acc, 0, idx, resp, 0, st);
-    if (m == 1) return launch_lse_tm<DP, XT, 1>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
-    if (m == 2) return launch_lse_tm<DP, XT, 2>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
-    return launch_lse_tm<DP, XT, 4>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st);
+                               int km, hipStream_t st, const int* skip) {
+    if (m <= 0) return launch_lse_tm<DP, XT, 0>(pl, x, n, ldx, lse_out, ll_acc, 0, idx, resp, 0, st, skip);
+    if (m == 1) return launch_lse_tm<DP, XT, 1>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st, skip);
+    if (m == 2) return launch_lse_tm<DP, XT, 2>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st, skip);
+    return launch_lse_tm<DP, XT, 4>(pl, x, n, ldx, lse_out, ll_acc, m, idx, resp, km, st, skip);
 }
 
 template <int DP, typename XT>
 static hipError_t launch_stats_t(const Plan& pl, const void* x, int64_t n, int64_t ldx,
-                                 const double* lse, int acc, hipStream_t st) {
+                                 const double* lse, int acc, hipStream_t st, const int* skip) {
     using G = StatsGeom<DP>;
     int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
     if (rpg < STATS_ROWS) rpg = STATS_ROWS;
     hipLaunchKernelGGL((k_stats<DP, XT>), dim3(pl.ngroups * (pl.ntiles / G::WV)), dim3(G::NT), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, lse, rpg,
-                       pl.part, pl.npart, acc);
+                       pl.part, pl.npart, acc, skip);
     return hipGetLastError();
 }
 
@@ -951,14 +953,14 @@ static hipError_t launch_stats_t(const Plan& pl, const void* x, int64_t n, int64
 
 hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                       double* lse_out, int ll_acc, int m, int32_t* idx, float* resp,
-                      hipStream_t st, int km) {
+                      hipStream_t st, int km, const int* skip) {
     switch (pl.dp) {
 #define CASE(DPV)                                                                          \
     case DPV:                                                                              \
         return dtype == 0 ? launch_lse_t<DPV, float>(pl, x, n, ldx, lse_out, ll_acc, m, idx, \
-                                                     resp, km, st)                          \
+                                                     resp, km, st, skip)                    \
                           : launch_lse_t<DPV, uint16_t>(pl, x, n, ldx, lse_out, ll_acc, m,   \
-                                                        idx, resp, km, st);
+                                                        idx, resp, km, st, skip);
         GMM_DP_CASES(CASE)
 #undef CASE
     }
@@ -990,12 +992,12 @@ hipError_t launch_km_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx
 }
 
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
-                        const double* lse, int acc, hipStream_t st) {
+                        const double* lse, int acc, hipStream_t st, const int* skip) {
     switch (pl.dp) {
-#define CASE(DPV)                                                                    \
-    case DPV:                                                                        \
-        return dtype == 0 ? launch_stats_t<DPV, float>(pl, x, n, ldx, lse, acc, st) \
-                          : launch_stats_t<DPV, uint16_t>(pl, x, n, ldx, lse, acc, st);
+#define CASE(DPV)                                                                          \
+    case DPV:                                                                              \
+        return dtype == 0 ? launch_stats_t<DPV, float>(pl, x, n, ldx, lse, acc, st, skip) \
+                          : launch_stats_t<DPV, uint16_t>(pl, x, n, ldx, lse, acc, st, skip);
         GMM_DP_CASES(CASE)
 #undef CASE
     }

@@ -35,6 +35,8 @@ lib.gmm_ivf_workspace_bytes.argtypes = [_i64, _i32, _i32]
 lib.gmm_ivf_workspace_bytes.restype = _sz
 lib.gmm_ivf_build.argtypes = [_vp, _vp, _i64, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.gmm_device_status.argtypes = [_vp, _vp]
+lib.gmm_estep_arithmetic.argtypes = [_vp, _vp]
+lib.gmm_estep_arithmetic.restype = ctypes.c_int
 lib.gmm_status_string.argtypes = [ctypes.c_int]
 lib.gmm_status_string.restype = ctypes.c_char_p
 lib.gmm_version.restype = _i32
@@ -230,6 +232,16 @@ def ivf_build(idx, resp, k: int, min_resp: float = 0.0, values: bool = True):
 def device_status(ws, device="cuda") -> int:
     """Synchronise and return the status of the last call that used ``ws``."""
     return int(lib.gmm_device_status(_ptr(ws), _stream(torch.device(device))))
+
+
+GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES, GMM_ESTEP_INT8_SLICES_BOTH = 0, 1, 2
+
+
+def estep_arithmetic(ws, device="cuda") -> int:
+    """Synchronise; the gmm_estep_kind of the last EM step / log-likelihood call
+    on ``ws``: GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES (normaliser pass on exact
+    int8 slices) or GMM_ESTEP_INT8_SLICES_BOTH (both passes)."""
+    return int(lib.gmm_estep_arithmetic(_ptr(ws), _stream(torch.device(device))))
 
 
 def profile_begin(max_launches: int = 4096) -> None:

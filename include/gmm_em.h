@@ -61,6 +61,13 @@ typedef enum {
 
 typedef enum { GMM_F32 = 0, GMM_BF16 = 1 } gmm_dtype;
 
+/* Arithmetic of the E-step contraction (see gmm_estep_arithmetic). */
+typedef enum {
+    GMM_ESTEP_FP64 = 0,             /* both passes' E-step in fp64 */
+    GMM_ESTEP_INT8_SLICES = 1,      /* normaliser pass on int8 slices, statistics pass fp64 */
+    GMM_ESTEP_INT8_SLICES_BOTH = 2  /* both passes' E-step on int8 slices */
+} gmm_estep_kind;
+
 /* Bytes of device workspace needed for data of dimension d and k components.
  * Independent of the number of rows. Returns 0 for unsupported shapes:
  * d <= 768 and k <= 2^22 are supported (d <= 128 uses register-tiled
@@ -81,6 +88,17 @@ size_t gmm_workspace_bytes(int32_t d, int32_t k);
  * r is never stored: it lives in registers between the two contractions.
  * Schedule: two passes over the rows (normalisers, then statistics); the
  * second recomputes the log-densities instead of storing them.
+ * Arithmetic: the E-step contraction sum_d (w b a - w a^2 / 2) (a = x - s,
+ * b = mu - s, w = 1/var, s a per-dimension shift) runs either in fp64 or
+ * exactly on int8 slices (the features and coefficients written as 7-bit
+ * digits with power-of-two scales; integer products and sums are exact and
+ * the digit levels are added in fp64), which differs from the fp64
+ * contraction by at most 2^-20 nats per log-density plus fp64 rounding. The
+ * call picks the int8 form on the device whenever its error bound holds for
+ * the data and parameters at hand (always, for integer-valued data within
+ * the supported range); gmm_estep_arithmetic reports which one ran. When
+ * both passes use it they compute bitwise identical log-densities. The M-step
+ * contraction is fp64 in every case.
  * Responsibilities keep the fp64 exponent range: a component whose
  * responsibilities are all below fp32's smallest value but above fp64's
  * still gets a nonzero N[k].
@@ -175,6 +193,12 @@ int gmm_kmeans_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_d
  * this workspace found invalid parameter values, GMM_OK otherwise, or
  * GMM_E_HIP if the synchronisation failed. */
 int gmm_device_status(const void* workspace, void* stream);
+
+/* Synchronises the stream and returns the gmm_estep_kind of the E-step of the
+ * last gmm_em_step / gmm_fit / gmm_loglik call that used this workspace
+ * (GMM_ESTEP_FP64 for the other entry points and for rows wider than 128),
+ * or -1 if the workspace is NULL or the synchronisation failed. */
+int gmm_estep_arithmetic(const void* workspace, void* stream);
 
 /* Static description of a status code. */
 const char* gmm_status_string(int status);

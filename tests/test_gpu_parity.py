@@ -40,7 +40,7 @@ def _gpu_step(ops, xt, w, mu, var, floor=1e-6, ws=None):
     return L.item()
 
 
-def _per_step(ops, x, w0, m0, v0, steps, floor=1e-6, tol=1e-4, ltol=1e-5, label=""):
+def _per_step(ops, x, w0, m0, v0, steps, floor=1e-6, tol=1e-4, ltol=1e-5, label="", path=None):
     xt, w, mu, var = _to_dev(x, w0, m0, v0)
     ws = ops.workspace(x.shape[1], len(w0), DEV)
     worst = {}
@@ -56,6 +56,12 @@ def _per_step(ops, x, w0, m0, v0, steps, floor=1e-6, tol=1e-4, ltol=1e-5, label=
         # while the oracle keeps them (asserted zero above)
         print(f"{label} step {t}: tiny components {e['n_tiny']}, killed {e['killed']}, "
               f"dead {e['n_dead']}")
+        if path is not None:
+            got = ops.estep_arithmetic(ws, DEV)
+            assert got in ((path,) if path == ops.GMM_ESTEP_FP64 else
+                           (ops.GMM_ESTEP_INT8_SLICES, ops.GMM_ESTEP_INT8_SLICES_BOTH)), \
+                f"{label} step {t}: E-step arithmetic {got}"
+            print(f"{label} step {t}: E-step arithmetic {got}")
     assert ops.device_status(ws, DEV) == ops.GMM_OK
     return worst
 
@@ -183,7 +189,8 @@ def test_descriptor_prefix_per_step(ops):
     W = dg.WORKLOADS["descriptor"]
     x = dg.rows(W, 200_000)
     w0, m0, v0 = dg.init_params(W, x)
-    worst = _per_step(ops, x, w0, m0, v0, 4, W.var_floor, label="descriptor prefix")
+    worst = _per_step(ops, x, w0, m0, v0, 4, W.var_floor, label="descriptor prefix",
+                      path=ops.GMM_ESTEP_INT8_SLICES)
     print("descriptor per-step worst", worst)
 
 
@@ -343,3 +350,89 @@ def test_bf16_large_prefix_per_step(ops):
         # bf16 data: the 5e-3 bar applies; the arithmetic itself is fp64
         e = assert_params_close(_host(w, mu, var), (rw, rmu, rv), nk, len(x), 5e-3, f"bf16_large step {t}")
         print(f"bf16_large prefix step {t}:", e)
+
+
+# ---------------------------------------------------------------------------
+# The E-step on exact int8 slices. Integer-valued data (features exact in a
+# few 7-bit digits) selects it; real-valued fp32 data whose truncation cannot
+# be bounded below 2^-20 nats keeps the fp64 E-step.
+# ---------------------------------------------------------------------------
+def _int_data(n, d, k, seed, scale=8.0, offset=40.0, hi=None):
+    x, _, _ = dg.custom(n, d, k, seed=seed)
+    x = np.clip(np.rint(x * scale + offset), 0, hi)
+    return x.astype(np.float32)
+
+
+def _seed_params(x, k, seed):
+    rng = np.random.default_rng(seed)
+    n, d = x.shape
+    w0 = np.full(k, 1.0 / k, np.float32)
+    m0 = x[rng.choice(n, k, replace=False)].copy()
+    v0 = np.ones((k, d), np.float32)
+    return w0, m0, v0
+
+
+def test_estep_arithmetic_selection(ops):
+    W = dg.WORKLOADS["descriptor"]
+    x = dg.rows(W, 20_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    xt, w, mu, var = _to_dev(x, w0, m0, v0)
+    ws = ops.workspace(W.d, W.k, DEV)
+    ops.em_step(xt, w, mu, var, W.var_floor, ws=ws)
+    assert ops.estep_arithmetic(ws, DEV) == ops.GMM_ESTEP_INT8_SLICES_BOTH
+    ops.loglik(xt, w, mu, var, ws=ws)
+    assert ops.estep_arithmetic(ws, DEV) in (ops.GMM_ESTEP_INT8_SLICES, ops.GMM_ESTEP_INT8_SLICES_BOTH)
+    T = dg.WORKLOADS["tiny"]
+    xr = dg.rows(T)
+    xt2, w2, mu2, var2 = _to_dev(xr, *dg.init_params(T, xr))
+    ws2 = ops.workspace(T.d, T.k, DEV)
+    ops.em_step(xt2, w2, mu2, var2, T.var_floor, ws=ws2)
+    assert ops.estep_arithmetic(ws2, DEV) == ops.GMM_ESTEP_FP64
+
+
+@pytest.mark.parametrize("n,d,k,seed", [(1007, 5, 3, 1), (3001, 20, 70, 2), (64 * 7 + 5, 33, 17, 4),
+                                         (5000, 128, 100, 5), (3000, 96, 1024, 6), (700, 1, 9, 7)])
+def test_int8_path_ragged_integer_data(ops, n, d, k, seed):
+    # values in [0, 120]: |a| <= 127, one digit for a and two for a^2 (at
+    # d = 128 a wider range needs more chunks than the int8 kernels hold,
+    # and the fp64 E-step runs instead)
+    x = _int_data(n, d, k, seed, hi=120.0)
+    w0, m0, v0 = _seed_params(x, k, seed)
+    worst = _per_step(ops, x, w0, m0, v0, 3, label=f"int8 n={n} d={d} k={k}",
+                      path=ops.GMM_ESTEP_INT8_SLICES)
+    print(f"int8 path n={n} d={d} k={k} per-step worst", worst)
+
+
+@pytest.mark.parametrize("hi,scale,step", [(1000.0, 60.0, 1.0), (120.0, 8.0, 0.5), (60.0, 4.0, 0.25)])
+def test_int8_path_multi_digit_features(ops, hi, scale, step):
+    # |a| beyond 127 needs two digits for a and three for a^2; values on a
+    # grid of 1/2 or 1/4 need one more low digit each: every case is still
+    # exact in at most three digits per column, so the int8 path runs
+    x, _, _ = dg.custom(3000, 32, 40, seed=8)
+    x = (np.clip(np.rint((x * scale + hi / 2) / step), 0, hi / step) * step).astype(np.float32)
+    w0, m0, v0 = _seed_params(x, 40, 8)
+    _per_step(ops, x, w0, m0, v0, 3, label=f"int8 range {hi} grid {step}",
+              path=ops.GMM_ESTEP_INT8_SLICES)
+
+
+def test_int8_path_rows_beyond_one_chunk(ops):
+    n = (1 << 22) + 1234
+    x = _int_data(n, 8, 4, 9)
+    w0, m0, v0 = _seed_params(x, 4, 9)
+    _per_step(ops, x, w0, m0, v0, 1, label="int8 two chunks", path=ops.GMM_ESTEP_INT8_SLICES)
+
+
+def test_int8_loglik_rows(ops):
+    W = dg.WORKLOADS["descriptor"]
+    x = dg.rows(W, 50_000)
+    w0, m0, v0 = dg.init_params(W, x)
+    rw, rmu, rv, *_ = oracle.em_step(x, w0, m0, v0, W.var_floor)
+    th = [a.astype(np.float32) for a in (rw, rmu, rv)]
+    xt, w, mu, var = _to_dev(x, *th)
+    ws = ops.workspace(W.d, W.k, DEV)
+    tot, rows = ops.loglik(xt, w, mu, var, per_row=True, ws=ws)
+    assert ops.estep_arithmetic(ws, DEV) in (ops.GMM_ESTEP_INT8_SLICES, ops.GMM_ESTEP_INT8_SLICES_BOTH)
+    rL, rrows = oracle.loglik(x, *th, per_row=True)
+    assert rel(tot.item(), rL) <= 1e-9
+    g = rows.cpu().numpy()
+    assert np.max(np.abs(g - rrows) / np.maximum(np.abs(rrows), 1.0)) <= 1e-6
