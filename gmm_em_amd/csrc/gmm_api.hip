@@ -227,6 +227,30 @@ static int em_step_planned(const Plan& pl, const void* x, int64_t n, int64_t ldx
     return hip_status(e);
 }
 
+// Device scratch of the allocation-free EM step: one copy per GPU, held for
+// the life of the process, shared by every gmm_em_step_noalloc call on that
+// GPU. Host code never passes this symbol to a kernel (on the host it is only
+// a stand-in): scratch_address() looks up the device address once per device,
+// with that device current, and every use goes through that address.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+static int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GMM_E_HIP;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return GMM_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GMM_E_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GMM_OK;
+}
+
 extern "C" {
 
 size_t gmm_workspace_bytes(int32_t d, int32_t k) {
@@ -242,6 +266,32 @@ int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtyp
                           workspace_bytes, &pl);
     if (rc) return rc;
     if (n < 1 || !(var_floor >= 0.0f) || !isfinite(var_floor)) return GMM_E_INVALID;
+    return em_step_planned(pl, x, n, ldx, x_dtype, weights, means, variances, var_floor, loglik_dev,
+                           (hipStream_t)stream);
+}
+
+int gmm_em_step_noalloc(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                        float* weights, float* means, float* variances, int32_t k, float var_floor,
+                        double* loglik_dev, void* stream) {
+    if (n < 0 || d < 1 || k < 1 || ldx < d) return GMM_E_INVALID;
+    if (ldx > MAX_LDX) return GMM_E_UNSUPPORTED;
+    if ((n > 0 && !x) || !weights || !means || !variances) return GMM_E_INVALID;
+    if (x_dtype != GMM_F32 && x_dtype != GMM_BF16) return GMM_E_DTYPE;
+    if (n < 1 || !(var_floor >= 0.0f) || !isfinite(var_floor)) return GMM_E_INVALID;
+    // the plan with the scratch's row chunk, and as many statistics row
+    // groups as fit the scratch
+    Plan pl;
+    int groups = 512;
+    for (;;) {
+        if (!make_plan(d, k, nullptr, &pl, NOALLOC_CHUNK_ROWS, groups)) return GMM_E_UNSUPPORTED;
+        if (pl.bytes <= NOALLOC_SCRATCH_BYTES) break;
+        if (groups == 1) return GMM_E_UNSUPPORTED;  // (d, k) too large for the scratch
+        groups = groups / 2 > 1 ? groups / 2 : 1;
+    }
+    void* scr = nullptr;
+    const int rc = scratch_address(&scr);
+    if (rc) return rc;
+    make_plan(d, k, scr, &pl, NOALLOC_CHUNK_ROWS, groups);
     return em_step_planned(pl, x, n, ldx, x_dtype, weights, means, variances, var_floor, loglik_dev,
                            (hipStream_t)stream);
 }

@@ -19,6 +19,10 @@ constexpr int WIDE_TM = 4;
 // Rows per chunk: bounds the per-row normaliser scratch (lse) so that the
 // workspace size does not depend on the number of rows.
 constexpr int64_t CHUNK_ROWS = (int64_t)1 << 22;
+// Allocation-free EM step: bytes of its per-device scratch and the row chunk
+// its plan uses.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)128 << 20;
+constexpr int64_t NOALLOC_CHUNK_ROWS = (int64_t)1 << 18;
 // Largest leading dimension (elements): 32 rows of fp32 values must span
 // fewer than 2^31 bytes (the statistics pass's per-tile buffer offsets).
 constexpr int64_t MAX_LDX = ((int64_t)1 << 24) - 1;

@@ -108,6 +108,23 @@ int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtyp
                 float* weights, float* means, float* variances, int32_t k, float var_floor,
                 double* loglik_dev, void* workspace, size_t workspace_bytes, void* stream);
 
+/* gmm_em_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same EM step with the same arguments and results, but no workspace
+ * argument. It uses a device array of 128 MiB that the library holds in its
+ * code object (one copy per GPU, kept until the process ends); the call
+ * itself allocates nothing. The array is shared by every call on a GPU:
+ * calls that overlap in time on one GPU (several streams or host threads)
+ * race and give undefined results. It holds no state that a call depends on
+ * (each call rewrites what it reads). Shapes whose workspace does not fit
+ * 128 MiB (with its 262,144-row chunks and the statistics pass's row groups
+ * reduced to fit) return GMM_E_UNSUPPORTED: d = 96 with k = 1024 fits, d = 768
+ * with k = 16384 does not. The reduction order differs from gmm_em_step's,
+ * so results agree to rounding, not bitwise. */
+int gmm_em_step_noalloc(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
+                        float* weights, float* means, float* variances, int32_t k,
+                        float var_floor, double* loglik_dev, void* stream);
+
 /* max_iter EM iterations (gmm_em_step repeated). loglik_hist_dev (device,
  * max_iter doubles, may be NULL) receives L(theta_t) for t = 0, 1, ...
  * When tol > 0 the host reads each L after its step (one synchronisation per
