@@ -449,6 +449,7 @@ int gmm_estep_arithmetic(const void* workspace, void* stream) {
     int st2[16] = {0};
     if (hipMemcpy(st2, workspace, sizeof(st2), hipMemcpyDeviceToHost) != hipSuccess) return -1;
     if (st2[I8S_MODE] != 1) return GMM_ESTEP_FP64;
+    if (st2[I8S_MODE2] == 2) return GMM_ESTEP_INT8_SLICES_MSTEP;
     return st2[I8S_MODE2] == 1 ? GMM_ESTEP_INT8_SLICES_BOTH : GMM_ESTEP_INT8_SLICES;
 }
 

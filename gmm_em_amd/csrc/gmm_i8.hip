@@ -50,25 +50,30 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 }
 
 // Layout of the packed feature row (bytes): digit blocks i = 1 .. max(Ia, Ib),
-// each [a^2 digit i (d bytes) if i <= Ib][a digit i (d bytes) if i <= Ia],
-// zero padding up to a multiple of 64 (one MFMA chunk).
+// each [a^2 digit i (dq bytes) if i <= Ib][a digit i (dq bytes) if i <= Ia]
+// with dq = d rounded up to 16 (dims d .. dq-1 hold 0, so every block starts
+// on a 16-byte MFMA column tile), zero padding up to a multiple of 64 (one
+// MFMA chunk).
 struct I8Layout {
     int ia, ib, fl0, nc;  // digit counts, used bytes, 64-byte chunks
     int off_b[I8_MAX_DIGITS + 1], off_a[I8_MAX_DIGITS + 1];  // block offsets, -1 if absent
 };
 
+__device__ __forceinline__ int i8_dq(int d) { return (d + 15) / 16 * 16; }
+
 __device__ __forceinline__ I8Layout i8_layout(const int* plan, int d) {
     I8Layout L;
     L.ia = plan[I8P_IA];
     L.ib = plan[I8P_IB];
+    const int dq = i8_dq(d);
     int off = 0;
     const int im = L.ia > L.ib ? L.ia : L.ib;
     for (int i = 1; i <= I8_MAX_DIGITS; ++i) {
         L.off_b[i] = -1;
         L.off_a[i] = -1;
         if (i <= im) {
-            if (i <= L.ib) { L.off_b[i] = off; off += d; }
-            if (i <= L.ia) { L.off_a[i] = off; off += d; }
+            if (i <= L.ib) { L.off_b[i] = off; off += dq; }
+            if (i <= L.ia) { L.off_a[i] = off; off += dq; }
         }
     }
     L.fl0 = off;
@@ -204,7 +209,7 @@ __global__ void k_i8_plan(const unsigned long long* __restrict__ amax, const int
         plan[I8P_IA] = ma;
         plan[I8P_IB] = mb;
         dbl[0] = tot;
-        const int fl0 = d * (ma + mb);
+        const int fl0 = i8_dq(d) * (ma + mb);
         if ((fl0 + 63) / 64 > I8_MAX_NC) atomicOr(&status[I8S_FAIL], 1);
     }
 }
@@ -319,14 +324,17 @@ __global__ __launch_bounds__(256) void k_i8_coef(const float* __restrict__ w, co
 
 // Mode: the int8 normaliser pass runs when no check failed and the data is
 // finite; the int8 statistics pass as well when a tile's digit levels fit
-// its registers (stats_ok: the kernel exists for this dimension).
+// its registers (stats_ok: the kernel exists for this dimension): with the
+// M-step on int8 slices too (mode 2) when every feature is exact in its
+// digits, else with the fp64 M-step (mode 1).
 __global__ void k_i8_mode(int* status, const int* plan, int d, int stats_ok) {
     if (threadIdx.x == 0) {
         const int m1 = (status[I8S_FAIL] == 0 && status[I8S_NONFINITE] == 0) ? 1 : 0;
         const I8Layout L = i8_layout(plan, d);
         status[I8S_MODE] = m1;
-        status[I8S_MODE2] =
-            (m1 && stats_ok && L.nc <= S8_NC && status[I8S_MAXLEV] <= S8_LV) ? 1 : 0;
+        int m2 = (m1 && stats_ok && L.nc <= S8_NC && status[I8S_MAXLEV] <= S8_LV) ? 1 : 0;
+        if (m2 && plan[I8P_TRUNC_A] == 0 && plan[I8P_TRUNC_B] == 0) m2 = 2;
+        status[I8S_MODE2] = m2;
     }
 }
 
@@ -375,7 +383,7 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
     const int64_t wrow = (int64_t)blockIdx.x * L8_ROWS + wave * (L8_RT * 16);
     const I8Layout LY = i8_layout(plan, d);
     const int dph = dp >> 1;
-    const bool hand_off = status[I8S_MODE2] == 1;
+    const bool hand_off = status[I8S_MODE2] != 0;
 
     // ---- pack the wave's rows: digits of a^2 and a, through LDS
     v4i A[L8_RT][NC];
@@ -763,6 +771,313 @@ void k_stats8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 }
 
 // ---------------------------------------------------------------------------
+// Pass 2 with the M-step on int8 slices as well (mode 2: every feature is
+// exact in its digits). The statistics [sum r, sum r a, sum r a^2] are the
+// contraction over rows of the responsibilities with the rows' features, and
+// the features' digits are already in the packed rows. Per 64-row block and
+// component, the responsibilities are put on a block exponent e (every r of
+// the block is below 2^e) and cut to r' = u 2^(e - 41), u an integer of at
+// most 42 bits written as six 7-bit digits: r' is r to fp32 precision for
+// every row within 2^-18 of the block's largest responsibility and below it
+// by less than 2^(e - 41) for the others (six digits rather than four: where
+// a component's main rows agree in a dimension, its variance there comes from
+// rows of small responsibility, which need their own relative precision).
+// Sums of digit products are exact in int32, so the kernel
+// computes the statistics of the weights r' exactly (up to the fp64 rounding
+// of the block sums), and the mass sum r' is taken from the same integers:
+// mean and variance are those of one consistent set of weights, so the
+// variance's cancellation (E[a^2] - mean^2) does not magnify the rounding.
+//
+// Block = 4 waves, wave w owns K-tile kg*4 + w as in the other statistics
+// passes; the block walks its row group in 64-row blocks. Per block:
+//  * the packed digit rows arrive by buffer-to-LDS copies (one block ahead);
+//  * they are transposed in LDS to column order, position p = 16h + 4s + q
+//    of a column holding row 16s + 4h + q: that is the order in which the
+//    E-step's int8 result leaves the rows in lane (h, i) (rows 4h + q of
+//    16-row tile s), so the responsibilities become MFMA operands without
+//    leaving the lane;
+//  * the E-step as in the pass above (same fold, same bits), then the
+//    digits of r', and the M-step: A = feature digit columns (16 dims),
+//    B = responsibility digits (16 components), one int32 accumulator per
+//    level (feature digit i + responsibility digit j), levels folded in
+//    pairs into fp64 with the block's scale 2^(e - 20 - 7 level).
+// The feature scale 2^G of each dimension multiplies the sums once at the end.
+// ---------------------------------------------------------------------------
+constexpr int X8_ROWS = 64;  // rows per block: the int8 MFMA's contraction length
+constexpr int X8_FTS = 80;   // LDS stride of a transposed column (64 rows + 16: conflict-free)
+constexpr int X8_RD = 6;     // responsibility digits
+
+template <int DP, int IM>
+__global__ __launch_bounds__(256, 1)
+void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
+               const int8_t* __restrict__ coef8, const int* __restrict__ ek,
+               const int* __restrict__ tinfo, const double* __restrict__ cvec,
+               const int* __restrict__ plan, int ntiles, const double* __restrict__ lse,
+               int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
+               int accumulate, const int* __restrict__ status) {
+    constexpr int WV = 4, NT = 256;
+    constexpr int NJ = DP / 16;
+    constexpr int NLV = IM + X8_RD - 1;           // M-step levels 2 .. IM + X8_RD
+    constexpr int FTB = 2 * IM * DP * X8_FTS;     // transposed columns of one block
+    constexpr int DGB = X8_ROWS * S8_FLG;         // packed digit rows of one block
+    constexpr int DGP = (DGB + 1023) / 1024;      // 1 KB copy pieces
+    constexpr double LOG2E = 1.4426950408889634074;
+    __shared__ __attribute__((aligned(16))) int8_t dg[2][DGP * 1024];
+    __shared__ __attribute__((aligned(16))) int8_t ft[FTB];
+    __shared__ double ls[2][X8_ROWS];
+    if (status[I8S_MODE2] != 2) return;  // another statistics pass runs instead
+    const int ia = plan[I8P_IA], ib = plan[I8P_IB];
+    if ((ia > ib ? ia : ib) != IM) return;  // the variant for this digit count runs
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = lane & 15, h = lane >> 4;
+    const int kgroups = ntiles / WV;
+    const int nb = gridDim.x;
+    const int o = (nb % 8 == 0) ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int g = o / kgroups;
+    const int tile = (o % kgroups) * WV + wave;
+    const int slot = tile * 16 + ci;
+    const int nl = tinfo[tile * I8_TINFO];
+    const int dq = i8_dq(d);
+
+    // the K-tile's E-step digit levels (B operands), resident for the pass
+    v4i qd[S8_LV][S8_NC];
+    {
+        const int nc = i8_layout(plan, d).nc;
+        const int8_t* cp = coef8 + (int64_t)tile * (I8_MAX_LEV * I8_MAX_NC * 1024) + lane * 16;
+#pragma unroll
+        for (int lev = 0; lev < S8_LV; ++lev)
+#pragma unroll
+            for (int c = 0; c < S8_NC; ++c)
+                qd[lev][c] = (lev < nl && c < nc) ? *(const v4i*)(cp + (lev * nc + c) * 1024)
+                                                  : v4i{0, 0, 0, 0};
+    }
+    const double scale = ldexp(1.0, ek[slot] - 14);
+    const double cc = cvec[slot];
+
+    double acc[2][NJ][4];  // [a^2, a][dim tile][dim 16 j + 4 h + q], component ci
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[k2][j][q] = 0.0;
+    double n64 = 0.0;
+
+    const int64_t gr0 = (int64_t)g * rows_per_group;
+    int64_t gr1 = gr0 + rows_per_group;
+    if (gr1 > n) gr1 = n;
+    const int64_t nblk = gr1 > gr0 ? (gr1 - gr0 + X8_ROWS - 1) / X8_ROWS : 0;
+
+    // column blocks of an absent digit (i above that kind's count) stay zero
+    for (int e = tid; e < FTB / 16; e += NT) {
+        const int sl = (e * 16) / (DP * X8_FTS);
+        const int kind = sl / IM, i = sl % IM + 1;
+        if (i > (kind == 0 ? ib : ia)) ((v4i*)ft)[e] = v4i{0, 0, 0, 0};
+    }
+
+    auto rows_in = [&](int64_t it) -> int {
+        const int64_t nv = gr1 - (gr0 + it * X8_ROWS);
+        return nv < 0 ? 0 : (nv > X8_ROWS ? X8_ROWS : (int)nv);
+    };
+    // packed digit rows of block it (rows past the group read as 0)
+    auto issue_dg = [&](int64_t it, int buf) {
+        const int64_t rbase = gr0 + it * X8_ROWS;
+        const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(drows + rbase * S8_FLG), (short)0, rows_in(it) * S8_FLG, BUF_RSRC_WORD3);
+        for (int p = wave; p < DGP; p += WV)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                dr, (__attribute__((address_space(3))) void*)(dg[buf] + p * 1024), 16, lane * 16,
+                p * 1024, 0, 0);
+    };
+    // normaliser of row tid of block it (+inf past the group: r = 0)
+    auto load_ls = [&](int64_t it) -> double {
+        const int nv = rows_in(it);
+        return tid < nv ? lse[gr0 + it * X8_ROWS + tid] : INFINITY;
+    };
+
+    if (nblk > 0) {
+        issue_dg(0, 0);
+        if (tid < X8_ROWS) ls[0][tid] = load_ls(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // the present column blocks, in packed-row order of their offsets:
+    // a^2 digit i at dq (min(i-1, ib) + min(i-1, ia)), a digit i after it
+    const int nps = ia + ib;
+    for (int64_t it = 0; it < nblk; ++it) {
+        const int buf = (int)(it & 1);
+        double lsn = INFINITY;
+        if (it + 1 < nblk) {
+            issue_dg(it + 1, buf ^ 1);
+            if (tid < X8_ROWS) lsn = load_ls(it + 1);
+        }
+        const int8_t* db = dg[buf];
+
+        // ---- transpose the block's feature digits into column order
+        for (int task = tid; task < nps * DP * 4; task += NT) {
+            const int s = task & 3, hh = (task >> 2) & 3;
+            const int rem = task >> 4;
+            const int dd4 = rem % (DP / 4), sidx = rem / (DP / 4);
+            const int kind = sidx < ib ? 0 : 1;
+            const int i = kind == 0 ? sidx + 1 : sidx - ib + 1;
+            const int im1 = i - 1;
+            const int off = dq * ((im1 < ib ? im1 : ib) + (im1 < ia ? im1 : ia) + (kind == 1 && i <= ib ? 1 : 0));
+            const int8_t* src = db + (16 * s + 4 * hh) * S8_FLG + off + 4 * dd4;
+            const uint32_t w0 = *(const uint32_t*)(src);
+            const uint32_t w1 = *(const uint32_t*)(src + S8_FLG);
+            const uint32_t w2 = *(const uint32_t*)(src + 2 * S8_FLG);
+            const uint32_t w3 = *(const uint32_t*)(src + 3 * S8_FLG);
+            int8_t* dst = ft + ((kind * IM + im1) * DP + 4 * dd4) * X8_FTS + 16 * hh + 4 * s;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t v = ((w0 >> (8 * c)) & 0xffu) | (((w1 >> (8 * c)) & 0xffu) << 8) |
+                                   (((w2 >> (8 * c)) & 0xffu) << 16) | (((w3 >> (8 * c)) & 0xffu) << 24);
+                *(uint32_t*)(dst + c * X8_FTS) = v;
+            }
+        }
+
+        // ---- E-step: four 16-row tiles, the normaliser pass's fold
+        double l[4][4];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            v4i A[2][S8_NC];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int c = 0; c < S8_NC; ++c)
+                    A[rb][c] = *(const v4i*)(db + (16 * (2 * hf + rb) + ci) * S8_FLG + 64 * c + 16 * h);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) l[2 * hf + rb][q] = 0.0;
+            double sc = scale * (1.0 / 128.0);
+#pragma unroll
+            for (int lev = 0; lev < S8_LV; lev += 2) {
+                if (lev < nl) {
+                    v4i a0[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+                    v4i a1[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+#pragma unroll
+                    for (int c = 0; c < S8_NC; ++c) {
+#pragma unroll
+                        for (int rb = 0; rb < 2; ++rb) a0[rb] = mfma_i8(A[rb][c], qd[lev][c], a0[rb]);
+                        if (lev + 1 < S8_LV) {
+#pragma unroll
+                            for (int rb = 0; rb < 2; ++rb)
+                                a1[rb] = mfma_i8(A[rb][c], qd[lev + 1 < S8_LV ? lev + 1 : lev][c], a1[rb]);
+                        }
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            fold_pair(l[2 * hf + rb][q], a0[rb][q], a1[rb][q], sc);
+                    sc *= 1.0 / 16384.0;
+                }
+            }
+        }
+        __syncthreads();  // the transposed columns are complete
+
+        // ---- responsibilities on the block exponent, as four 7-bit digits
+        double t[4][4];
+        double tm = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                t[s][q] = l[s][q] + cc - ls[buf][16 * s + 4 * h + q];
+                tm = fmax(tm, t[s][q]);
+            }
+        tm = fmax(tm, shfl_xor_d(tm, 16));
+        tm = fmax(tm, shfl_xor_d(tm, 32));
+        const double z = tm * LOG2E;
+        const int e = z > -1000.0 ? (int)floor(z) + 1 : -1000;  // every r of the block < 2^e
+        const double yb = (double)(6 - e);
+        const double snh = ldexp(1.0, e - 20), snl = ldexp(1.0, e - 41);
+        v4i R[X8_RD];
+        bool any = false;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint32_t uh[4], ul[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double y = fmax(fma(t[s][q], LOG2E, yb), -64.0);  // log2(r 2^(6 - e)) < 6
+                const float v = __builtin_amdgcn_exp2f((float)y);
+                // v = hi 2^-14 + lo 2^-35 (+ less than 2^-35): hi < 2^20 + 1, lo < 2^21
+                const float hf = floorf(v * 16384.0f);
+                const float vl = fmaf(hf, -1.0f / 16384.0f, v);  // exact
+                uh[q] = (uint32_t)hf;
+                ul[q] = (uint32_t)(vl * 34359738368.0f);
+                n64 = fma((double)(int)uh[q], snh, fma((double)(int)ul[q], snl, n64));
+                any |= (uh[q] | ul[q]) != 0u;
+            }
+#pragma unroll
+            for (int jr = 0; jr < X8_RD; ++jr) {
+                const uint32_t* u = jr < 3 ? uh : ul;
+                const int sh = 7 * (2 - jr % 3);
+                R[jr][s] = (int)(((u[0] >> sh) & 127u) | (((u[1] >> sh) & 127u) << 8) |
+                                 (((u[2] >> sh) & 127u) << 16) | (((u[3] >> sh) & 127u) << 24));
+            }
+        }
+
+        // ---- M-step: feature digit columns x responsibility digits
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
+            const double sp0 = ldexp(1.0, e - 20);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int kind = 0; kind < 2; ++kind) {
+                    v4i B[IM];
+#pragma unroll
+                    for (int i = 0; i < IM; ++i)
+                        B[i] = *(const v4i*)(ft + ((kind * IM + i) * DP + 16 * j + ci) * X8_FTS + 16 * h);
+                    v4i S[NLV];
+#pragma unroll
+                    for (int lv = 0; lv < NLV; ++lv) S[lv] = v4i{0, 0, 0, 0};
+#pragma unroll
+                    for (int i = 0; i < IM; ++i)
+#pragma unroll
+                        for (int jr = 0; jr < X8_RD; ++jr) S[i + jr] = mfma_i8(B[i], R[jr], S[i + jr]);
+                    double sp = sp0;
+#pragma unroll
+                    for (int lv = 0; lv < NLV; lv += 2) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            fold_pair(acc[kind][j][q], S[lv][q], lv + 1 < NLV ? S[lv + 1][q] : 0, sp);
+                        sp *= 1.0 / 16384.0;
+                    }
+                }
+        }
+        if (it + 1 < nblk && tid < X8_ROWS) ls[buf ^ 1][tid] = lsn;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's digit copies of the next block have landed
+        __syncthreads();
+    }
+
+    // responsibility mass: lanes ci, ci+16, ci+32, ci+48 hold disjoint rows
+    n64 += shfl_xor_d(n64, 16);
+    n64 += shfl_xor_d(n64, 32);
+    const int64_t gbase = (int64_t)g * ntiles * 16;
+    if (h == 0) {
+        double* np = npart + gbase + slot;
+        *np = (accumulate ? *np : 0.0) + n64;
+    }
+    double* pc = part + (gbase + slot) * (2 * DP);
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int dd = 16 * j + 4 * h + q;
+                const int gexp = dd < d ? plan[(kind == 0 ? I8P_GB : I8P_GA) + dd] : 0;
+                double* p2 = pc + (kind == 0 ? DP : 0) + dd;
+                *p2 = (accumulate ? *p2 : 0.0) + ldexp(acc[kind][j][q], gexp);
+            }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers.
 // ---------------------------------------------------------------------------
 hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
@@ -803,8 +1118,9 @@ static hipError_t launch_lse8_t(const Plan& pl, const void* x, int64_t n, int64_
 // at this dimension (unused chunks of a row hold zeros and are skipped by the
 // per-level chunk ranges).
 int i8_nc_for(int d) {
-    // digits: up to 3 for a and 3 for a^2, but at most I8_MAX_NC chunks
-    const int nc = (d * 2 * I8_MAX_DIGITS + 63) / 64;
+    // digits: up to 3 for a and 3 for a^2 (blocks of d rounded up to 16),
+    // but at most I8_MAX_NC chunks
+    const int nc = ((d + 15) / 16 * 16 * 2 * I8_MAX_DIGITS + 63) / 64;
     return nc > I8_MAX_NC ? I8_MAX_NC : (nc < 2 ? 2 : nc);
 }
 
@@ -833,19 +1149,42 @@ static hipError_t launch_stats8_t(const Plan& pl, const void* x, int64_t n, int6
     return hipGetLastError();
 }
 
+// The three digit-count variants of the int8 M-step pass (each returns at
+// once unless the mode flag and the plan's digit count select it).
+template <int DP>
+static hipError_t launch_stats8x_t(const Plan& pl, int64_t n, const double* lse, int acc,
+                                   hipStream_t st) {
+    int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + X8_ROWS - 1) / X8_ROWS * X8_ROWS;
+    if (rpg < X8_ROWS) rpg = X8_ROWS;
+    const dim3 grid(pl.ngroups * (pl.ntiles / 4)), block(256);
+    hipLaunchKernelGGL((k_stats8x<DP, 1>), grid, block, 0, st, pl.i8_rows, n, pl.d, pl.i8_coef,
+                       pl.i8_ek, pl.i8_tinfo, pl.cvec, pl.i8_plan, pl.ntiles, lse, rpg, pl.part,
+                       pl.npart, acc, pl.status);
+    hipLaunchKernelGGL((k_stats8x<DP, 2>), grid, block, 0, st, pl.i8_rows, n, pl.d, pl.i8_coef,
+                       pl.i8_ek, pl.i8_tinfo, pl.cvec, pl.i8_plan, pl.ntiles, lse, rpg, pl.part,
+                       pl.npart, acc, pl.status);
+    hipLaunchKernelGGL((k_stats8x<DP, 3>), grid, block, 0, st, pl.i8_rows, n, pl.d, pl.i8_coef,
+                       pl.i8_ek, pl.i8_tinfo, pl.cvec, pl.i8_plan, pl.ntiles, lse, rpg, pl.part,
+                       pl.npart, acc, pl.status);
+    return hipGetLastError();
+}
+
 bool i8_stats_for(int dp) { return dp <= S8_MAX_DP; }
 
 hipError_t launch_stats8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                          const double* lse, int acc, hipStream_t st) {
+    hipError_t e = hipErrorInvalidValue;
     switch (pl.dp) {
 #define CASE(DPV)                                                                          \
     case DPV:                                                                              \
-        return dtype == 0 ? launch_stats8_t<DPV, float>(pl, x, n, ldx, lse, acc, st)      \
-                          : launch_stats8_t<DPV, uint16_t>(pl, x, n, ldx, lse, acc, st);
+        e = dtype == 0 ? launch_stats8_t<DPV, float>(pl, x, n, ldx, lse, acc, st)         \
+                       : launch_stats8_t<DPV, uint16_t>(pl, x, n, ldx, lse, acc, st);     \
+        if (e == hipSuccess) e = launch_stats8x_t<DPV>(pl, n, lse, acc, st);              \
+        break;
         CASE(16) CASE(32) CASE(48) CASE(64) CASE(80) CASE(96) CASE(112)
 #undef CASE
     }
-    return hipErrorInvalidValue;
+    return e;
 }
 
 }  // namespace gmm

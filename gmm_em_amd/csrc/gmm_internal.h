@@ -118,8 +118,9 @@ hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, c
                               const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st);
 hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                        double* lse_out, int ll_acc, hipStream_t st);
-// int8-slice statistics pass (runs when status[I8S_MODE2] == 1; the fp64
-// statistics kernel is then told to skip through the same flag)
+// int8-slice statistics passes (status[I8S_MODE2] == 1: int8 E-step with the
+// fp64 M-step; == 2: the M-step on int8 slices too; the fp64 statistics
+// kernel is told to skip through the same flag when it is nonzero)
 hipError_t launch_stats8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                          const double* lse, int acc, hipStream_t st);
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,

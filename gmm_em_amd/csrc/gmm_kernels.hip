@@ -189,7 +189,7 @@ void k_lse(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
            double* __restrict__ llpart, int ll_accumulate, int k, int m_out,
            int32_t* __restrict__ idx_out, float* __restrict__ resp_out, int km,
            const int* __restrict__ skip) {
-    if (skip && *skip == 1) return;  // the int8-slice pass runs instead
+    if (skip && *skip != 0) return;  // the int8-slice pass runs instead
     constexpr int DPH = DP / 2;
     constexpr int PSTR = 2 * DP + 2;  // LDS stride of one component (doubles)
     constexpr int TMA = TM > 0 ? TM : 1;
@@ -483,7 +483,7 @@ void k_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
              const double* __restrict__ shift, int ntiles, const double* __restrict__ lse,
              int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
              int accumulate, const int* __restrict__ skip) {
-    if (skip && *skip == 1) return;  // the int8-slice statistics pass runs instead
+    if (skip && *skip != 0) return;  // the int8-slice statistics pass runs instead
     using G = StatsGeom<DP>;
     constexpr int DPH = G::DPH, HS = G::HS, S = G::S, WV = G::WV, NT = G::NT, PER = G::PER;
     constexpr int NJ = DP / 16;  // 16-dim column blocks per power

@@ -61,11 +61,12 @@ typedef enum {
 
 typedef enum { GMM_F32 = 0, GMM_BF16 = 1 } gmm_dtype;
 
-/* Arithmetic of the E-step contraction (see gmm_estep_arithmetic). */
+/* Arithmetic of the E-step and M-step contractions (see gmm_estep_arithmetic). */
 typedef enum {
-    GMM_ESTEP_FP64 = 0,             /* both passes' E-step in fp64 */
-    GMM_ESTEP_INT8_SLICES = 1,      /* normaliser pass on int8 slices, statistics pass fp64 */
-    GMM_ESTEP_INT8_SLICES_BOTH = 2  /* both passes' E-step on int8 slices */
+    GMM_ESTEP_FP64 = 0,              /* both passes' E-step in fp64 */
+    GMM_ESTEP_INT8_SLICES = 1,       /* normaliser pass on int8 slices, statistics pass fp64 */
+    GMM_ESTEP_INT8_SLICES_BOTH = 2,  /* both passes' E-step on int8 slices, M-step fp64 */
+    GMM_ESTEP_INT8_SLICES_MSTEP = 3  /* as 2, and the M-step on int8 slices too */
 } gmm_estep_kind;
 
 /* Bytes of device workspace needed for data of dimension d and k components.
@@ -98,7 +99,12 @@ size_t gmm_workspace_bytes(int32_t d, int32_t k);
  * the data and parameters at hand (always, for integer-valued data within
  * the supported range); gmm_estep_arithmetic reports which one ran. When
  * both passes use it they compute bitwise identical log-densities. The M-step
- * contraction is fp64 in every case.
+ * contraction is fp64, except where every feature is exact in its digits
+ * (integer-valued data, or data on a grid of 2^-m, within the range): then
+ * it runs on int8 slices as well, on responsibilities cut per 64-row block
+ * and component to 42 bits below the block's largest one (fp32 precision
+ * for every row within 2^-18 of it); N[k], S1[k] and S2[k] are then exact for
+ * those weights up to fp64 rounding, so the variance keeps full accuracy.
  * Responsibilities keep the fp64 exponent range: a component whose
  * responsibilities are all below fp32's smallest value but above fp64's
  * still gets a nonzero N[k].
