@@ -23,6 +23,10 @@ FLAGS = [
     "-shared",
     # packed fp32 VALU ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: long-lived MFMA operands (the statistics passes'
+    # resident coefficient digits) go to the accumulator registers instead,
+    # so the VALU reads the products without v_accvgpr_read copies
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -302,11 +302,13 @@ __global__ __launch_bounds__(256) void k_i8_coef(const float* __restrict__ w, co
         atomicMax(&status[I8S_MAXLEV], nlev);
     }
     // level vectors in B-operand order, every chunk of the packed row (zero
-    // where the level pairs no digits): piece (lev * nc + chunk) holds, at
-    // [lane 16h + c][16 bytes], positions 64 chunk + 16h .. +15 of component c
+    // where the level pairs no digits, and for every level past the tile's
+    // count, so that kernels may contract a fixed number of levels): piece
+    // (lev * nc + chunk) holds, at [lane 16h + c][16 bytes], positions
+    // 64 chunk + 16h .. +15 of component c
     const int nc = L.nc;
     int8_t* dst = coef8 + (int64_t)tile * I8_MAX_LEV * I8_MAX_NC * 1024;
-    for (int lev = 0; lev < nlev; ++lev) {
+    for (int lev = 0; lev < I8_MAX_LEV; ++lev) {
         const int Lv = lev + 2;
         for (int pos = sub; pos < nc * 64; pos += 16) {
             int v = 0;
@@ -352,16 +354,20 @@ __device__ __forceinline__ void fold_pair(double& l, int a, int b, double sc) {
 // Block = 8 waves, 64 rows per wave (four 16-row MFMA tiles), 512 rows. Each
 // wave packs the digit rows of its 64 rows once (through LDS) and keeps them
 // in registers as A operands; the K-tiles' level vectors stream through two
-// LDS buffers (tile t+1 is copied while tile t is contracted). Per tile and
-// level: the chunks holding nonzero digits, one int32 accumulator per row
-// tile, then l += acc * 2^(E_k - 7L) in fp64. The finished tile's values go
-// into the online logsumexp (fp64 running maximum, fp32 scaled sum).
+// LDS buffers (tile t+1 is copied while tile t is contracted). The kernel is
+// built for an exact chunk count NC and level count LV (the variants whose
+// NC or LV do not match the plan return at once), so a tile is one
+// branch-free block: per level, all NC chunks into one int32 accumulator
+// per row tile, levels folded in pairs (l += acc * 2^(E_k - 7L) in fp64)
+// while the next pair's products run; the finished tile's values go into the
+// online logsumexp (fp64 running maximum, fp32 scaled sum). A tile's levels
+// past its own count have zero digits.
 // ---------------------------------------------------------------------------
 constexpr int L8_WAVES = 8;
 constexpr int L8_RT = 4;  // 16-row tiles per wave
 constexpr int L8_ROWS = L8_WAVES * L8_RT * 16;
 
-template <int NC, typename XT>
+template <int NC, int LV, typename XT>
 __global__ __launch_bounds__(L8_WAVES * 64, 1)
 void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             const double* __restrict__ shift, const int* __restrict__ plan,
@@ -370,18 +376,20 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             double* __restrict__ lse_out, double* __restrict__ llpart, int ll_accumulate,
             int8_t* __restrict__ drows, const int* __restrict__ status) {
     constexpr int FLS = NC * 64 + 16;            // LDS stride of a packed row (conflict-free b128 reads)
-    constexpr int TB = I8_MAX_LEV * NC * 1024;   // bytes of one tile's level vectors
+    constexpr int TBL = LV * NC * 1024;          // bytes of one tile's level vectors
     constexpr int STG = L8_WAVES * 16 * FLS;     // staging of 16 rows per wave
-    static_assert(STG <= TB, "row staging aliases the second coefficient buffer");
+    constexpr int TB = TBL > STG ? TBL : STG;
     __shared__ __attribute__((aligned(16))) int8_t cbuf[2][TB];
     __shared__ double rowll[L8_ROWS];
     if (status[I8S_MODE] != 1) return;  // the fp64 kernels run instead
+    const I8Layout LY = i8_layout(plan, d);
+    const int maxlev = status[I8S_MAXLEV];
+    if (LY.nc != NC || maxlev > LV || (LV > S8_LV && maxlev <= S8_LV)) return;  // another variant runs
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ci = lane & 15, h = lane >> 4;
     const int64_t wrow = (int64_t)blockIdx.x * L8_ROWS + wave * (L8_RT * 16);
-    const I8Layout LY = i8_layout(plan, d);
     const int dph = dp >> 1;
     const bool hand_off = status[I8S_MODE2] != 0;
 
@@ -429,12 +437,10 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
     // other buffer by buffer-to-LDS loads (one 1 KB operand piece per wave
     // instruction, no registers held) while tile t is contracted
     constexpr int TSTRIDE = I8_MAX_LEV * I8_MAX_NC * 1024;
-    const int nc = LY.nc;  // chunks of this call's packed rows (<= NC)
     auto issue_tile = [&](int t, int buf) {
-        const int pieces = tinfo[t * I8_TINFO] * nc;
         const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(coef8 + (int64_t)t * TSTRIDE), (short)0, TSTRIDE, BUF_RSRC_WORD3);
-        for (int p = wave; p < pieces; p += L8_WAVES)
+        for (int p = wave; p < LV * NC; p += L8_WAVES)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 cr, (__attribute__((address_space(3))) void*)(cbuf[buf] + p * 1024), 16, lane * 16,
                 p * 1024, 0, 0);
@@ -449,47 +455,55 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             s[rt][q] = 0.0f;
         }
     issue_tile(0, 0);
+    // per-component scale exponent and constant of the next tile, loaded one
+    // tile ahead (their latency would otherwise stall the first fold)
+    int ekn = ek[ci];
+    double ccn = cvec[ci];
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
         if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
-        const int nl = tinfo[t * I8_TINFO];
-        const int slot = t * 16 + ci;
-        const double scale = ldexp(1.0, ek[slot] - 14);  // level 2
-        const double cc = cvec[slot];
+        const double scale = ldexp(1.0, ekn - 14);  // level 2
+        const double cc = ccn;
+        if (t + 1 < ntiles) {
+            ekn = ek[(t + 1) * 16 + ci];
+            ccn = cvec[(t + 1) * 16 + ci];
+        }
         double l[L8_RT][4];
 #pragma unroll
         for (int rt = 0; rt < L8_RT; ++rt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) l[rt][q] = 0.0;
         const int8_t* cb = cbuf[buf] + lane * 16;
-        // one level: every chunk of the row (chunk NC-1 only when the rows
-        // use it), one int32 accumulator per row tile
-        auto mfma_level = [&](int lev, v4i (&acc)[L8_RT]) {
-            const int8_t* bl = cb + lev * nc * 1024;
+        double sc = scale * (1.0 / 128.0);  // a pair starting at level 2
 #pragma unroll
-            for (int rt = 0; rt < L8_RT; ++rt) acc[rt] = v4i{0, 0, 0, 0};
+        for (int lev = 0; lev < LV; lev += 2) {
+            v4i acc0[L8_RT], acc1[L8_RT];
+#pragma unroll
+            for (int rt = 0; rt < L8_RT; ++rt) {
+                acc0[rt] = v4i{0, 0, 0, 0};
+                acc1[rt] = v4i{0, 0, 0, 0};
+            }
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                if (c < NC - 1 || nc == NC) {
-                    const v4i b = *(const v4i*)(bl + c * 1024);
+                const v4i b0 = *(const v4i*)(cb + (lev * NC + c) * 1024);
 #pragma unroll
-                    for (int rt = 0; rt < L8_RT; ++rt) acc[rt] = mfma_i8(A[rt][c], b, acc[rt]);
+                for (int rt = 0; rt < L8_RT; ++rt) acc0[rt] = mfma_i8(A[rt][c], b0, acc0[rt]);
+                if (lev + 1 < LV) {
+                    const v4i b1 = *(const v4i*)(cb + ((lev + 1 < LV ? lev + 1 : lev) * NC + c) * 1024);
+#pragma unroll
+                    for (int rt = 0; rt < L8_RT; ++rt) acc1[rt] = mfma_i8(A[rt][c], b1, acc1[rt]);
                 }
             }
-        };
-        v4i acc0[L8_RT], acc1[L8_RT];
-        double sc = scale * (1.0 / 128.0);  // a pair starting at level 2
-        for (int lev = 0; lev < nl; lev += 2) {
-            const bool two = lev + 1 < nl;
-            mfma_level(lev, acc0);
-            if (two) mfma_level(lev + 1, acc1);
 #pragma unroll
             for (int rt = 0; rt < L8_RT; ++rt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) fold_pair(l[rt][q], acc0[rt][q], two ? acc1[rt][q] : 0, sc);
+                for (int q = 0; q < 4; ++q) fold_pair(l[rt][q], acc0[rt][q], acc1[rt][q], sc);
             sc *= 1.0 / 16384.0;
+            // keep each pair's products and fold together: bounds the live
+            // accumulators (the register budget of two waves per SIMD)
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int rt = 0; rt < L8_RT; ++rt)
@@ -953,29 +967,29 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) l[2 * hf + rb][q] = 0.0;
+            // every level (a tile's levels past its count have zero
+            // digits): one branch-free block the scheduler can interleave
             double sc = scale * (1.0 / 128.0);
 #pragma unroll
             for (int lev = 0; lev < S8_LV; lev += 2) {
-                if (lev < nl) {
-                    v4i a0[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-                    v4i a1[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+                v4i a0[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+                v4i a1[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
 #pragma unroll
-                    for (int c = 0; c < S8_NC; ++c) {
+                for (int c = 0; c < S8_NC; ++c) {
 #pragma unroll
-                        for (int rb = 0; rb < 2; ++rb) a0[rb] = mfma_i8(A[rb][c], qd[lev][c], a0[rb]);
-                        if (lev + 1 < S8_LV) {
+                    for (int rb = 0; rb < 2; ++rb) a0[rb] = mfma_i8(A[rb][c], qd[lev][c], a0[rb]);
+                    if (lev + 1 < S8_LV) {
 #pragma unroll
-                            for (int rb = 0; rb < 2; ++rb)
-                                a1[rb] = mfma_i8(A[rb][c], qd[lev + 1 < S8_LV ? lev + 1 : lev][c], a1[rb]);
-                        }
+                        for (int rb = 0; rb < 2; ++rb)
+                            a1[rb] = mfma_i8(A[rb][c], qd[lev + 1 < S8_LV ? lev + 1 : lev][c], a1[rb]);
                     }
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            fold_pair(l[2 * hf + rb][q], a0[rb][q], a1[rb][q], sc);
-                    sc *= 1.0 / 16384.0;
                 }
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        fold_pair(l[2 * hf + rb][q], a0[rb][q], a1[rb][q], sc);
+                sc *= 1.0 / 16384.0;
             }
         }
         __syncthreads();  // the transposed columns are complete
@@ -1022,7 +1036,8 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
             }
         }
 
-        // ---- M-step: feature digit columns x responsibility digits
+        // ---- M-step: feature digit columns x responsibility digits (a
+        // block whose responsibilities are all exactly zero adds nothing)
         if (__builtin_amdgcn_ballot_w64(any) != 0) {
             const double sp0 = ldexp(1.0, e - 20);
 #pragma unroll
@@ -1102,39 +1117,49 @@ hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, c
     return hipGetLastError();
 }
 
-template <int NC, typename XT>
-static hipError_t launch_lse8_t(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
-                                int ll_acc, hipStream_t st) {
+template <int NC, int LV, typename XT>
+static void launch_lse8_t(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
+                          int ll_acc, hipStream_t st) {
     const int64_t blocks = (n + L8_ROWS - 1) / L8_ROWS;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_lse8<NC, XT>), dim3((unsigned)blocks), dim3(L8_WAVES * 64), 0, st,
+    hipLaunchKernelGGL((k_lse8<NC, LV, XT>), dim3((unsigned)blocks), dim3(L8_WAVES * 64), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.dp, pl.shift, pl.i8_plan, pl.i8_coef, pl.i8_ek,
                        pl.i8_tinfo, pl.cvec, pl.ntiles, lse_out, pl.llpart, ll_acc, pl.i8_rows,
                        pl.status);
-    return hipGetLastError();
 }
 
-// The kernel is instantiated for the largest chunk count the layout can need
-// at this dimension (unused chunks of a row hold zeros and are skipped by the
-// per-level chunk ranges).
+// Chunk counts a packed row can have at this dimension: ceil(dq t / 64) for
+// t = Ia + Ib = 2 .. 2 * I8_MAX_DIGITS feature blocks, at most I8_MAX_NC
+// (wider layouts fail the plan). Bit c of the result marks chunk count c.
 int i8_nc_for(int d) {
-    // digits: up to 3 for a and 3 for a^2 (blocks of d rounded up to 16),
-    // but at most I8_MAX_NC chunks
-    const int nc = ((d + 15) / 16 * 16 * 2 * I8_MAX_DIGITS + 63) / 64;
-    return nc > I8_MAX_NC ? I8_MAX_NC : (nc < 2 ? 2 : nc);
+    const int dq = (d + 15) / 16 * 16;
+    int mask = 0;
+    for (int t = 2; t <= 2 * I8_MAX_DIGITS; ++t) {
+        const int nc = (dq * t + 63) / 64;
+        if (nc <= I8_MAX_NC) mask |= 1 << nc;
+    }
+    return mask;
+}
+
+// Every variant whose chunk count the plan can produce, for both level
+// counts; the plan's digit counts (on the device) let exactly one work.
+template <typename XT>
+static hipError_t launch_lse8_all(const Plan& pl, const void* x, int64_t n, int64_t ldx,
+                                  double* lse_out, int ll_acc, hipStream_t st) {
+#define VAR(NCV)                                                                    \
+    if (pl.i8_nc & (1 << NCV)) {                                                    \
+        launch_lse8_t<NCV, S8_LV, XT>(pl, x, n, ldx, lse_out, ll_acc, st);          \
+        launch_lse8_t<NCV, I8_MAX_LEV, XT>(pl, x, n, ldx, lse_out, ll_acc, st);     \
+    }
+    VAR(1) VAR(2) VAR(3) VAR(4) VAR(5) VAR(6)
+#undef VAR
+    return hipGetLastError();
 }
 
 hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                        double* lse_out, int ll_acc, hipStream_t st) {
-    switch (pl.i8_nc) {
-#define CASE(NCV)                                                                              \
-    case NCV:                                                                                  \
-        return dtype == 0 ? launch_lse8_t<NCV, float>(pl, x, n, ldx, lse_out, ll_acc, st)      \
-                          : launch_lse8_t<NCV, uint16_t>(pl, x, n, ldx, lse_out, ll_acc, st);
-        CASE(2) CASE(3) CASE(4) CASE(5) CASE(6)
-#undef CASE
-    }
-    return hipErrorInvalidValue;
+    if (n <= 0) return hipSuccess;
+    return dtype == 0 ? launch_lse8_all<float>(pl, x, n, ldx, lse_out, ll_acc, st)
+                      : launch_lse8_all<uint16_t>(pl, x, n, ldx, lse_out, ll_acc, st);
 }
 
 template <int DP, typename XT>

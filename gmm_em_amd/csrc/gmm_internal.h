@@ -88,7 +88,7 @@ struct Plan {
     int* i8_ek = nullptr;      // [kp] per-component scale exponent
     int* i8_tinfo = nullptr;   // [ntiles][I8_TINFO] levels per tile
     int8_t* i8_rows = nullptr; // [CHUNK_ROWS][S8_FLG] packed digit rows of the current chunk
-    int i8_nc = 0;             // chunks per packed row the pass-1 kernel is built for
+    int i8_nc = 0;             // bit c set: the pass-1 kernel for c chunks per packed row may run
     bool i8_stats = false;     // the int8 statistics pass exists for this dp
     double2* wlpart = nullptr; // wide: [chunk][ntiles] per-(row, K-tile) (max, sum)
     double* wtval = nullptr;   // wide: [chunk][ntiles][WIDE_TM] top-m candidate values
@@ -125,6 +125,7 @@ hipError_t launch_stats8(const Plan& pl, const void* x, int64_t n, int64_t ldx, 
                          const double* lse, int acc, hipStream_t st);
 hipError_t launch_stats(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                         const double* lse, int acc, hipStream_t st, const int* skip = nullptr);
+// bit mask of the chunk counts a packed row can have at dimension d
 int i8_nc_for(int d);
 bool i8_stats_for(int dp);
 hipError_t launch_finalize(const Plan& pl, int groups, int64_t n, float var_floor, float* w,
