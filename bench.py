@@ -36,7 +36,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense FP32 matrix peak (the metric's reference)
-PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (the contractions' own dtype)
+PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (the fp64 kernels' dtype)
+PEAK_INT8_MFMA_TOPS = 5000.0   # MI355X dense INT8 matrix peak (the int8-slice kernels' dtype)
 
 # HBM bytes per launch of the statistics kernel on the headline workload, from
 # rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this bench (profiles/
@@ -54,7 +55,7 @@ def _kernel_hash() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("gmm_kernels.hip", "gmm_device.h"):
+    for name in ("gmm_kernels.hip", "gmm_i8.hip", "gmm_device.h", "gmm_internal.h"):
         with open(os.path.join(ROOT, "gmm_em_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -164,27 +165,51 @@ def main() -> int:
     # statistics pass is credited with the M-step contraction alone (4 D K
     # flop per row: [r, r a, r a^2] against the row), not with the E-step it
     # recomputes to form responsibilities, and its skipped all-zero groups
-    # count as work. One launch processes one row chunk.
+    # count as work. One launch processes one row chunk. The peak is that of
+    # the MFMA the kernel issues: int8 for the int8-slice kernels (every
+    # product is computed exactly from 7-bit digit slices, so one method flop
+    # costs many int8 operations), fp64 for the fp64 kernels; the fractions
+    # of the fp64 and fp32 MFMA peaks are given beside it.
     (ms1, n1), (ms2, n2) = prof["pass1"], prof["pass2"]
     wide = W.d > 128  # rows past 128 dims run the D-sliced wide kernels
+    arith = ops.estep_arithmetic(ws, dev)
+    i8_pass1 = arith != ops.GMM_ESTEP_FP64
+    i8_pass2 = arith in (ops.GMM_ESTEP_INT8_SLICES_BOTH, ops.GMM_ESTEP_INT8_SLICES_MSTEP)
     if ms2 >= ms1:
-        kname = "k_wide statistics (pass 2)" if wide else "k_stats (pass 2)"
-        kms, kn, alg_row, exec_row = ms2, n2, 4.0 * W.d * W.k, 8.0 * W.d * W.k
+        if wide:
+            kname = "k_wide statistics (pass 2)"
+        elif arith == ops.GMM_ESTEP_INT8_SLICES_MSTEP:
+            kname = "k_stats8x (pass 2: int8-slice E-step and M-step)"
+        elif i8_pass2:
+            kname = "k_stats8 (pass 2: int8-slice E-step, fp64 M-step)"
+        else:
+            kname = "k_stats (pass 2)"
+        kms, kn, alg_row = ms2, n2, 4.0 * W.d * W.k
+        int8_kernel = arith == ops.GMM_ESTEP_INT8_SLICES_MSTEP and not wide
     else:
-        kname = "k_wide normaliser + k_wmerge (pass 1)" if wide else "k_lse (pass 1)"
-        kms, kn, alg_row, exec_row = ms1, n1, 4.0 * W.d * W.k, 4.0 * W.d * W.k
+        if wide:
+            kname = "k_wide normaliser + k_wmerge (pass 1)"
+        elif i8_pass1:
+            kname = "k_lse8 (pass 1: int8-slice E-step)"
+        else:
+            kname = "k_lse (pass 1)"
+        kms, kn, alg_row = ms1, n1, 4.0 * W.d * W.k
+        int8_kernel = i8_pass1 and not wide
     launches_per_step = kn / args.steps
     avg_ms = kms / kn
     rows_per_launch = n_rows / launches_per_step
     alg_flops_launch = alg_row * rows_per_launch
     achieved = alg_flops_launch / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_INT8_MFMA_TOPS if int8_kernel else PEAK_FP64_MFMA_TFLOPS
     roofline = {
         "kernel": kname,
         "bound": "mfma",
         "achieved": round(achieved, 2),
-        "peak": PEAK_FP64_MFMA_TFLOPS,
+        "peak": peak,
         "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_FP64_MFMA_TFLOPS, 4),
+        "peak_dtype": "int8 (dense, TOP/s)" if int8_kernel else "fp64 (dense)",
+        "frac": round(achieved / peak, 4),
+        "frac_of_fp64_mfma_peak": round(achieved / PEAK_FP64_MFMA_TFLOPS, 4),
         "frac_of_fp32_mfma_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
         "traffic": _traffic(W.key, kname),
         "avg_launch_ms": round(avg_ms, 4),
@@ -192,11 +217,7 @@ def main() -> int:
         "rows_per_launch": rows_per_launch,
         "alg_flops_per_row": alg_row,
         "alg_flops_per_launch": alg_flops_launch,
-        # what the kernel issues (the recomputed E-step included), as a
-        # utilisation figure beside the algorithmic one
-        "executed_flops_per_row": exec_row,
-        "executed_frac": round(exec_row * rows_per_launch / (avg_ms * 1e-3) / 1e12
-                               / PEAK_FP64_MFMA_TFLOPS, 4),
+        "estep_arithmetic": arith,
         "pass1_ms_per_step": round(ms1 / args.steps, 3),
         "pass2_ms_per_step": round(ms2 / args.steps, 3),
     }
@@ -246,7 +267,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64",
+        # the contractions' arithmetic: exact int8 slices with fp64 level
+        # sums where the device-side plan selects them, fp64 otherwise
+        "dtype": ("i8+f64" if arith == ops.GMM_ESTEP_INT8_SLICES_MSTEP and not wide
+                  else "i8+f64 (E-step), f64 (M-step)" if i8_pass1 and not wide else "f64"),
         "data": "synthetic",
         "config": {"workload": f"{W.key}: N={n_rows} D={W.d} K={W.k} {W.dtype}, EM iterations "
                                f"{args.warmup}..{args.warmup + args.steps - 1} from seeded init"
@@ -257,7 +281,8 @@ def main() -> int:
         # the metric's reference: 8*N*D*K flops per iteration against the
         # fp32-in/fp32-accumulate MFMA peak
         "pct_mfma_roofline": round(100.0 * tflops / PEAK_FP32_MFMA_TFLOPS, 2),
-        # the same flops against the fp64 MFMA peak the contractions run on
+        # the same flops against the fp64 MFMA peak (the exact arithmetic the
+        # int8 slices reproduce)
         "pct_fp64_mfma_roofline": round(100.0 * tflops / PEAK_FP64_MFMA_TFLOPS, 2),
         # the data matrix is read once per pass, two passes per step
         "hbm_gbs_data_reads": round(2.0 * x_bytes / (ms_step * 1e-3) / 1e9, 1),

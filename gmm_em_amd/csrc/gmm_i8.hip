@@ -324,6 +324,14 @@ __global__ __launch_bounds__(256) void k_i8_coef(const float* __restrict__ w, co
     }
 }
 
+// Digit counts (Ia, Ib) an exact layout can have: a^2 carries about twice
+// the bits of a, so Ib >= Ia, and with at most three digits each only these
+// three pairs occur (the mode kernel below checks it, and the int8
+// statistics pass with the int8 M-step is built for exactly these).
+__host__ __device__ constexpr bool x8_counts_ok(int ia, int ib) {
+    return (ia == 1 && (ib == 1 || ib == 2)) || (ia == 2 && ib == 3);
+}
+
 // Mode: the int8 normaliser pass runs when no check failed and the data is
 // finite; the int8 statistics pass as well when a tile's digit levels fit
 // its registers (stats_ok: the kernel exists for this dimension): with the
@@ -335,7 +343,9 @@ __global__ void k_i8_mode(int* status, const int* plan, int d, int stats_ok) {
         const I8Layout L = i8_layout(plan, d);
         status[I8S_MODE] = m1;
         int m2 = (m1 && stats_ok && L.nc <= S8_NC && status[I8S_MAXLEV] <= S8_LV) ? 1 : 0;
-        if (m2 && plan[I8P_TRUNC_A] == 0 && plan[I8P_TRUNC_B] == 0) m2 = 2;
+        if (m2 && plan[I8P_TRUNC_A] == 0 && plan[I8P_TRUNC_B] == 0 &&
+            x8_counts_ok(plan[I8P_IA], plan[I8P_IB]))
+            m2 = 2;
         status[I8S_MODE2] = m2;
     }
 }
@@ -821,7 +831,35 @@ constexpr int X8_ROWS = 64;  // rows per block: the int8 MFMA's contraction leng
 constexpr int X8_FTS = 80;   // LDS stride of a transposed column (64 rows + 16: conflict-free)
 constexpr int X8_RD = 6;     // responsibility digits
 
-template <int DP, int IM>
+// One 16-dimension tile of one feature kind: its NI digit columns (A
+// operands from the transposed block) against the responsibility digits,
+// one int32 accumulator per level i + j, levels folded in pairs into the
+// fp64 sums of dims 16 j + 4 h + q of component ci.
+template <int NI, int DP>
+__device__ __forceinline__ void x8_mstep_tile(const int8_t* ft, int slot0, int j, int ci, int h,
+                                              const v4i (&R)[X8_RD], double sp0, double (&acc)[4]) {
+    constexpr int NLV = NI + X8_RD - 1;
+    v4i B[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        B[i] = *(const v4i*)(ft + ((slot0 + i) * DP + 16 * j + ci) * X8_FTS + 16 * h);
+    v4i S[NLV];
+#pragma unroll
+    for (int lv = 0; lv < NLV; ++lv) S[lv] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int jr = 0; jr < X8_RD; ++jr) S[i + jr] = mfma_i8(B[i], R[jr], S[i + jr]);
+    double sp = sp0;
+#pragma unroll
+    for (int lv = 0; lv < NLV; lv += 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) fold_pair(acc[q], S[lv][q], lv + 1 < NLV ? S[lv + 1][q] : 0, sp);
+        sp *= 1.0 / 16384.0;
+    }
+}
+
+template <int DP, int IA, int IB>
 __global__ __launch_bounds__(256, 1)
 void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
                const int8_t* __restrict__ coef8, const int* __restrict__ ek,
@@ -831,8 +869,8 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
                int accumulate, const int* __restrict__ status) {
     constexpr int WV = 4, NT = 256;
     constexpr int NJ = DP / 16;
-    constexpr int NLV = IM + X8_RD - 1;           // M-step levels 2 .. IM + X8_RD
-    constexpr int FTB = 2 * IM * DP * X8_FTS;     // transposed columns of one block
+    constexpr int NPS = IA + IB;                  // digit columns per dimension
+    constexpr int FTB = NPS * DP * X8_FTS;        // transposed columns of one block
     constexpr int DGB = X8_ROWS * S8_FLG;         // packed digit rows of one block
     constexpr int DGP = (DGB + 1023) / 1024;      // 1 KB copy pieces
     constexpr double LOG2E = 1.4426950408889634074;
@@ -840,8 +878,8 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
     __shared__ __attribute__((aligned(16))) int8_t ft[FTB];
     __shared__ double ls[2][X8_ROWS];
     if (status[I8S_MODE2] != 2) return;  // another statistics pass runs instead
-    const int ia = plan[I8P_IA], ib = plan[I8P_IB];
-    if ((ia > ib ? ia : ib) != IM) return;  // the variant for this digit count runs
+    if (plan[I8P_IA] != IA || plan[I8P_IB] != IB) return;  // the variant for these counts runs
+    constexpr int ia = IA, ib = IB;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -884,13 +922,6 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
     if (gr1 > n) gr1 = n;
     const int64_t nblk = gr1 > gr0 ? (gr1 - gr0 + X8_ROWS - 1) / X8_ROWS : 0;
 
-    // column blocks of an absent digit (i above that kind's count) stay zero
-    for (int e = tid; e < FTB / 16; e += NT) {
-        const int sl = (e * 16) / (DP * X8_FTS);
-        const int kind = sl / IM, i = sl % IM + 1;
-        if (i > (kind == 0 ? ib : ia)) ((v4i*)ft)[e] = v4i{0, 0, 0, 0};
-    }
-
     auto rows_in = [&](int64_t it) -> int {
         const int64_t nv = gr1 - (gr0 + it * X8_ROWS);
         return nv < 0 ? 0 : (nv > X8_ROWS ? X8_ROWS : (int)nv);
@@ -918,9 +949,9 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // the present column blocks, in packed-row order of their offsets:
-    // a^2 digit i at dq (min(i-1, ib) + min(i-1, ia)), a digit i after it
-    const int nps = ia + ib;
+    // transposed column blocks: slot s < Ib holds a^2 digit s + 1, slot
+    // Ib + s holds a digit s + 1; in the packed row, a^2 digit i starts at
+    // dq (min(i-1, Ib) + min(i-1, Ia)) and a digit i after it
     for (int64_t it = 0; it < nblk; ++it) {
         const int buf = (int)(it & 1);
         double lsn = INFINITY;
@@ -931,7 +962,7 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
         const int8_t* db = dg[buf];
 
         // ---- transpose the block's feature digits into column order
-        for (int task = tid; task < nps * DP * 4; task += NT) {
+        for (int task = tid; task < NPS * DP * 4; task += NT) {
             const int s = task & 3, hh = (task >> 2) & 3;
             const int rem = task >> 4;
             const int dd4 = rem % (DP / 4), sidx = rem / (DP / 4);
@@ -944,7 +975,7 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
             const uint32_t w1 = *(const uint32_t*)(src + S8_FLG);
             const uint32_t w2 = *(const uint32_t*)(src + 2 * S8_FLG);
             const uint32_t w3 = *(const uint32_t*)(src + 3 * S8_FLG);
-            int8_t* dst = ft + ((kind * IM + im1) * DP + 4 * dd4) * X8_FTS + 16 * hh + 4 * s;
+            int8_t* dst = ft + (sidx * DP + 4 * dd4) * X8_FTS + 16 * hh + 4 * s;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t v = ((w0 >> (8 * c)) & 0xffu) | (((w1 >> (8 * c)) & 0xffu) << 8) |
@@ -1041,29 +1072,10 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
         if (__builtin_amdgcn_ballot_w64(any) != 0) {
             const double sp0 = ldexp(1.0, e - 20);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int kind = 0; kind < 2; ++kind) {
-                    v4i B[IM];
-#pragma unroll
-                    for (int i = 0; i < IM; ++i)
-                        B[i] = *(const v4i*)(ft + ((kind * IM + i) * DP + 16 * j + ci) * X8_FTS + 16 * h);
-                    v4i S[NLV];
-#pragma unroll
-                    for (int lv = 0; lv < NLV; ++lv) S[lv] = v4i{0, 0, 0, 0};
-#pragma unroll
-                    for (int i = 0; i < IM; ++i)
-#pragma unroll
-                        for (int jr = 0; jr < X8_RD; ++jr) S[i + jr] = mfma_i8(B[i], R[jr], S[i + jr]);
-                    double sp = sp0;
-#pragma unroll
-                    for (int lv = 0; lv < NLV; lv += 2) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            fold_pair(acc[kind][j][q], S[lv][q], lv + 1 < NLV ? S[lv + 1][q] : 0, sp);
-                        sp *= 1.0 / 16384.0;
-                    }
-                }
+            for (int j = 0; j < NJ; ++j) {
+                x8_mstep_tile<IB, DP>(ft, 0, j, ci, h, R, sp0, acc[0][j]);
+                x8_mstep_tile<IA, DP>(ft, IB, j, ci, h, R, sp0, acc[1][j]);
+            }
         }
         if (it + 1 < nblk && tid < X8_ROWS) ls[buf ^ 1][tid] = lsn;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's digit copies of the next block have landed
@@ -1175,22 +1187,20 @@ static hipError_t launch_stats8_t(const Plan& pl, const void* x, int64_t n, int6
 }
 
 // The three digit-count variants of the int8 M-step pass (each returns at
-// once unless the mode flag and the plan's digit count select it).
+// once unless the mode flag and the plan's digit counts select it).
 template <int DP>
 static hipError_t launch_stats8x_t(const Plan& pl, int64_t n, const double* lse, int acc,
                                    hipStream_t st) {
     int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + X8_ROWS - 1) / X8_ROWS * X8_ROWS;
     if (rpg < X8_ROWS) rpg = X8_ROWS;
     const dim3 grid(pl.ngroups * (pl.ntiles / 4)), block(256);
-    hipLaunchKernelGGL((k_stats8x<DP, 1>), grid, block, 0, st, pl.i8_rows, n, pl.d, pl.i8_coef,
-                       pl.i8_ek, pl.i8_tinfo, pl.cvec, pl.i8_plan, pl.ntiles, lse, rpg, pl.part,
-                       pl.npart, acc, pl.status);
-    hipLaunchKernelGGL((k_stats8x<DP, 2>), grid, block, 0, st, pl.i8_rows, n, pl.d, pl.i8_coef,
-                       pl.i8_ek, pl.i8_tinfo, pl.cvec, pl.i8_plan, pl.ntiles, lse, rpg, pl.part,
-                       pl.npart, acc, pl.status);
-    hipLaunchKernelGGL((k_stats8x<DP, 3>), grid, block, 0, st, pl.i8_rows, n, pl.d, pl.i8_coef,
-                       pl.i8_ek, pl.i8_tinfo, pl.cvec, pl.i8_plan, pl.ntiles, lse, rpg, pl.part,
-                       pl.npart, acc, pl.status);
+#define VAR(IAV, IBV)                                                                          \
+    hipLaunchKernelGGL((k_stats8x<DP, IAV, IBV>), grid, block, 0, st, pl.i8_rows, n, pl.d,     \
+                       pl.i8_coef, pl.i8_ek, pl.i8_tinfo, pl.cvec, pl.i8_plan, pl.ntiles, lse, \
+                       rpg, pl.part, pl.npart, acc, pl.status);
+    static_assert(x8_counts_ok(1, 1) && x8_counts_ok(1, 2) && x8_counts_ok(2, 3), "variants");
+    VAR(1, 1) VAR(1, 2) VAR(2, 3)
+#undef VAR
     return hipGetLastError();
 }
 
