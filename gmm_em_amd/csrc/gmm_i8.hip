@@ -815,11 +815,12 @@ void k_stats8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 // Block = 4 waves, wave w owns K-tile kg*4 + w as in the other statistics
 // passes; the block walks its row group in 64-row blocks. Per block:
 //  * the packed digit rows arrive by buffer-to-LDS copies (one block ahead);
-//  * they are transposed in LDS to column order, position p = 16h + 4s + q
-//    of a column holding row 16s + 4h + q: that is the order in which the
-//    E-step's int8 result leaves the rows in lane (h, i) (rows 4h + q of
-//    16-row tile s), so the responsibilities become MFMA operands without
-//    leaving the lane;
+//  * the E-step's int8 result leaves lane (h, i) with rows 16s + 4h + q
+//    (tile s, register q) of component i: these 16 rows become the lane's
+//    16 positions of the M-step contraction, so the responsibilities turn
+//    into MFMA operands without leaving the lane, and the feature digit
+//    columns are read in the same row order by transposed LDS reads
+//    (ds_read_b64_tr_b8) straight from the packed rows;
 //  * the E-step as in the pass above (same fold, same bits), then the
 //    digits of r', and the M-step: A = feature digit columns (16 dims),
 //    B = responsibility digits (16 components), one int32 accumulator per
@@ -828,21 +829,36 @@ void k_stats8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 // The feature scale 2^G of each dimension multiplies the sums once at the end.
 // ---------------------------------------------------------------------------
 constexpr int X8_ROWS = 64;  // rows per block: the int8 MFMA's contraction length
-constexpr int X8_FTS = 80;   // LDS stride of a transposed column (64 rows + 16: conflict-free)
 constexpr int X8_RD = 6;     // responsibility digits
 
-// One 16-dimension tile of one feature kind: its NI digit columns (A
-// operands from the transposed block) against the responsibility digits,
-// one int32 accumulator per level i + j, levels folded in pairs into the
-// fp64 sums of dims 16 j + 4 h + q of component ci.
-template <int NI, int DP>
-__device__ __forceinline__ void x8_mstep_tile(const int8_t* ft, int slot0, int j, int ci, int h,
-                                              const v4i (&R)[X8_RD], double sp0, double (&acc)[4]) {
+// Transposed LDS read (ds_read_b64_tr_b8, measured on gfx950): within each
+// group of 16 lanes, lane 8u + b receives byte b of the 8 bytes read by
+// lanes 2k + u, k = 0 .. 7 (its byte k), whatever the addresses.
+typedef int v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2i lds_read_tr8(const int8_t* p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+}
+
+// One 16-dimension tile of one feature kind: its NI digit columns against
+// the responsibility digits, one int32 accumulator per level i + j, levels
+// folded in pairs into the fp64 sums of dims 16 j + 4 h + q of component ci.
+// The digit columns come straight from the block's packed rows: column
+// 16 j + ci of lane (h, ci) at position 8 t + k is row 16 (2t + k/4) + 4h +
+// k%4, the row the responsibility digits hold at that position; lane
+// (h, m) reads 8 bytes of row 16 (2t + m/8) + 4h + (m/2)%4 at column
+// 16 j + 8 (m%2) (rofs[t] is that row's offset plus 8 (m%2)).
+template <int NI>
+__device__ __forceinline__ void x8_mstep_tile(const int8_t* db, const int (&rofs)[2], const int (&coff)[NI],
+                                              int j, const v4i (&R)[X8_RD], double sp0,
+                                              double (&acc)[4]) {
     constexpr int NLV = NI + X8_RD - 1;
     v4i B[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-        B[i] = *(const v4i*)(ft + ((slot0 + i) * DP + 16 * j + ci) * X8_FTS + 16 * h);
+    for (int i = 0; i < NI; ++i) {
+        const v2i lo = lds_read_tr8(db + rofs[0] + coff[i] + 16 * j);
+        const v2i hi = lds_read_tr8(db + rofs[1] + coff[i] + 16 * j);
+        B[i] = v4i{lo[0], lo[1], hi[0], hi[1]};
+    }
     v4i S[NLV];
 #pragma unroll
     for (int lv = 0; lv < NLV; ++lv) S[lv] = v4i{0, 0, 0, 0};
@@ -869,17 +885,13 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
                int accumulate, const int* __restrict__ status) {
     constexpr int WV = 4, NT = 256;
     constexpr int NJ = DP / 16;
-    constexpr int NPS = IA + IB;                  // digit columns per dimension
-    constexpr int FTB = NPS * DP * X8_FTS;        // transposed columns of one block
     constexpr int DGB = X8_ROWS * S8_FLG;         // packed digit rows of one block
     constexpr int DGP = (DGB + 1023) / 1024;      // 1 KB copy pieces
     constexpr double LOG2E = 1.4426950408889634074;
     __shared__ __attribute__((aligned(16))) int8_t dg[2][DGP * 1024];
-    __shared__ __attribute__((aligned(16))) int8_t ft[FTB];
     __shared__ double ls[2][X8_ROWS];
     if (status[I8S_MODE2] != 2) return;  // another statistics pass runs instead
     if (plan[I8P_IA] != IA || plan[I8P_IB] != IB) return;  // the variant for these counts runs
-    constexpr int ia = IA, ib = IB;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -949,9 +961,19 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // transposed column blocks: slot s < Ib holds a^2 digit s + 1, slot
-    // Ib + s holds a digit s + 1; in the packed row, a^2 digit i starts at
-    // dq (min(i-1, Ib) + min(i-1, Ia)) and a digit i after it
+    // M-step operand addresses: digit block offsets in the packed row (a^2
+    // digit i at dq (min(i-1, Ib) + min(i-1, Ia)), a digit i after it) and
+    // this lane's two row offsets for the transposed reads
+    int cb[IB], ca[IA];
+#pragma unroll
+    for (int i = 0; i < IB; ++i) cb[i] = dq * ((i < IB ? i : IB) + (i < IA ? i : IA));
+#pragma unroll
+    for (int i = 0; i < IA; ++i) ca[i] = dq * ((i < IB ? i : IB) + (i < IA ? i : IA) + (i < IB ? 1 : 0));
+    int rofs[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        rofs[t] = (16 * (2 * t + (ci >> 3)) + 4 * h + ((ci >> 1) & 3)) * S8_FLG + 8 * (ci & 1);
+
     for (int64_t it = 0; it < nblk; ++it) {
         const int buf = (int)(it & 1);
         double lsn = INFINITY;
@@ -960,29 +982,6 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
             if (tid < X8_ROWS) lsn = load_ls(it + 1);
         }
         const int8_t* db = dg[buf];
-
-        // ---- transpose the block's feature digits into column order
-        for (int task = tid; task < NPS * DP * 4; task += NT) {
-            const int s = task & 3, hh = (task >> 2) & 3;
-            const int rem = task >> 4;
-            const int dd4 = rem % (DP / 4), sidx = rem / (DP / 4);
-            const int kind = sidx < ib ? 0 : 1;
-            const int i = kind == 0 ? sidx + 1 : sidx - ib + 1;
-            const int im1 = i - 1;
-            const int off = dq * ((im1 < ib ? im1 : ib) + (im1 < ia ? im1 : ia) + (kind == 1 && i <= ib ? 1 : 0));
-            const int8_t* src = db + (16 * s + 4 * hh) * S8_FLG + off + 4 * dd4;
-            const uint32_t w0 = *(const uint32_t*)(src);
-            const uint32_t w1 = *(const uint32_t*)(src + S8_FLG);
-            const uint32_t w2 = *(const uint32_t*)(src + 2 * S8_FLG);
-            const uint32_t w3 = *(const uint32_t*)(src + 3 * S8_FLG);
-            int8_t* dst = ft + (sidx * DP + 4 * dd4) * X8_FTS + 16 * hh + 4 * s;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t v = ((w0 >> (8 * c)) & 0xffu) | (((w1 >> (8 * c)) & 0xffu) << 8) |
-                                   (((w2 >> (8 * c)) & 0xffu) << 16) | (((w3 >> (8 * c)) & 0xffu) << 24);
-                *(uint32_t*)(dst + c * X8_FTS) = v;
-            }
-        }
 
         // ---- E-step: four 16-row tiles, the normaliser pass's fold
         double l[4][4];
@@ -1023,7 +1022,6 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
                 sc *= 1.0 / 16384.0;
             }
         }
-        __syncthreads();  // the transposed columns are complete
 
         // ---- responsibilities on the block exponent, as four 7-bit digits
         double t[4][4];
@@ -1073,8 +1071,8 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
             const double sp0 = ldexp(1.0, e - 20);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                x8_mstep_tile<IB, DP>(ft, 0, j, ci, h, R, sp0, acc[0][j]);
-                x8_mstep_tile<IA, DP>(ft, IB, j, ci, h, R, sp0, acc[1][j]);
+                x8_mstep_tile<IB>(db, rofs, cb, j, R, sp0, acc[0][j]);
+                x8_mstep_tile<IA>(db, rofs, ca, j, R, sp0, acc[1][j]);
             }
         }
         if (it + 1 < nblk && tid < X8_ROWS) ls[buf ^ 1][tid] = lsn;
