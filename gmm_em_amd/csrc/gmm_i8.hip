@@ -403,27 +403,54 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
     const int dph = dp >> 1;
     const bool hand_off = status[I8S_MODE2] != 0;
 
-    // ---- pack the wave's rows: digits of a^2 and a, through LDS
+    // ---- pack the wave's rows: digits of a^2 and a, through LDS. Lane l
+    // handles dims l and l + 64 (d <= 128) of 16 rows at a time, with the
+    // per-dimension shift and scales loaded once and the 32 values of a
+    // 16-row tile loaded together.
     v4i A[L8_RT][NC];
     {
         int8_t* stg = &cbuf[1][wave * 16 * FLS];
-        for (int rt = 0; rt < L8_RT; ++rt) {
+        double sh[2], ga[2], gb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int dd = lane + 64 * u;
+            const bool live = dd < d;
+            sh[u] = live ? shift[(dd & 1) * dph + (dd >> 1)] : 0.0;
+            ga[u] = live ? ldexp(1.0, -plan[I8P_GA + dd]) : 0.0;
+            gb[u] = live ? ldexp(1.0, -plan[I8P_GB + dd]) : 0.0;
+        }
+#pragma unroll
+        for (int rt = 0; rt < L8_RT; ++rt) {  // unrolled: A stays in registers
+            float xv[16][2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int64_t row = wrow + rt * 16 + r;
+                    const int dd = lane + 64 * u;
+                    xv[r][u] = (row < n && dd < d) ? load_x(x + row * ldx + dd) : 0.0f;
+                }
             for (int e = lane; e < 16 * FLS / 16; e += 64) ((v4i*)stg)[e] = v4i{0, 0, 0, 0};
             __syncthreads();
-            for (int e = lane; e < 16 * d; e += 64) {
-                const int r = e / d, dd = e - r * d;
-                const int64_t row = wrow + rt * 16 + r;
-                const double s = shift[(dd & 1) * dph + (dd >> 1)];
-                const double a = row < n ? (double)load_x(x + row * ldx + dd) - s : 0.0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
                 int8_t* pr = stg + r * FLS;
-                double va = ldexp(a, -plan[I8P_GA + dd]), vb = ldexp(a * a, -plan[I8P_GB + dd]);
-                for (int i = 1; i <= I8_MAX_DIGITS; ++i) {
-                    const double ta = va * 128.0, tb = vb * 128.0;
-                    const double qa = rint(ta), qb = rint(tb);
-                    va = ta - qa;
-                    vb = tb - qb;
-                    if (LY.off_a[i] >= 0) pr[LY.off_a[i] + dd] = (int8_t)qa;
-                    if (LY.off_b[i] >= 0) pr[LY.off_b[i] + dd] = (int8_t)qb;
+                const bool rv = wrow + rt * 16 + r < n;  // rows past n pack as zeros
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int dd = lane + 64 * u;
+                    if (dd >= d) continue;
+                    const double a = rv ? (double)xv[r][u] - sh[u] : 0.0;
+                    double va = a * ga[u], vb = (a * a) * gb[u];
+#pragma unroll
+                    for (int i = 1; i <= I8_MAX_DIGITS; ++i) {
+                        const double ta = va * 128.0, tb = vb * 128.0;
+                        const double qa = rint(ta), qb = rint(tb);
+                        va = ta - qa;
+                        vb = tb - qb;
+                        if (LY.off_a[i] >= 0) pr[LY.off_a[i] + dd] = (int8_t)qa;
+                        if (LY.off_b[i] >= 0) pr[LY.off_b[i] + dd] = (int8_t)qb;
+                    }
                 }
             }
             __syncthreads();
