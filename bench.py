@@ -39,15 +39,16 @@ PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense FP32 matrix peak (the metric's ref
 PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (the fp64 kernels' dtype)
 PEAK_INT8_MFMA_TOPS = 5000.0   # MI355X dense INT8 matrix peak (the int8-slice kernels' dtype)
 
-# HBM bytes per launch of the statistics kernel on the headline workload, from
+# HBM bytes per launch of the dominant kernel on the headline workload, from
 # rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this bench (profiles/
-# k_stats_descriptor_n10M_d96_k1024_hbm.md), each scaled by what the counter
-# reads for a plain 3.84 GB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0).
-# Keyed by a hash of the kernel sources: a changed kernel reports null until
-# it is profiled again.
+# int8_passes_descriptor_n10M_d96_k1024_hbm.md), each scaled by what the
+# counter reads for a plain 3.84 GB device copy (FETCH_SIZE x2.0, WRITE_SIZE
+# x1.0). Keyed by a hash of the kernel sources: a changed kernel reports null
+# until it is profiled again.
 MEASURED_TRAFFIC = {
-    "45f21e27e4ec1449": {"workload": "descriptor", "kernel": "k_stats (pass 2)",
-                         "bytes_per_launch": 1.6817e9},
+    "54e9df864cecdd62": {"workload": "descriptor",
+                         "kernel": "k_stats8x (pass 2: int8-slice E-step and M-step)",
+                         "bytes_per_launch": 1.3963e9},
 }
 
 

@@ -416,6 +416,17 @@ def test_int8_path_multi_digit_features(ops, hi, scale, step):
               path=(ops.GMM_ESTEP_INT8_SLICES, ops.GMM_ESTEP_INT8_SLICES_MSTEP))
 
 
+def test_int8_mstep_single_digit_squares(ops):
+    # integers in [0, 16]: |a| <= 8 after the shift, so a and a^2 are each
+    # one exact digit (the (1, 1) variant of the int8 M-step)
+    rng = np.random.default_rng(23)
+    n, d, k = 4000 + 11, 24, 40
+    x = rng.integers(0, 17, size=(n, d)).astype(np.float32)
+    w0, m0, v0 = _seed_params(x, k, 23)
+    _per_step(ops, x, w0, m0, v0, 3, label="int8 one-digit squares",
+              path=ops.GMM_ESTEP_INT8_SLICES_MSTEP)
+
+
 def test_int8_estep_with_fp64_mstep(ops):
     # data on a grid of 2^-12: a is exact in three digits, a^2 is not, so the
     # M-step stays fp64; variances so large that the truncation of a^2 moves a
