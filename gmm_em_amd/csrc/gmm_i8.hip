@@ -365,13 +365,12 @@ __device__ __forceinline__ void fold_pair(double& l, int a, int b, double sc) {
 // wave packs the digit rows of its 64 rows once (through LDS) and keeps them
 // in registers as A operands; the K-tiles' level vectors stream through two
 // LDS buffers (tile t+1 is copied while tile t is contracted). The kernel is
-// built for an exact chunk count NC and level count LV (the variants whose
-// NC or LV do not match the plan return at once), so a tile is one
-// branch-free block: per level, all NC chunks into one int32 accumulator
-// per row tile, levels folded in pairs (l += acc * 2^(E_k - 7L) in fp64)
-// while the next pair's products run; the finished tile's values go into the
-// online logsumexp (fp64 running maximum, fp32 scaled sum). A tile's levels
-// past its own count have zero digits.
+// built for an exact chunk count NC and at most LV levels (the variants
+// whose NC or LV do not match the plan return at once): per level pair of
+// the tile (its count is loaded one tile ahead), all NC chunks into one
+// int32 accumulator per row tile, folded into fp64 (l += acc * 2^(E_k - 7L));
+// the finished tile's values go into the online logsumexp (fp64 running
+// maximum, fp32 scaled sum). Levels past a tile's count have zero digits.
 // ---------------------------------------------------------------------------
 constexpr int L8_WAVES = 8;
 constexpr int L8_RT = 4;  // 16-row tiles per wave
@@ -496,6 +495,7 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
     // tile ahead (their latency would otherwise stall the first fold)
     int ekn = ek[ci];
     double ccn = cvec[ci];
+    int nln = tinfo[0];
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
@@ -503,9 +503,11 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
         if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
         const double scale = ldexp(1.0, ekn - 14);  // level 2
         const double cc = ccn;
+        const int nl = nln;  // this tile's digit levels (those past it are zero)
         if (t + 1 < ntiles) {
             ekn = ek[(t + 1) * 16 + ci];
             ccn = cvec[(t + 1) * 16 + ci];
+            nln = tinfo[(t + 1) * I8_TINFO];
         }
         double l[L8_RT][4];
 #pragma unroll
@@ -516,6 +518,7 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
         double sc = scale * (1.0 / 128.0);  // a pair starting at level 2
 #pragma unroll
         for (int lev = 0; lev < LV; lev += 2) {
+            if (lev >= nl) break;  // the tile's remaining levels are zero
             v4i acc0[L8_RT], acc1[L8_RT];
 #pragma unroll
             for (int rt = 0; rt < L8_RT; ++rt) {
@@ -1024,8 +1027,9 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) l[2 * hf + rb][q] = 0.0;
-            // every level (a tile's levels past its count have zero
-            // digits): one branch-free block the scheduler can interleave
+            // every level (a tile's levels past its count have zero digits):
+            // one branch-free block the scheduler can interleave, measured
+            // faster here than stopping at the tile's count
             double sc = scale * (1.0 / 128.0);
 #pragma unroll
             for (int lev = 0; lev < S8_LV; lev += 2) {
