@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense FP32 matrix peak (the metric's reference)
 PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (the fp64 kernels' dtype)
 PEAK_INT8_MFMA_TOPS = 5000.0   # MI355X dense INT8 matrix peak (the int8-slice kernels' dtype)
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak (the split-bf16 kernels' dtype)
 
 # HBM bytes per launch of the dominant kernel on the headline workload, from
 # rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this bench (profiles/
@@ -56,7 +57,7 @@ def _kernel_hash() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("gmm_kernels.hip", "gmm_i8.hip", "gmm_device.h", "gmm_internal.h"):
+    for name in ("gmm_kernels.hip", "gmm_i8.hip", "gmm_b16.hip", "gmm_device.h", "gmm_internal.h"):
         with open(os.path.join(ROOT, "gmm_em_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -169,16 +170,20 @@ def main() -> int:
     # count as work. One launch processes one row chunk. The peak is that of
     # the MFMA the kernel issues: int8 for the int8-slice kernels (every
     # product is computed exactly from 7-bit digit slices, so one method flop
-    # costs many int8 operations), fp64 for the fp64 kernels; the fractions
-    # of the fp64 and fp32 MFMA peaks are given beside it.
+    # costs many int8 operations), bf16 for the split-bf16 kernels (eight
+    # bf16 products per method product), fp64 for the fp64 kernels; the
+    # fractions of the fp64 and fp32 MFMA peaks are given beside it.
     (ms1, n1), (ms2, n2) = prof["pass1"], prof["pass2"]
     wide = W.d > 128  # rows past 128 dims run the D-sliced wide kernels
     arith = ops.estep_arithmetic(ws, dev)
-    i8_pass1 = arith != ops.GMM_ESTEP_FP64
+    b16 = arith == ops.GMM_ESTEP_BF16_SPLIT and not wide
+    i8_pass1 = arith not in (ops.GMM_ESTEP_FP64, ops.GMM_ESTEP_BF16_SPLIT)
     i8_pass2 = arith in (ops.GMM_ESTEP_INT8_SLICES_BOTH, ops.GMM_ESTEP_INT8_SLICES_MSTEP)
     if ms2 >= ms1:
         if wide:
             kname = "k_wide statistics (pass 2)"
+        elif b16:
+            kname = "k_stats16 (pass 2: split-bf16 E-step and M-step)"
         elif arith == ops.GMM_ESTEP_INT8_SLICES_MSTEP:
             kname = "k_stats8x (pass 2: int8-slice E-step and M-step)"
         elif i8_pass2:
@@ -190,6 +195,8 @@ def main() -> int:
     else:
         if wide:
             kname = "k_wide normaliser + k_wmerge (pass 1)"
+        elif b16:
+            kname = "k_lse16 (pass 1: split-bf16 E-step)"
         elif i8_pass1:
             kname = "k_lse8 (pass 1: int8-slice E-step)"
         else:
@@ -201,14 +208,16 @@ def main() -> int:
     rows_per_launch = n_rows / launches_per_step
     alg_flops_launch = alg_row * rows_per_launch
     achieved = alg_flops_launch / (avg_ms * 1e-3) / 1e12
-    peak = PEAK_INT8_MFMA_TOPS if int8_kernel else PEAK_FP64_MFMA_TFLOPS
+    peak = (PEAK_INT8_MFMA_TOPS if int8_kernel else PEAK_BF16_MFMA_TFLOPS if b16
+            else PEAK_FP64_MFMA_TFLOPS)
     roofline = {
         "kernel": kname,
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,
         "unit": "TFLOP/s",
-        "peak_dtype": "int8 (dense, TOP/s)" if int8_kernel else "fp64 (dense)",
+        "peak_dtype": ("int8 (dense, TOP/s)" if int8_kernel else "bf16 (dense)" if b16
+                       else "fp64 (dense)"),
         "frac": round(achieved / peak, 4),
         "frac_of_fp64_mfma_peak": round(achieved / PEAK_FP64_MFMA_TFLOPS, 4),
         "frac_of_fp32_mfma_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
@@ -271,7 +280,8 @@ def main() -> int:
         # the contractions' arithmetic: exact int8 slices with fp64 level
         # sums where the device-side plan selects them, fp64 otherwise
         "dtype": ("i8+f64" if arith == ops.GMM_ESTEP_INT8_SLICES_MSTEP and not wide
-                  else "i8+f64 (E-step), f64 (M-step)" if i8_pass1 and not wide else "f64"),
+                  else "i8+f64 (E-step), f64 (M-step)" if i8_pass1 and not wide
+                  else "bf16x3+f32+f64 (split bf16)" if b16 else "f64"),
         "data": "synthetic",
         "config": {"workload": f"{W.key}: N={n_rows} D={W.d} K={W.k} {W.dtype}, EM iterations "
                                f"{args.warmup}..{args.warmup + args.steps - 1} from seeded init"

@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgmm_em.so")
-SOURCES = ["gmm_api.hip", "gmm_kernels.hip", "gmm_wide.hip", "gmm_ivf.hip", "gmm_i8.hip"]
+SOURCES = ["gmm_api.hip", "gmm_kernels.hip", "gmm_wide.hip", "gmm_ivf.hip", "gmm_i8.hip",
+           "gmm_b16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -62,6 +62,10 @@ bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows, int max_gro
     p.i8_nc = i8 ? i8_nc_for(d) : 0;
     p.i8_stats = i8 && i8_stats_for(p.dp);
     const size_t o_ir = take(p.i8_stats ? (size_t)chunk_rows * S8_FLG : 0);
+    const size_t o_bc = take(i8 ? (size_t)p.ntiles * B16_TILE_BYTES : 0);
+    const size_t o_bv = take(i8 ? (size_t)p.kp * sizeof(double) : 0);
+    const size_t o_ba = take(i8 ? MAX_DP * sizeof(unsigned long long) : 0);
+    const size_t o_bl = take(i8 ? MAX_DP * sizeof(int) : 0);
     const size_t wpart = p.wide ? (size_t)WIDE_CHUNK_ROWS * p.ntiles : 0;
     const size_t o_wl = take(wpart * sizeof(double2));
     const size_t o_wv = take(wpart * WIDE_TM * sizeof(double));
@@ -87,6 +91,10 @@ bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows, int max_gro
             p.i8_ek = (int*)(b + o_ie);
             p.i8_tinfo = (int*)(b + o_it);
             if (p.i8_stats) p.i8_rows = (int8_t*)(b + o_ir);
+            p.b16_coef = (uint16_t*)(b + o_bc);
+            p.b16_cvec = (double*)(b + o_bv);
+            p.b16_amax = (unsigned long long*)(b + o_ba);
+            p.b16_lsb = (int*)(b + o_bl);
         }
         if (p.wide) {
             p.wlpart = (double2*)(b + o_wl);
@@ -177,9 +185,11 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
         if (pl.wide) {
             e = launch_wide_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st);
         } else if (i8) {
-            // both variants are launched; the mode flag the prologue wrote
+            // every variant is launched; the mode flag the prologue wrote
             // lets exactly one of them do the work
             e = launch_lse8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+            if (e == hipSuccess && dtype == GMM_BF16)
+                e = launch_lse16(pl, xc, cn, ldx, lse, ci > 0, st);
             if (e == hipSuccess)
                 e = launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st, 0,
                                pl.status + I8S_MODE);
@@ -192,9 +202,11 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
             prof_mark(2, true, st);
             if (pl.wide) {
                 e = launch_wide_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
-            } else if (i8 && pl.i8_stats) {
-                // as for pass 1: the mode flag lets one of the two work
-                e = launch_stats8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+            } else if (i8) {
+                // as for pass 1: the mode flag lets one of them work
+                if (pl.i8_stats) e = launch_stats8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+                if (e == hipSuccess && dtype == GMM_BF16)
+                    e = launch_stats16(pl, xc, cn, ldx, lse, ci > 0, st);
                 if (e == hipSuccess)
                     e = launch_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st, pl.status + I8S_MODE2);
             } else {
@@ -448,6 +460,7 @@ int gmm_estep_arithmetic(const void* workspace, void* stream) {
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return -1;
     int st2[16] = {0};
     if (hipMemcpy(st2, workspace, sizeof(st2), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+    if (st2[I8S_MODE] == MODE1_B16) return GMM_ESTEP_BF16_SPLIT;
     if (st2[I8S_MODE] != 1) return GMM_ESTEP_FP64;
     if (st2[I8S_MODE2] == 2) return GMM_ESTEP_INT8_SLICES_MSTEP;
     return st2[I8S_MODE2] == 1 ? GMM_ESTEP_INT8_SLICES_BOTH : GMM_ESTEP_INT8_SLICES;

@@ -1,0 +1,639 @@
+// gmm_b16.hip - the E-step and M-step contractions on split bf16
+// (v_mfma_f32_16x16x32_bf16) for data stored in bf16.
+//
+// The fused EM step ("Flash-GMM: A Memory-Efficient Kernel for Scalable Soft
+// Clustering", section 3) contracts, per row n and component k,
+//   l[n][k] = sum_d (P2[k][d] a^2 + P1[k][d] a) + c_k,  a = x - s,
+//   P2 = -w/2, P1 = w b (w = 1/var, b = mu - s),
+// and then the responsibilities r = exp(l - lse) with [a, a^2] over the rows.
+// For bf16 data these contractions run on the bf16 matrix units with every
+// operand split into bf16 parts whose products are exact in fp32:
+//  * the path takes the shift s = 0, so a = x is a bf16 value (8 significant
+//    bits), a^2 has at most 16 significant bits and is exactly a2hi + a2lo,
+//    two bf16 values (the data pass checks that a^2 and its low bits stay in
+//    the normal range);
+//  * each coefficient (fp64) is split into three bf16 parts h + m + l, which
+//    hold it to about 2^-25 relative;
+//  * per 32-dim slice, eight products accumulate in fp32 in increasing order
+//    of size (a2lo Pm, a2hi Pl, a Pl1, a2lo Ph, a2hi Pm, a Pm1, a2hi Ph, a Ph1)
+//    and the slice sums are added in fp64, so the fp32 rounding acts on one
+//    slice at a time: the log-density differs from the fp64 contraction by
+//    about 2^-24 of the slice sums' magnitude (sum_d |P2 a^2| + |P1 a| at
+//    most). The prologue computes that magnitude from the data's largest |x|
+//    per dimension and selects this path only when 2^-23 times it stays
+//    below B16_DELTA (2^-7 nats) for every component; otherwise the fp64
+//    kernels run. The path has its own constants c_k (b = mu), and selecting
+//    it sets the shift to 0 for the finalisation of the statistics.
+//  * M-step: r in fp32 (below 2^-100 it is taken as 0) is exactly rh + rm +
+//    rl in bf16 (24 significant bits in three 8-bit parts), and
+//    sum r a = sum (rl + rm + rh) a, sum r a^2 = sum (rm a2lo + rl a2hi +
+//    rh a2lo + rm a2hi + rh a2hi) (the product rl a2lo, below 2^-25 of the
+//    total, is left out), in fp32 per 32-row tile and in fp64 across tiles.
+//    The mass sum r is taken from the same fp32 values.
+// Both passes contract the E-step in the same order, so they compute the
+// same log-densities bit for bit.
+//
+// MFMA layout (16x16x32 bf16, wave64, measured on gfx950): lane l = 16h + i
+// holds A[i][8h .. 8h+7] and B[8h .. 8h+7][i]; register q of the result is
+// C[4h + q][i].
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "gmm_device.h"
+#include "gmm_internal.h"
+
+namespace gmm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_bf16(v4i a, v4i b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// bf16 bits of a finite fp32 value, rounded to nearest even
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Feature kind (0: a^2 hi, 1: a^2 lo, 2: a) and coefficient part of product
+// m of a slice, in increasing order of size.
+__host__ __device__ constexpr int b16_kind(int m) {
+    return m == 0 || m == 3 ? 1 : (m == 2 || m == 5 || m == 7 ? 2 : 0);
+}
+
+// ---------------------------------------------------------------------------
+// Coefficient pieces, one block per 16-component K-tile (256 threads: 16 per
+// component). Piece (slice j, product m) holds, at [lane 16h + c][8 values],
+// the coefficient part of product m for dims 32j + 8h .. +7 of component c
+// (the MFMA B operand). Dims past d and components past k hold 0. Also the
+// applicability checks: coefficient range, the rounding estimate, and (block
+// 0) the data range per dimension.
+// ---------------------------------------------------------------------------
+
+// nearest value with 8 significant bits (fp64; values below 2^-126, where bf16
+// loses bits, are flushed to 0)
+__device__ __forceinline__ double round_bf16(double r) {
+    if (!(fabs(r) >= 0x1p-126)) return 0.0;
+    const double sc = ldexp(1.0, ilogb(r) - 7);
+    return rint(r / sc) * sc;
+}
+
+// p = q0 + q1 + q2 + (residual below 2^-24 |p|); false if p is out of range
+__device__ __forceinline__ bool split3(double p, uint32_t (&q)[3]) {
+    if (!(fabs(p) < 0x1p126)) {
+        q[0] = q[1] = q[2] = 0;
+        return false;
+    }
+    double r = p;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const double v = round_bf16(r);
+        q[i] = __float_as_uint((float)v) >> 16;  // exact: 8 significant bits
+        r -= v;                                  // exact
+    }
+    return true;
+}
+
+__global__ __launch_bounds__(256) void k_b16_coef(const float* __restrict__ w,
+                                                  const float* __restrict__ mu,
+                                                  const float* __restrict__ var, int k, int d,
+                                                  const unsigned long long* __restrict__ amax,
+                                                  const int* __restrict__ lsb,
+                                                  uint16_t* __restrict__ coef,
+                                                  double* __restrict__ cvec,
+                                                  int* __restrict__ status) {
+    const int tile = blockIdx.x;
+    const int c = threadIdx.x >> 4, sub = threadIdx.x & 15;
+    const int slot = tile * 16 + c;
+    const bool live = slot < k;
+    const int dq = (d + 31) / 32 * 32;
+    uint16_t* dst = coef + (size_t)tile * (B16_TILE_BYTES / 2);
+    double mag = 0.0, csum = 0.0;
+    bool ok = true;
+    for (int dd = sub; dd < dq; dd += 16) {
+        double p2 = 0.0, p1 = 0.0;
+        if (live && dd < d) {
+            const double v = (double)var[(int64_t)slot * d + dd];
+            const double b = (double)mu[(int64_t)slot * d + dd];
+            const double iw = 1.0 / v;
+            p2 = -0.5 * iw;
+            p1 = iw * b;
+            csum += iw * b * b + log(v);
+            const double am = __longlong_as_double((long long)amax[dd]);
+            mag += fabs(p2) * am * am + fabs(p1) * am;
+        }
+        uint32_t q2[3], q1[3];
+        ok &= split3(p2, q2);
+        ok &= split3(p1, q1);
+        // parts by product: P2m, P2l, P1l, P2h, P2m, P1m, P2h, P1h
+        const uint32_t part[B16_PROD] = {q2[1], q2[2], q1[2], q2[0], q2[1], q1[1], q2[0], q1[0]};
+        const int j = dd >> 5, h = (dd >> 3) & 3, e = dd & 7;
+#pragma unroll
+        for (int m = 0; m < B16_PROD; ++m)
+            dst[((j * B16_PROD + m) * 64 + 16 * h + c) * 8 + e] = (uint16_t)part[m];
+    }
+    // the 16 threads of a component are 16 consecutive lanes
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        mag += __shfl_xor(mag, off);
+        csum += __shfl_xor(csum, off);
+    }
+    if (!ok || (live && !(ldexp(mag, -23) <= B16_DELTA))) atomicOr(&status[I8S_B16FAIL], 1);
+    // c_k = log pi_k - 1/2 sum_d (w b^2 + log var) - d/2 log 2 pi, with b = mu
+    if (sub == 0) {
+        const double LOG_2PI = 1.8378770664093454835606594728112;
+        cvec[slot] = live ? log((double)w[slot]) - 0.5 * (csum + (double)d * LOG_2PI) : -INFINITY;
+    }
+    // a^2 = hi + lo exactly needs a^2 and its low bits in the normal range
+    // (amax, lsb: the largest |x| and lowest set bit of x per dimension)
+    if (tile == 0 && threadIdx.x < d) {
+        const double am = __longlong_as_double((long long)amax[threadIdx.x]);
+        if (am > 0.0 && (am >= 0x1p62 || lsb[threadIdx.x] < -63)) atomicOr(&status[I8S_B16FAIL], 1);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1 on split bf16: per-row logsumexp over all components. Block = 4
+// waves (one per SIMD), 64 rows per wave (four 16-row MFMA tiles), 256 rows.
+// Each wave builds the bf16 features [a^2 hi | a^2 lo | a] of its rows once
+// (through LDS) and keeps them in registers as A operands; the K-tiles'
+// coefficient pieces stream through two LDS buffers (tile t+1 is copied by
+// buffer-to-LDS loads while tile t is contracted). Per tile and slice: eight
+// MFMAs into one fp32 accumulator per row tile, added into fp64; the tile's
+// values go into the online logsumexp (fp64 running maximum, fp32 scaled sum).
+// ---------------------------------------------------------------------------
+constexpr int L16_WAVES = 4;
+constexpr int L16_RT = 4;  // 16-row tiles per wave
+constexpr int L16_ROWS = L16_WAVES * L16_RT * 16;
+static_assert(L16_RT * 16 == LL_ROWS, "one log-likelihood partial per wave");
+
+template <int DC>
+__global__ __launch_bounds__(L16_WAVES * 64, 1)
+void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
+             const uint16_t* __restrict__ coef,
+             const double* __restrict__ cvec, int ntiles, double* __restrict__ lse_out,
+             double* __restrict__ llpart, int ll_accumulate, const int* __restrict__ status) {
+    constexpr int DQ = 32 * DC;
+    constexpr int RS = 3 * DQ + 8;  // staged row stride (bf16 values): conflict-free b128 reads
+    constexpr int NP = B16_PROD * DC;
+    constexpr int TBL = NP * 1024;
+    constexpr int STG = L16_WAVES * 16 * RS * 2;
+    constexpr int TB = TBL > STG ? TBL : STG;
+    __shared__ __attribute__((aligned(16))) unsigned char cbuf[2][TB];
+    __shared__ double rowll[L16_ROWS];
+    if (status[I8S_MODE] != MODE1_B16) return;  // another pass-1 kernel runs instead
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = lane & 15, h = lane >> 4;
+    const int64_t wrow = (int64_t)blockIdx.x * L16_ROWS + wave * (L16_RT * 16);
+
+    // ---- features of the wave's rows; lane l handles dims l and l + 64
+    v4i A[L16_RT][3 * DC];
+    {
+        uint16_t* stg = (uint16_t*)&cbuf[1][wave * 16 * RS * 2];
+#pragma unroll
+        for (int rt = 0; rt < L16_RT; ++rt) {  // unrolled: A stays in registers
+            float xv[16][2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int64_t row = wrow + rt * 16 + r;
+                    const int dd = lane + 64 * u;
+                    xv[r][u] = (row < n && dd < d) ? load_x(x + row * ldx + dd) : 0.0f;
+                }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool rv = wrow + rt * 16 + r < n;  // rows past n are zeros
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int dd = lane + 64 * u;
+                    if (dd >= DQ) continue;
+                    // a = x, a bf16 value; a^2 exact in fp32
+                    const float af = (rv && dd < d) ? xv[r][u] : 0.0f;
+                    const float a2 = af * af;
+                    const uint32_t hb = bf16_rne(a2);
+                    const uint32_t lb = __float_as_uint(a2 - bf16_val(hb)) >> 16;  // exact
+                    uint16_t* pr = stg + r * RS;
+                    pr[dd] = (uint16_t)hb;
+                    pr[DQ + dd] = (uint16_t)lb;
+                    pr[2 * DQ + dd] = (uint16_t)(__float_as_uint(af) >> 16);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < 3 * DC; ++c)
+                A[rt][c] = *(const v4i*)(stg + ci * RS + (c / DC) * DQ + (c % DC) * 32 + 8 * h);
+            __syncthreads();
+        }
+    }
+
+    // ---- stream the K-tiles
+    auto issue_tile = [&](int t, int buf) {
+        const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(coef + (int64_t)t * (B16_TILE_BYTES / 2)), (short)0, TBL, BUF_RSRC_WORD3);
+        for (int p = wave; p < NP; p += L16_WAVES)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                cr, (__attribute__((address_space(3))) void*)(cbuf[buf] + p * 1024), 16, lane * 16,
+                p * 1024, 0, 0);
+    };
+    double m[L16_RT][4];
+    float s[L16_RT][4];
+#pragma unroll
+    for (int rt = 0; rt < L16_RT; ++rt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            m[rt][q] = -1.0e300;
+            s[rt][q] = 0.0f;
+        }
+    issue_tile(0, 0);
+    double ccn = cvec[ci];  // the next tile's constant, loaded one tile ahead
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+        const double cc = ccn;
+        if (t + 1 < ntiles) ccn = cvec[(t + 1) * 16 + ci];
+        const unsigned char* cb = cbuf[buf] + lane * 16;
+        double l[L16_RT][4];
+#pragma unroll
+        for (int rt = 0; rt < L16_RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) l[rt][q] = 0.0;
+#pragma unroll
+        for (int j = 0; j < DC; ++j) {
+            f32x4 acc[L16_RT];
+#pragma unroll
+            for (int rt = 0; rt < L16_RT; ++rt) acc[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int mm = 0; mm < B16_PROD; ++mm) {
+                const v4i b = *(const v4i*)(cb + (j * B16_PROD + mm) * 1024);
+#pragma unroll
+                for (int rt = 0; rt < L16_RT; ++rt)
+                    acc[rt] = mfma_bf16(A[rt][b16_kind(mm) * DC + j], b, acc[rt]);
+            }
+#pragma unroll
+            for (int rt = 0; rt < L16_RT; ++rt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) l[rt][q] += (double)acc[rt][q];
+        }
+#pragma unroll
+        for (int rt = 0; rt < L16_RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) lse_push(m[rt][q], s[rt][q], l[rt][q] + cc);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t+1 have landed
+        __syncthreads();                // ... and every wave's; tile t's buffer is free
+    }
+
+    // ---- merge the 16 lanes holding the same rows (fixed butterfly order)
+#pragma unroll
+    for (int rt = 0; rt < L16_RT; ++rt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll 1
+            for (int off = 1; off < 16; off <<= 1) {
+                const double m2 = shfl_xor_d(m[rt][q], off);
+                const float s2 = __shfl_xor(s[rt][q], off);
+                lse_merge(m[rt][q], s[rt][q], m2, s2);
+            }
+        }
+    if (ci == 0) {
+#pragma unroll
+        for (int rt = 0; rt < L16_RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int lr = wave * (L16_RT * 16) + rt * 16 + 4 * h + q;
+                const int64_t row = (int64_t)blockIdx.x * L16_ROWS + lr;
+                double v = 0.0;
+                if (row < n) {
+                    v = m[rt][q] + log((double)s[rt][q]);
+                    if (lse_out) lse_out[row] = v;
+                }
+                rowll[lr] = v;
+            }
+    }
+    __syncthreads();
+    {
+        double tot = rowll[wave * 64 + lane];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) tot += shfl_xor_d(tot, off);
+        const int64_t pi = (int64_t)blockIdx.x * (L16_ROWS / LL_ROWS) + wave;
+        if (lane == 0 && wrow < n) llpart[pi] = (ll_accumulate ? llpart[pi] : 0.0) + tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2 on split bf16: statistics. Block = 4 waves, wave w owning K-tile
+// kg*4 + w (its coefficient pieces stay in registers); the block walks its row
+// group in 32-row tiles. Per tile, the block builds the rows' bf16 features
+// once into LDS (double-buffered, the next tile's while this one is used) in
+// two layouts: row-major [row][a^2 hi | a^2 lo | a] for the E-step's A
+// operand and column-major [feature][row] for the M-step's. The E-step is the
+// normaliser pass's contraction (same order, same bits); the E-step result
+// leaves lane (h, i) with rows 16 rt + 4h + q of component i, and these 8 rows
+// are the lane's 8 positions of the M-step contraction, so the
+// responsibilities become the M-step's B operand without leaving the lane
+// (A = features of 16 columns at the same 8 rows, two 8-byte column reads).
+// A wave skips the M-step of a tile whose responsibilities are all 0.
+// ---------------------------------------------------------------------------
+template <int DC>
+__global__ __launch_bounds__(256, 1)
+void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
+               const uint16_t* __restrict__ coef, const double* __restrict__ cvec, int ntiles,
+               const double* __restrict__ lse,
+               int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
+               int accumulate, const int* __restrict__ status) {
+    constexpr int WV = 4;
+    constexpr int DQ = 32 * DC;
+    constexpr int RS = 3 * DQ + 8;  // row-major stride (bf16 values)
+    constexpr int CS = STATS_ROWS + 8;  // column-major stride: conflict-free 8-byte reads
+    constexpr int NP = B16_PROD * DC;
+    constexpr int NJ = DQ / 16;     // 16-column M-step tiles per feature kind
+    constexpr int TQ = DQ / 4;      // builder threads per 4-row group (4 dims each)
+    static_assert(8 * TQ <= 256, "one builder thread per 4 rows x 4 dims");
+    __shared__ __attribute__((aligned(16))) uint16_t fr[2][STATS_ROWS * RS];
+    __shared__ __attribute__((aligned(16))) uint16_t fc[2][3 * DQ * CS];
+    __shared__ double ls[2][STATS_ROWS];
+    if (status[I8S_MODE2] != MODE2_B16) return;  // another statistics pass runs instead
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = lane & 15, h = lane >> 4;
+    const int kgroups = ntiles / WV;
+    const int nb = gridDim.x;
+    // blocks of one XCD take consecutive (row group, K-group) pairs: the
+    // K-groups of a row group share that XCD's L2 copy of the rows
+    const int o = (nb % 8 == 0) ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int g = o / kgroups;
+    const int tile = (o % kgroups) * WV + wave;
+    const int slot = tile * 16 + ci;
+
+    v4i qb[NP];  // the K-tile's coefficient pieces (B operands), resident
+    {
+        const uint16_t* cp = coef + (int64_t)tile * (B16_TILE_BYTES / 2) + lane * 8;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) qb[p] = *(const v4i*)(cp + p * 512);
+    }
+    const double cc = cvec[slot];
+
+    double tA[NJ][4], tB[NJ][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            tA[j][q] = 0.0;
+            tB[j][q] = 0.0;
+        }
+    double n64 = 0.0;
+
+    const int64_t gr0 = (int64_t)g * rows_per_group;
+    int64_t gr1 = gr0 + rows_per_group;
+    if (gr1 > n) gr1 = n;
+    const int64_t ntile_rows = gr1 > gr0 ? (gr1 - gr0 + STATS_ROWS - 1) / STATS_ROWS : 0;
+
+    // builder: thread (rq, q4) handles rows 4 rq .. +3, dims 4 q4 .. +3
+    const bool bw = tid < 8 * TQ;
+    const int rq = tid / TQ, q4 = tid % TQ;
+    uint32_t xoff[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int dd = 4 * q4 + u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            xoff[r][u] = (bw && dd < d) ? (uint32_t)((((int64_t)(4 * rq + r)) * ldx + dd) * 2)
+                                        : 0xFFFFFFF0u;  // past the buffer: reads 0
+    }
+    float xv[4][4];
+    int nvl = 0;  // valid rows of the loaded tile
+    double lv = 0.0;
+    auto load = [&](int64_t it) {
+        const int64_t rbase = gr0 + it * STATS_ROWS;
+        int64_t nv = gr1 - rbase;
+        nv = nv < 0 ? 0 : (nv > STATS_ROWS ? STATS_ROWS : nv);
+        nvl = (int)nv;
+        const int xbytes = nv > 0 ? (int)(((nv - 1) * ldx + d) * 2) : 0;
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(x + rbase * ldx), (short)0, xbytes, BUF_RSRC_WORD3);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xv[r][u] = buf_load_x<uint16_t>(xr, xoff[r][u]);
+        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
+        const int lrow = tid & (STATS_ROWS - 1);
+        const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
+        lv = lrow < nv ? v : INFINITY;  // rows past the row group: responsibility 0
+    };
+    auto store = [&](int buf) {
+        if (bw) {
+            uint32_t hb[4][4], lb[4][4], ab[4][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    // rows past the group hold zeros (their responsibilities are 0)
+                    const bool live = 4 * rq + r < nvl && 4 * q4 + u < d;
+                    const float af = live ? xv[r][u] : 0.0f;  // a = x
+                    const float a2 = af * af;
+                    hb[r][u] = bf16_rne(a2);
+                    lb[r][u] = __float_as_uint(a2 - bf16_val(hb[r][u])) >> 16;
+                    ab[r][u] = __float_as_uint(af) >> 16;
+                }
+            uint16_t* R = fr[buf];
+            uint16_t* C = fc[buf];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint16_t* pr = R + (4 * rq + r) * RS + 4 * q4;
+                *(uint2*)(pr) = uint2{hb[r][0] | (hb[r][1] << 16), hb[r][2] | (hb[r][3] << 16)};
+                *(uint2*)(pr + DQ) = uint2{lb[r][0] | (lb[r][1] << 16), lb[r][2] | (lb[r][3] << 16)};
+                *(uint2*)(pr + 2 * DQ) = uint2{ab[r][0] | (ab[r][1] << 16), ab[r][2] | (ab[r][3] << 16)};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint16_t* pc = C + (4 * q4 + u) * CS + 4 * rq;
+                *(uint2*)(pc) = uint2{hb[0][u] | (hb[1][u] << 16), hb[2][u] | (hb[3][u] << 16)};
+                *(uint2*)(pc + DQ * CS) = uint2{lb[0][u] | (lb[1][u] << 16), lb[2][u] | (lb[3][u] << 16)};
+                *(uint2*)(pc + 2 * DQ * CS) =
+                    uint2{ab[0][u] | (ab[1][u] << 16), ab[2][u] | (ab[3][u] << 16)};
+            }
+        }
+        ls[buf][tid & (STATS_ROWS - 1)] = lv;
+    };
+
+    if (ntile_rows > 0) {
+        load(0);
+        store(0);
+        if (ntile_rows > 1) load(1);
+    }
+    __syncthreads();
+
+    for (int64_t it = 0; it < ntile_rows; ++it) {
+        const int buf = (int)(it & 1);
+        // E-step: two 16-row tiles, the normaliser pass's order
+        const uint16_t* F = fr[buf];
+        double l[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) l[rt][q] = 0.0;
+#pragma unroll
+        for (int j = 0; j < DC; ++j) {
+            v4i a[2][3];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int kd = 0; kd < 3; ++kd)
+                    a[rt][kd] = *(const v4i*)(F + (16 * rt + ci) * RS + kd * DQ + 32 * j + 8 * h);
+            f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+            for (int mm = 0; mm < B16_PROD; ++mm)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    acc[rt] = mfma_bf16(a[rt][b16_kind(mm)], qb[j * B16_PROD + mm], acc[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) l[rt][q] += (double)acc[rt][q];
+        }
+        // responsibilities of rows 16 rt + 4h + q, split into three bf16 parts
+        // (element 4 rt + q of the lane's B operands)
+        uint32_t rh[8], rm[8], rl[8];
+        bool any = false;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double tv = (l[rt][q] + cc) - ls[buf][16 * rt + 4 * h + q];
+                const float r = tv > -69.31471805599453
+                                    ? __builtin_amdgcn_exp2f((float)(tv * 1.4426950408889634074))
+                                    : 0.0f;  // below 2^-100: 0
+                n64 += (double)r;
+                any |= r != 0.0f;
+                const int e = 4 * rt + q;
+                rh[e] = bf16_rne(r);
+                const float r1 = r - bf16_val(rh[e]);
+                rm[e] = bf16_rne(r1);
+                rl[e] = __float_as_uint(r1 - bf16_val(rm[e])) >> 16;  // exact
+            }
+        v4i Rh, Rm, Rl;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            Rh[w] = (int)(rh[2 * w] | (rh[2 * w + 1] << 16));
+            Rm[w] = (int)(rm[2 * w] | (rm[2 * w + 1] << 16));
+            Rl[w] = (int)(rl[2 * w] | (rl[2 * w + 1] << 16));
+        }
+        // stage the next tile (its buffer was last read before the previous
+        // iteration's closing barrier)
+        if (it + 1 < ntile_rows) {
+            store(buf ^ 1);
+            if (it + 2 < ntile_rows) load(it + 2);
+        }
+        // M-step: C[column 16J + 4h + q][component ci] over the tile's 32 rows
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
+            const uint16_t* C = fc[buf];
+            auto col = [&](int c) -> v4i {
+                const uint2 lo = *(const uint2*)(C + c * CS + 4 * h);
+                const uint2 hi = *(const uint2*)(C + c * CS + 16 + 4 * h);
+                return v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+            };
+#pragma unroll
+            for (int J = 0; J < NJ; ++J) {
+                const int c0 = 16 * J + ci;
+                const v4i fh = col(c0), fl = col(DQ + c0), fa = col(2 * DQ + c0);
+                f32x4 sa = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                sa = mfma_bf16(fa, Rl, sa);
+                sa = mfma_bf16(fa, Rm, sa);
+                sa = mfma_bf16(fa, Rh, sa);
+                sb = mfma_bf16(fl, Rm, sb);
+                sb = mfma_bf16(fh, Rl, sb);
+                sb = mfma_bf16(fl, Rh, sb);
+                sb = mfma_bf16(fh, Rm, sb);
+                sb = mfma_bf16(fh, Rh, sb);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    tA[J][q] += (double)sa[q];
+                    tB[J][q] += (double)sb[q];
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // responsibility mass: lanes ci, ci+16, ci+32, ci+48 hold disjoint rows
+    n64 += shfl_xor_d(n64, 16);
+    n64 += shfl_xor_d(n64, 32);
+    const int64_t gbase = (int64_t)g * ntiles * 16;
+    if (h == 0) {
+        double* np = npart + gbase + slot;
+        *np = (accumulate ? *np : 0.0) + n64;
+    }
+    double* pp = part + (gbase + slot) * (2 * (int64_t)dp);
+#pragma unroll
+    for (int J = 0; J < NJ; ++J)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int dd = 16 * J + 4 * h + q;
+            if (dd < dp) {
+                pp[dd] = (accumulate ? pp[dd] : 0.0) + tA[J][q];
+                pp[dp + dd] = (accumulate ? pp[dp + dd] : 0.0) + tB[J][q];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_b16_coef(const Plan& pl, const float* w, const float* mu, const float* var,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(k_b16_coef, dim3(pl.ntiles), dim3(256), 0, st, w, mu, var, pl.k, pl.d,
+                       pl.b16_amax, pl.b16_lsb, pl.b16_coef, pl.b16_cvec, pl.status);
+    return hipGetLastError();
+}
+
+hipError_t launch_lse16(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
+                        int ll_acc, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((n + L16_ROWS - 1) / L16_ROWS)), block(L16_WAVES * 64);
+    const uint16_t* xb = (const uint16_t*)x;
+    switch ((pl.d + 31) / 32) {
+#define CASE(DCV)                                                                               \
+    case DCV:                                                                                   \
+        hipLaunchKernelGGL((k_lse16<DCV>), grid, block, 0, st, xb, n, pl.d, ldx, pl.b16_coef,   \
+                           pl.b16_cvec, pl.ntiles, lse_out, pl.llpart, ll_acc, pl.status);     \
+        break;
+        CASE(1) CASE(2) CASE(3) CASE(4)
+#undef CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_stats16(const Plan& pl, const void* x, int64_t n, int64_t ldx, const double* lse,
+                          int acc, hipStream_t st) {
+    int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
+    if (rpg < STATS_ROWS) rpg = STATS_ROWS;
+    const dim3 grid(pl.ngroups * (pl.ntiles / 4)), block(256);
+    const uint16_t* xb = (const uint16_t*)x;
+    switch ((pl.d + 31) / 32) {
+#define CASE(DCV)                                                                              \
+    case DCV:                                                                                  \
+        hipLaunchKernelGGL((k_stats16<DCV>), grid, block, 0, st, xb, n, pl.d, ldx, pl.dp,      \
+                           pl.b16_coef, pl.b16_cvec, pl.ntiles, lse, rpg, pl.part, pl.npart,   \
+                           acc, pl.status);                                                    \
+        break;
+        CASE(1) CASE(2) CASE(3) CASE(4)
+#undef CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gmm

@@ -84,11 +84,16 @@ __device__ __forceinline__ I8Layout i8_layout(const int* plan, int d) {
 // ---------------------------------------------------------------------------
 // Data pass: per dimension, the largest |a| (a = x - s) and the lowest set bit
 // over all rows. a is formed in fp64 exactly (fp32 data minus an integer).
+// For bf16 data also the same two figures of x itself (the split-bf16 path
+// works without the shift).
 // ---------------------------------------------------------------------------
-__global__ void k_i8_reset(unsigned long long* amax, int* lsb, int dp) {
+__global__ void k_i8_reset(unsigned long long* amax, int* lsb, unsigned long long* amax0,
+                           int* lsb0, int dp) {
     for (int i = threadIdx.x; i < dp; i += blockDim.x) {
         amax[i] = 0ull;
         lsb[i] = 0x7fffffff;
+        amax0[i] = 0ull;
+        lsb0[i] = 0x7fffffff;
     }
 }
 
@@ -104,14 +109,16 @@ template <typename XT>
 __global__ __launch_bounds__(256) void k_i8_xstats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
                                                    int dp, const double* __restrict__ shift,
                                                    unsigned long long* __restrict__ amax,
-                                                   int* __restrict__ lsb, int* __restrict__ status) {
-    __shared__ unsigned long long sm[256];
-    __shared__ int sl[256];
+                                                   int* __restrict__ lsb,
+                                                   unsigned long long* __restrict__ amax0,
+                                                   int* __restrict__ lsb0, int* __restrict__ status) {
+    __shared__ unsigned long long sm[256], sm0[256];
+    __shared__ int sl[256], sl0[256];
     const int dd = threadIdx.x & 127, r0 = threadIdx.x >> 7;  // two rows per sweep, 128 dims
     const bool live = dd < d;
     const double s = live ? shift[(dd & 1) * (dp >> 1) + (dd >> 1)] : 0.0;
-    unsigned long long mx = 0ull;
-    int lo = 0x7fffffff, bad = 0;
+    unsigned long long mx = 0ull, mx0 = 0ull;
+    int lo = 0x7fffffff, lo0 = 0x7fffffff, bad = 0;
     if (live) {
         // 8 rows per thread and sweep, loaded together
         constexpr int U = 8;
@@ -128,6 +135,13 @@ __global__ __launch_bounds__(256) void k_i8_xstats(const XT* __restrict__ x, int
                 if (base + 2 * u >= n) continue;
                 const double a = (double)xv[u] - s;
                 if (!isfinite(a)) { bad = 1; continue; }
+                if (sizeof(XT) == 2 && xv[u] != 0.0f) {
+                    const double x0 = (double)xv[u];
+                    const unsigned long long b = (unsigned long long)__double_as_longlong(fabs(x0));
+                    mx0 = b > mx0 ? b : mx0;
+                    const int e = lowest_bit_exponent(x0);
+                    lo0 = e < lo0 ? e : lo0;
+                }
                 if (a != 0.0) {
                     const unsigned long long b = (unsigned long long)__double_as_longlong(fabs(a));
                     mx = b > mx ? b : mx;
@@ -139,6 +153,8 @@ __global__ __launch_bounds__(256) void k_i8_xstats(const XT* __restrict__ x, int
     }
     sm[threadIdx.x] = mx;
     sl[threadIdx.x] = lo;
+    sm0[threadIdx.x] = mx0;
+    sl0[threadIdx.x] = lo0;
     __syncthreads();
     if (threadIdx.x < 128 && live) {
         const unsigned long long m2 = sm[threadIdx.x + 128];
@@ -147,6 +163,14 @@ __global__ __launch_bounds__(256) void k_i8_xstats(const XT* __restrict__ x, int
         lo = lo < l2 ? lo : l2;
         if (mx) atomicMax(&amax[dd], mx);
         if (lo != 0x7fffffff) atomicMin(&lsb[dd], lo);
+        if (sizeof(XT) == 2) {
+            const unsigned long long n2 = sm0[threadIdx.x + 128];
+            const int k2 = sl0[threadIdx.x + 128];
+            mx0 = mx0 > n2 ? mx0 : n2;
+            lo0 = lo0 < k2 ? lo0 : k2;
+            if (mx0) atomicMax(&amax0[dd], mx0);
+            if (lo0 != 0x7fffffff) atomicMin(&lsb0[dd], lo0);
+        }
     }
     if (bad) atomicOr(&status[I8S_NONFINITE], 1);
 }
@@ -336,18 +360,28 @@ __host__ __device__ constexpr bool x8_counts_ok(int ia, int ib) {
 // finite; the int8 statistics pass as well when a tile's digit levels fit
 // its registers (stats_ok: the kernel exists for this dimension): with the
 // M-step on int8 slices too (mode 2) when every feature is exact in its
-// digits, else with the fp64 M-step (mode 1).
-__global__ void k_i8_mode(int* status, const int* plan, int d, int stats_ok) {
+// digits, else with the fp64 M-step (mode 1). Otherwise, for bf16 data
+// (b16_ok: the split-bf16 kernels were launched for this call) whose checks
+// passed, both passes run on split bf16 (else on fp64); that path works on x
+// itself, so the shift is set to 0 for the finalisation.
+__global__ void k_i8_mode(int* status, const int* plan, int d, int dp, int stats_ok, int b16_ok,
+                          double* shift) {
+    __shared__ int sel_b16;
     if (threadIdx.x == 0) {
         const int m1 = (status[I8S_FAIL] == 0 && status[I8S_NONFINITE] == 0) ? 1 : 0;
         const I8Layout L = i8_layout(plan, d);
-        status[I8S_MODE] = m1;
         int m2 = (m1 && stats_ok && L.nc <= S8_NC && status[I8S_MAXLEV] <= S8_LV) ? 1 : 0;
         if (m2 && plan[I8P_TRUNC_A] == 0 && plan[I8P_TRUNC_B] == 0 &&
             x8_counts_ok(plan[I8P_IA], plan[I8P_IB]))
             m2 = 2;
-        status[I8S_MODE2] = m2;
+        const int b16 = (!m1 && b16_ok && status[I8S_B16FAIL] == 0 && status[I8S_NONFINITE] == 0) ? 1 : 0;
+        status[I8S_MODE] = b16 ? MODE1_B16 : m1;
+        status[I8S_MODE2] = b16 ? MODE2_B16 : m2;
+        sel_b16 = b16;
     }
+    __syncthreads();
+    if (sel_b16)
+        for (int i = threadIdx.x; i < dp; i += blockDim.x) shift[i] = 0.0;
 }
 
 // One fold of the level sums: a pair of consecutive levels L, L+1 is first
@@ -1138,23 +1172,31 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
 // ---------------------------------------------------------------------------
 hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
                               const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st) {
-    hipLaunchKernelGGL(k_i8_reset, dim3(1), dim3(128), 0, st, pl.i8_amax, pl.i8_lsb, pl.dp);
+    hipLaunchKernelGGL(k_i8_reset, dim3(1), dim3(128), 0, st, pl.i8_amax, pl.i8_lsb, pl.b16_amax,
+                       pl.b16_lsb, pl.dp);
     if (n > 0) {
         int64_t b = (n + 2047) / 2048;
         const unsigned blocks = (unsigned)(b > 8192 ? 8192 : (b < 1 ? 1 : b));
         if (dtype == 0)
             hipLaunchKernelGGL(k_i8_xstats<float>, dim3(blocks), dim3(256), 0, st, (const float*)x, n,
-                               pl.d, ldx, pl.dp, pl.shift, pl.i8_amax, pl.i8_lsb, pl.status);
+                               pl.d, ldx, pl.dp, pl.shift, pl.i8_amax, pl.i8_lsb, pl.b16_amax,
+                               pl.b16_lsb, pl.status);
         else
             hipLaunchKernelGGL(k_i8_xstats<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t*)x,
-                               n, pl.d, ldx, pl.dp, pl.shift, pl.i8_amax, pl.i8_lsb, pl.status);
+                               n, pl.d, ldx, pl.dp, pl.shift, pl.i8_amax, pl.i8_lsb, pl.b16_amax,
+                               pl.b16_lsb, pl.status);
     }
     hipLaunchKernelGGL(k_i8_plan, dim3(1), dim3(128), 0, st, pl.i8_amax, pl.i8_lsb, pl.d, pl.i8_plan,
                        pl.i8_dbl, pl.status);
     hipLaunchKernelGGL(k_i8_coef, dim3(pl.ntiles), dim3(256), 0, st, w, mu, var, pl.k, pl.d, pl.dp,
                        pl.shift, pl.i8_plan, pl.i8_dbl, pl.i8_coef, pl.i8_ek, pl.i8_tinfo, pl.status);
-    hipLaunchKernelGGL(k_i8_mode, dim3(1), dim3(64), 0, st, pl.status, pl.i8_plan, pl.d,
-                       pl.i8_stats ? 1 : 0);
+    const bool b16 = dtype != 0 && pl.b16_coef != nullptr;
+    if (b16) {
+        const hipError_t e = launch_b16_coef(pl, w, mu, var, st);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_i8_mode, dim3(1), dim3(64), 0, st, pl.status, pl.i8_plan, pl.d, pl.dp,
+                       pl.i8_stats ? 1 : 0, b16 ? 1 : 0, pl.shift);
     return hipGetLastError();
 }
 

@@ -51,6 +51,22 @@ constexpr int I8P_IA = 0, I8P_IB = 1, I8P_TRUNC_A = 2, I8P_TRUNC_B = 3, I8P_GA =
 constexpr int I8S_MODE = 4, I8S_FAIL = 5, I8S_NONFINITE = 6;
 // [7] int8 statistics pass selected, [8] largest level count over the tiles
 constexpr int I8S_MODE2 = 7, I8S_MAXLEV = 8;
+// Mode values: status[I8S_MODE] 0 = fp64 pass 1, 1 = int8 slices, 2 = split
+// bf16; status[I8S_MODE2] 0 = fp64 statistics, 1 = int8 E-step + fp64
+// M-step, 2 = int8 E-step and M-step, 3 = split bf16 E-step and M-step.
+constexpr int MODE1_B16 = 2, MODE2_B16 = 3;
+// [9] split-bf16 path not applicable (data or coefficients out of range, or
+// its rounding estimate above B16_DELTA)
+constexpr int I8S_B16FAIL = 9;
+
+// E-step and M-step on split bf16 (gmm_b16.hip), for bf16 data with d <= 128:
+// 32-dim slices (d padded to DQ = 32 * dc), eight bf16 products per slice,
+// one 1 KB MFMA operand piece per (slice, product) and K-tile.
+constexpr int B16_MAX_DC = 4;
+constexpr int B16_PROD = 8;
+constexpr int B16_TILE_BYTES = B16_MAX_DC * B16_PROD * 1024;
+// accepted estimate of the fp32 rounding of a log-density (nats): 2^-7
+constexpr double B16_DELTA = 0.0078125;
 // The statistics pass keeps a K-tile's digit levels in registers: at most
 // S8_LV levels of S8_NC chunks; rows of packed digits are handed from the
 // normaliser pass through the workspace with this stride (bytes), and the
@@ -88,6 +104,10 @@ struct Plan {
     int* i8_ek = nullptr;      // [kp] per-component scale exponent
     int* i8_tinfo = nullptr;   // [ntiles][I8_TINFO] levels per tile
     int8_t* i8_rows = nullptr; // [CHUNK_ROWS][S8_FLG] packed digit rows of the current chunk
+    uint16_t* b16_coef = nullptr;  // [ntiles][B16_TILE_BYTES / 2] split-bf16 coefficient pieces
+    double* b16_cvec = nullptr;    // [kp] per-component constants of the split-bf16 path (shift 0)
+    unsigned long long* b16_amax = nullptr;  // [MAX_DP] largest |x| per dim (fp64 bits), bf16 data
+    int* b16_lsb = nullptr;        // [MAX_DP] lowest set bit exponent of x per dim, bf16 data
     int i8_nc = 0;             // bit c set: the pass-1 kernel for c chunks per packed row may run
     bool i8_stats = false;     // the int8 statistics pass exists for this dp
     double2* wlpart = nullptr; // wide: [chunk][ntiles] per-(row, K-tile) (max, sum)
@@ -118,6 +138,15 @@ hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, c
                               const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st);
 hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                        double* lse_out, int ll_acc, hipStream_t st);
+// Split-bf16 path: coefficient pieces and the applicability check (run by
+// launch_i8_prologue for bf16 data), the normaliser pass (status[I8S_MODE] ==
+// MODE1_B16) and the statistics pass (status[I8S_MODE2] == MODE2_B16).
+hipError_t launch_b16_coef(const Plan& pl, const float* w, const float* mu, const float* var,
+                           hipStream_t st);
+hipError_t launch_lse16(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
+                        int ll_acc, hipStream_t st);
+hipError_t launch_stats16(const Plan& pl, const void* x, int64_t n, int64_t ldx, const double* lse,
+                          int acc, hipStream_t st);
 // int8-slice statistics passes (status[I8S_MODE2] == 1: int8 E-step with the
 // fp64 M-step; == 2: the M-step on int8 slices too; the fp64 statistics
 // kernel is told to skip through the same flag when it is nonzero)

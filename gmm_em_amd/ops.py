@@ -234,14 +234,16 @@ def device_status(ws, device="cuda") -> int:
     return int(lib.gmm_device_status(_ptr(ws), _stream(torch.device(device))))
 
 
-GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES, GMM_ESTEP_INT8_SLICES_BOTH, GMM_ESTEP_INT8_SLICES_MSTEP = 0, 1, 2, 3
+(GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES, GMM_ESTEP_INT8_SLICES_BOTH, GMM_ESTEP_INT8_SLICES_MSTEP,
+ GMM_ESTEP_BF16_SPLIT) = 0, 1, 2, 3, 4
 
 
 def estep_arithmetic(ws, device="cuda") -> int:
     """Synchronise; the gmm_estep_kind of the last EM step / log-likelihood call
     on ``ws``: GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES (normaliser pass on exact
     int8 slices), GMM_ESTEP_INT8_SLICES_BOTH (both passes) or
-    GMM_ESTEP_INT8_SLICES_MSTEP (both passes, and the M-step too)."""
+    GMM_ESTEP_INT8_SLICES_MSTEP (both passes, and the M-step too) or
+    GMM_ESTEP_BF16_SPLIT (bf16 data: both passes on split bf16)."""
     return int(lib.gmm_estep_arithmetic(_ptr(ws), _stream(torch.device(device))))
 
 

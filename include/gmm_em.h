@@ -66,7 +66,8 @@ typedef enum {
     GMM_ESTEP_FP64 = 0,              /* both passes' E-step in fp64 */
     GMM_ESTEP_INT8_SLICES = 1,       /* normaliser pass on int8 slices, statistics pass fp64 */
     GMM_ESTEP_INT8_SLICES_BOTH = 2,  /* both passes' E-step on int8 slices, M-step fp64 */
-    GMM_ESTEP_INT8_SLICES_MSTEP = 3  /* as 2, and the M-step on int8 slices too */
+    GMM_ESTEP_INT8_SLICES_MSTEP = 3, /* as 2, and the M-step on int8 slices too */
+    GMM_ESTEP_BF16_SPLIT = 4         /* bf16 data: E-step and M-step on split bf16 */
 } gmm_estep_kind;
 
 /* Bytes of device workspace needed for data of dimension d and k components.
@@ -108,6 +109,16 @@ size_t gmm_workspace_bytes(int32_t d, int32_t k);
  * Responsibilities keep the fp64 exponent range: a component whose
  * responsibilities are all below fp32's smallest value but above fp64's
  * still gets a nonzero N[k].
+ * bf16 data (d <= 128) that the int8 form does not cover runs both passes on
+ * the bf16 matrix units instead when its checks hold: a = x - s exact in
+ * bf16, and 2^-23 * max_k sum_d (|w/2| amax_d^2 + |w b| amax_d) <= 2^-7
+ * (amax_d the largest |a| in dimension d). Features [a^2 hi, a^2 lo, a] are
+ * exact in bf16, coefficients are split in three bf16 parts, each 32-dim
+ * slice accumulates in fp32 and the slices add in fp64: the log-densities
+ * differ from the fp64 contraction by about 2^-24 of the slices' magnitude
+ * (that estimate is what the check bounds). The M-step contracts fp32
+ * responsibilities (exact as three bf16 parts; those below 2^-100 count as
+ * 0) in fp32 per 32-row tile and fp64 across tiles.
  * loglik_dev (device, 1 double, may be NULL) receives sum_n lse[n] for the
  * INPUT parameters. var_floor must be finite and >= 0. n >= 1. */
 int gmm_em_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,

@@ -162,3 +162,13 @@ def test_profile_hook_states(ops):
     assert ops.lib.gmm_profile_end(*refs) == ops.GMM_E_INVALID
     assert ops.lib.gmm_profile_begin(0) == ops.GMM_E_INVALID
     assert ops.lib.gmm_profile_begin(1 << 20) == ops.GMM_E_INVALID
+
+
+def test_binding_constants_match_header(ops):
+    # the Python binding's status and arithmetic codes are the header's enums
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    vals = dict((m[0], int(m[1])) for m in re.findall(r"\b(GMM_[A-Z0-9_]+)\s*=\s*(-?\d+)", src))
+    for name in ("GMM_ESTEP_FP64", "GMM_ESTEP_INT8_SLICES", "GMM_ESTEP_INT8_SLICES_BOTH",
+                 "GMM_ESTEP_INT8_SLICES_MSTEP", "GMM_ESTEP_BF16_SPLIT", "GMM_OK",
+                 "GMM_E_INVALID", "GMM_E_WORKSPACE", "GMM_E_UNSUPPORTED", "GMM_E_PARAMS"):
+        assert getattr(ops, name) == vals[name], name
