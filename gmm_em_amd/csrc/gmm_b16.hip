@@ -24,7 +24,7 @@
 //    below B16_DELTA (2^-7 nats) for every component; otherwise the fp64
 //    kernels run. The path has its own constants c_k (b = mu), and selecting
 //    it sets the shift to 0 for the finalisation of the statistics.
-//  * M-step: r in fp32 (below 2^-100 it is taken as 0) is exactly rh + rm +
+//  * M-step: r in fp32 (below about 2^-100 it is taken as 0) is exactly rh + rm +
 //    rl in bf16 (24 significant bits in three 8-bit parts), and
 //    sum r a = sum (rl + rm + rh) a, sum r a^2 = sum (rm a2lo + rl a2hi +
 //    rh a2lo + rm a2hi + rh a2hi) (the product rl a2lo, below 2^-25 of the
@@ -60,6 +60,36 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 __device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two fp32 values rounded to nearest even bf16, packed (x in the low half):
+// one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t bf16_pack(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// v = hi + mid + lo exactly for two fp32 values (24 significant bits in three
+// 8-bit parts; the last part is exact, so its rounding is too), packed in pairs
+__device__ __forceinline__ void bf16_split3_pack(float x, float y, uint32_t& ph, uint32_t& pm,
+                                                 uint32_t& pl) {
+    ph = bf16_pack(x, y);
+    const float x1 = x - bf16_lo(ph), y1 = y - bf16_hi(ph);  // exact
+    pm = bf16_pack(x1, y1);
+    pl = bf16_pack(x1 - bf16_lo(pm), y1 - bf16_hi(pm));      // exact
+}
+
+// The three feature kinds of two bf16 values a, b, packed in pairs:
+// a^2 hi, a^2 lo (a^2 = hi + lo exactly: at most 16 significant bits) and a
+__device__ __forceinline__ void b16_features_pack(float a, float b, uint32_t& ph, uint32_t& pl,
+                                                  uint32_t& pa) {
+    const float a2 = a * a, b2 = b * b;  // exact
+    ph = bf16_pack(a2, b2);
+    pl = bf16_pack(a2 - bf16_lo(ph), b2 - bf16_hi(ph));  // exact remainders
+    pa = bf16_pack(a, b);                                // exact
+}
 
 // Feature kind (0: a^2 hi, 1: a^2 lo, 2: a) and coefficient part of product
 // m of a slice, in increasing order of size.
@@ -159,31 +189,45 @@ __global__ __launch_bounds__(256) void k_b16_coef(const float* __restrict__ w,
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1 on split bf16: per-row logsumexp over all components. Block = 4
-// waves (one per SIMD), 64 rows per wave (four 16-row MFMA tiles), 256 rows.
-// Each wave builds the bf16 features [a^2 hi | a^2 lo | a] of its rows once
-// (through LDS) and keeps them in registers as A operands; the K-tiles'
-// coefficient pieces stream through two LDS buffers (tile t+1 is copied by
-// buffer-to-LDS loads while tile t is contracted). Per tile and slice: eight
-// MFMAs into one fp32 accumulator per row tile, added into fp64; the tile's
-// values go into the online logsumexp (fp64 running maximum, fp32 scaled sum).
+// Pass 1 on split bf16: per-row logsumexp over all components. Block = 8
+// waves (two per SIMD, so that one wave's VALU work overlaps the other's
+// MFMAs), 32 rows per wave (two 16-row MFMA tiles), 256 rows. Each wave
+// builds the bf16 features [a^2 hi | a^2 lo | a] of its rows once (through
+// LDS, one kind at a time) and keeps them in registers as A operands; the
+// K-tiles' coefficient pieces stream through two LDS buffers (tile t+1 is
+// copied by buffer-to-LDS loads while tile t is contracted). Per tile and
+// slice: eight MFMAs into one fp32 accumulator per row tile; the slice sums
+// of the first half of the slices and those of the second half are added in
+// fp64 separately, then together (the statistics pass gives the two halves
+// to two waves and adds them the same way); the tile's values go into the
+// online logsumexp (fp64 running maximum, fp32 scaled sum).
 // ---------------------------------------------------------------------------
-constexpr int L16_WAVES = 4;
-constexpr int L16_RT = 4;  // 16-row tiles per wave
+constexpr int L16_WAVES = 8;
+constexpr int L16_RT = 2;  // 16-row tiles per wave
 constexpr int L16_ROWS = L16_WAVES * L16_RT * 16;
-static_assert(L16_RT * 16 == LL_ROWS, "one log-likelihood partial per wave");
+static_assert(L16_ROWS % LL_ROWS == 0 && LL_ROWS % (L16_RT * 16) == 0,
+              "whole log-likelihood partials per block");
+
+// bf16 bits of feature kind kd (0: a^2 hi, 1: a^2 lo, 2: a) of a bf16 value a
+__device__ __forceinline__ uint32_t b16_feature(float a, int kd) {
+    if (kd == 2) return __float_as_uint(a) >> 16;
+    const float a2 = a * a;  // exact: at most 16 significant bits
+    const uint32_t hb = bf16_rne(a2);
+    return kd == 0 ? hb : __float_as_uint(a2 - bf16_val(hb)) >> 16;  // the rest, exact
+}
 
 template <int DC>
 __global__ __launch_bounds__(L16_WAVES * 64, 1)
 void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
-             const uint16_t* __restrict__ coef,
-             const double* __restrict__ cvec, int ntiles, double* __restrict__ lse_out,
-             double* __restrict__ llpart, int ll_accumulate, const int* __restrict__ status) {
+             const uint16_t* __restrict__ coef, const double* __restrict__ cvec, int ntiles,
+             double* __restrict__ lse_out, double* __restrict__ llpart, int ll_accumulate,
+             const int* __restrict__ status) {
     constexpr int DQ = 32 * DC;
-    constexpr int RS = 3 * DQ + 8;  // staged row stride (bf16 values): conflict-free b128 reads
+    constexpr int DCA = (DC + 1) / 2;  // slices of the first half
+    constexpr int KS = DQ + 8;         // staged stride of one kind (bf16 values): conflict-free reads
     constexpr int NP = B16_PROD * DC;
     constexpr int TBL = NP * 1024;
-    constexpr int STG = L16_WAVES * 16 * RS * 2;
+    constexpr int STG = L16_WAVES * 16 * KS * 2;
     constexpr int TB = TBL > STG ? TBL : STG;
     __shared__ __attribute__((aligned(16))) unsigned char cbuf[2][TB];
     __shared__ double rowll[L16_ROWS];
@@ -197,7 +241,7 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
     // ---- features of the wave's rows; lane l handles dims l and l + 64
     v4i A[L16_RT][3 * DC];
     {
-        uint16_t* stg = (uint16_t*)&cbuf[1][wave * 16 * RS * 2];
+        uint16_t* stg = (uint16_t*)&cbuf[1][wave * 16 * KS * 2];
 #pragma unroll
         for (int rt = 0; rt < L16_RT; ++rt) {  // unrolled: A stays in registers
             float xv[16][2];
@@ -207,31 +251,24 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
                 for (int u = 0; u < 2; ++u) {
                     const int64_t row = wrow + rt * 16 + r;
                     const int dd = lane + 64 * u;
+                    // rows past n and dims past d are zeros
                     xv[r][u] = (row < n && dd < d) ? load_x(x + row * ldx + dd) : 0.0f;
                 }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool rv = wrow + rt * 16 + r < n;  // rows past n are zeros
+            for (int kd = 0; kd < 3; ++kd) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int dd = lane + 64 * u;
-                    if (dd >= DQ) continue;
-                    // a = x, a bf16 value; a^2 exact in fp32
-                    const float af = (rv && dd < d) ? xv[r][u] : 0.0f;
-                    const float a2 = af * af;
-                    const uint32_t hb = bf16_rne(a2);
-                    const uint32_t lb = __float_as_uint(a2 - bf16_val(hb)) >> 16;  // exact
-                    uint16_t* pr = stg + r * RS;
-                    pr[dd] = (uint16_t)hb;
-                    pr[DQ + dd] = (uint16_t)lb;
-                    pr[2 * DQ + dd] = (uint16_t)(__float_as_uint(af) >> 16);
-                }
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int dd = lane + 64 * u;
+                        if (dd < DQ) stg[r * KS + dd] = (uint16_t)b16_feature(xv[r][u], kd);
+                    }
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < DC; ++j)
+                    A[rt][kd * DC + j] = *(const v4i*)(stg + ci * KS + 32 * j + 8 * h);
+                __syncthreads();
             }
-            __syncthreads();
-#pragma unroll
-            for (int c = 0; c < 3 * DC; ++c)
-                A[rt][c] = *(const v4i*)(stg + ci * RS + (c / DC) * DQ + (c % DC) * 32 + 8 * h);
-            __syncthreads();
         }
     }
 
@@ -263,11 +300,14 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
         const double cc = ccn;
         if (t + 1 < ntiles) ccn = cvec[(t + 1) * 16 + ci];
         const unsigned char* cb = cbuf[buf] + lane * 16;
-        double l[L16_RT][4];
+        double la[L16_RT][4], lb[L16_RT][4];
 #pragma unroll
         for (int rt = 0; rt < L16_RT; ++rt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) l[rt][q] = 0.0;
+            for (int q = 0; q < 4; ++q) {
+                la[rt][q] = 0.0;
+                lb[rt][q] = 0.0;
+            }
 #pragma unroll
         for (int j = 0; j < DC; ++j) {
             f32x4 acc[L16_RT];
@@ -283,12 +323,15 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
 #pragma unroll
             for (int rt = 0; rt < L16_RT; ++rt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) l[rt][q] += (double)acc[rt][q];
+                for (int q = 0; q < 4; ++q) {
+                    if (j < DCA) la[rt][q] += (double)acc[rt][q];
+                    else lb[rt][q] += (double)acc[rt][q];
+                }
         }
 #pragma unroll
         for (int rt = 0; rt < L16_RT; ++rt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) lse_push(m[rt][q], s[rt][q], l[rt][q] + cc);
+            for (int q = 0; q < 4; ++q) lse_push(m[rt][q], s[rt][q], (la[rt][q] + lb[rt][q]) + cc);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t+1 have landed
         __syncthreads();                // ... and every wave's; tile t's buffer is free
     }
@@ -321,72 +364,86 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
             }
     }
     __syncthreads();
-    {
-        double tot = rowll[wave * 64 + lane];
+    // one partial per 64 rows (fixed order)
+    if (wave < L16_ROWS / LL_ROWS) {
+        double tot = rowll[wave * LL_ROWS + lane];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) tot += shfl_xor_d(tot, off);
         const int64_t pi = (int64_t)blockIdx.x * (L16_ROWS / LL_ROWS) + wave;
-        if (lane == 0 && wrow < n) llpart[pi] = (ll_accumulate ? llpart[pi] : 0.0) + tot;
+        if (lane == 0 && pi * LL_ROWS < n) llpart[pi] = (ll_accumulate ? llpart[pi] : 0.0) + tot;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2 on split bf16: statistics. Block = 4 waves, wave w owning K-tile
-// kg*4 + w (its coefficient pieces stay in registers); the block walks its row
-// group in 32-row tiles. Per tile, the block builds the rows' bf16 features
-// once into LDS (double-buffered, the next tile's while this one is used) in
-// two layouts: row-major [row][a^2 hi | a^2 lo | a] for the E-step's A
-// operand and column-major [feature][row] for the M-step's. The E-step is the
-// normaliser pass's contraction (same order, same bits); the E-step result
-// leaves lane (h, i) with rows 16 rt + 4h + q of component i, and these 8 rows
-// are the lane's 8 positions of the M-step contraction, so the
-// responsibilities become the M-step's B operand without leaving the lane
-// (A = features of 16 columns at the same 8 rows, two 8-byte column reads).
-// A wave skips the M-step of a tile whose responsibilities are all 0.
+// Pass 2 on split bf16: statistics. Block = 8 waves (two per SIMD) for 4
+// K-tiles: waves 2i and 2i+1 own K-tile kg*4 + i and split its dimensions,
+// the first and the second half of the 32-dim slices, for both contractions
+// (each keeps only its half of the coefficient pieces in registers). The
+// block walks its row group in 32-row tiles. Per tile, the block builds the
+// rows' bf16 features once into LDS (double-buffered, the next tile's while
+// this one is used) in two layouts: row-major [row][a^2 hi | a^2 lo | a] for
+// the E-step's A operand and column-major [feature][row] for the M-step's.
+// E-step: each wave contracts its slices (the normaliser pass's order), the
+// two halves' fp64 sums meet through LDS and are added as the normaliser
+// pass adds them, so both waves hold the same log-densities as pass 1, bit
+// for bit. The E-step result leaves lane (h, i) with rows 16 rt + 4h + q of
+// component i, and these 8 rows are the lane's 8 positions of the M-step
+// contraction, so the responsibilities become the M-step's B operand without
+// leaving the lane (A = features of 16 columns at the same 8 rows, two
+// 8-byte column reads); each wave contracts its half of the columns. A pair
+// skips the M-step of a tile whose responsibilities are all 0.
 // ---------------------------------------------------------------------------
 template <int DC>
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(512, 1)
 void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
                const uint16_t* __restrict__ coef, const double* __restrict__ cvec, int ntiles,
-               const double* __restrict__ lse,
-               int64_t rows_per_group, double* __restrict__ part, double* __restrict__ npart,
-               int accumulate, const int* __restrict__ status) {
-    constexpr int WV = 4;
+               const double* __restrict__ lse, int64_t rows_per_group, double* __restrict__ part,
+               double* __restrict__ npart, int accumulate, const int* __restrict__ status) {
+    constexpr int KT = 4;       // K-tiles per block
+    constexpr int NT = 512;
     constexpr int DQ = 32 * DC;
-    constexpr int RS = 3 * DQ + 8;  // row-major stride (bf16 values)
+    constexpr int DCA = (DC + 1) / 2;   // slices of the first half
+    constexpr int RS = 3 * DQ + 8;      // row-major stride (bf16 values)
     constexpr int CS = STATS_ROWS + 8;  // column-major stride: conflict-free 8-byte reads
-    constexpr int NP = B16_PROD * DC;
-    constexpr int NJ = DQ / 16;     // 16-column M-step tiles per feature kind
-    constexpr int TQ = DQ / 4;      // builder threads per 4-row group (4 dims each)
-    static_assert(8 * TQ <= 256, "one builder thread per 4 rows x 4 dims");
+    constexpr int XS = 17;              // exchange row stride (doubles)
+    constexpr int NJ = DQ / 16;         // 16-column M-step tiles per feature kind
+    constexpr int NJA = NJ / 2;         // ... per wave
+    constexpr int TQ = DQ / 2;          // builder threads per 4-row group (2 dims each)
+    static_assert(8 * TQ <= NT, "one builder thread per 4 rows x 2 dims");
     __shared__ __attribute__((aligned(16))) uint16_t fr[2][STATS_ROWS * RS];
     __shared__ __attribute__((aligned(16))) uint16_t fc[2][3 * DQ * CS];
     __shared__ double ls[2][STATS_ROWS];
+    __shared__ double xl[KT][2][STATS_ROWS * XS];
     if (status[I8S_MODE2] != MODE2_B16) return;  // another statistics pass runs instead
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ci = lane & 15, h = lane >> 4;
-    const int kgroups = ntiles / WV;
+    const int kq = wave >> 1, hf = wave & 1;
+    const int kgroups = ntiles / KT;
     const int nb = gridDim.x;
     // blocks of one XCD take consecutive (row group, K-group) pairs: the
     // K-groups of a row group share that XCD's L2 copy of the rows
     const int o = (nb % 8 == 0) ? (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
     const int g = o / kgroups;
-    const int tile = (o % kgroups) * WV + wave;
+    const int tile = (o % kgroups) * KT + kq;
     const int slot = tile * 16 + ci;
+    const int j0 = hf ? DCA : 0, nj = hf ? DC - DCA : DCA;  // this wave's E-step slices
+    const int J0 = hf * NJA;                                // ... and M-step column tiles
 
-    v4i qb[NP];  // the K-tile's coefficient pieces (B operands), resident
+    v4i qb[B16_PROD * DCA];  // this wave's coefficient pieces (B operands), resident
     {
         const uint16_t* cp = coef + (int64_t)tile * (B16_TILE_BYTES / 2) + lane * 8;
 #pragma unroll
-        for (int p = 0; p < NP; ++p) qb[p] = *(const v4i*)(cp + p * 512);
+        for (int p = 0; p < B16_PROD * DCA; ++p)
+            qb[p] = p < B16_PROD * nj ? *(const v4i*)(cp + (j0 * B16_PROD + p) * 512)
+                                      : v4i{0, 0, 0, 0};
     }
     const double cc = cvec[slot];
 
-    double tA[NJ][4], tB[NJ][4];
+    double tA[NJA][4], tB[NJA][4];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < NJA; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             tA[j][q] = 0.0;
@@ -399,19 +456,10 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
     if (gr1 > n) gr1 = n;
     const int64_t ntile_rows = gr1 > gr0 ? (gr1 - gr0 + STATS_ROWS - 1) / STATS_ROWS : 0;
 
-    // builder: thread (rq, q4) handles rows 4 rq .. +3, dims 4 q4 .. +3
+    // builder: thread (rq, q2) handles rows 4 rq .. +3, dims 2 q2 .. +1
     const bool bw = tid < 8 * TQ;
-    const int rq = tid / TQ, q4 = tid % TQ;
-    uint32_t xoff[4][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int dd = 4 * q4 + u;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            xoff[r][u] = (bw && dd < d) ? (uint32_t)((((int64_t)(4 * rq + r)) * ldx + dd) * 2)
-                                        : 0xFFFFFFF0u;  // past the buffer: reads 0
-    }
-    float xv[4][4];
+    const int rq = tid / TQ, q2 = tid % TQ;
+    float xv[4][2];
     int nvl = 0;  // valid rows of the loaded tile
     double lv = 0.0;
     auto load = [&](int64_t it) {
@@ -425,7 +473,14 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) xv[r][u] = buf_load_x<uint16_t>(xr, xoff[r][u]);
+            for (int u = 0; u < 2; ++u) {
+                const int dd = 2 * q2 + u;
+                // dims past d read past the buffer (0); rows past nv likewise
+                const uint32_t off = (bw && dd < d)
+                                         ? (uint32_t)((((int64_t)(4 * rq + r)) * ldx + dd) * 2)
+                                         : 0xFFFFFFF0u;
+                xv[r][u] = buf_load_x<uint16_t>(xr, off);
+            }
         const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
         const int lrow = tid & (STATS_ROWS - 1);
@@ -434,38 +489,29 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
     };
     auto store = [&](int buf) {
         if (bw) {
-            uint32_t hb[4][4], lb[4][4], ab[4][4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    // rows past the group hold zeros (their responsibilities are 0)
-                    const bool live = 4 * rq + r < nvl && 4 * q4 + u < d;
-                    const float af = live ? xv[r][u] : 0.0f;  // a = x
-                    const float a2 = af * af;
-                    hb[r][u] = bf16_rne(a2);
-                    lb[r][u] = __float_as_uint(a2 - bf16_val(hb[r][u])) >> 16;
-                    ab[r][u] = __float_as_uint(af) >> 16;
-                }
             uint16_t* R = fr[buf];
             uint16_t* C = fc[buf];
+            uint32_t f[3][4];  // [kind][row]: dims 2 q2 (low half) and 2 q2 + 1
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                uint16_t* pr = R + (4 * rq + r) * RS + 4 * q4;
-                *(uint2*)(pr) = uint2{hb[r][0] | (hb[r][1] << 16), hb[r][2] | (hb[r][3] << 16)};
-                *(uint2*)(pr + DQ) = uint2{lb[r][0] | (lb[r][1] << 16), lb[r][2] | (lb[r][3] << 16)};
-                *(uint2*)(pr + 2 * DQ) = uint2{ab[r][0] | (ab[r][1] << 16), ab[r][2] | (ab[r][3] << 16)};
+                const bool live = 4 * rq + r < nvl;  // rows past the group hold zeros
+                b16_features_pack(live ? xv[r][0] : 0.0f, live ? xv[r][1] : 0.0f, f[0][r], f[1][r],
+                                  f[2][r]);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                uint16_t* pc = C + (4 * q4 + u) * CS + 4 * rq;
-                *(uint2*)(pc) = uint2{hb[0][u] | (hb[1][u] << 16), hb[2][u] | (hb[3][u] << 16)};
-                *(uint2*)(pc + DQ * CS) = uint2{lb[0][u] | (lb[1][u] << 16), lb[2][u] | (lb[3][u] << 16)};
-                *(uint2*)(pc + 2 * DQ * CS) =
-                    uint2{ab[0][u] | (ab[1][u] << 16), ab[2][u] | (ab[3][u] << 16)};
+            for (int kd = 0; kd < 3; ++kd) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) *(uint32_t*)(R + (4 * rq + r) * RS + kd * DQ + 2 * q2) = f[kd][r];
+                // columns: rows 4 rq .. +3 of each dim (the low or high halves)
+                *(uint2*)(C + (kd * DQ + 2 * q2) * CS + 4 * rq) =
+                    uint2{__builtin_amdgcn_perm(f[kd][1], f[kd][0], 0x05040100u),
+                          __builtin_amdgcn_perm(f[kd][3], f[kd][2], 0x05040100u)};
+                *(uint2*)(C + (kd * DQ + 2 * q2 + 1) * CS + 4 * rq) =
+                    uint2{__builtin_amdgcn_perm(f[kd][1], f[kd][0], 0x07060302u),
+                          __builtin_amdgcn_perm(f[kd][3], f[kd][2], 0x07060302u)};
             }
         }
-        ls[buf][tid & (STATS_ROWS - 1)] = lv;
+        if (tid < STATS_ROWS) ls[buf][tid] = lv;
     };
 
     if (ntile_rows > 0) {
@@ -475,60 +521,71 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
     }
     __syncthreads();
 
+    double* xw = xl[kq][hf];
+    const double* xo = xl[kq][hf ^ 1];
     for (int64_t it = 0; it < ntile_rows; ++it) {
         const int buf = (int)(it & 1);
-        // E-step: two 16-row tiles, the normaliser pass's order
+        // E-step over this wave's slices, two 16-row tiles
         const uint16_t* F = fr[buf];
-        double l[2][4];
+        double lp[2][4];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) l[rt][q] = 0.0;
+            for (int q = 0; q < 4; ++q) lp[rt][q] = 0.0;
 #pragma unroll
-        for (int j = 0; j < DC; ++j) {
-            v4i a[2][3];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int kd = 0; kd < 3; ++kd)
-                    a[rt][kd] = *(const v4i*)(F + (16 * rt + ci) * RS + kd * DQ + 32 * j + 8 * h);
-            f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-            for (int mm = 0; mm < B16_PROD; ++mm)
+        for (int jj = 0; jj < DCA; ++jj) {
+            if (jj < nj) {
+                const int j = j0 + jj;
+                v4i a[2][3];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
-                    acc[rt] = mfma_bf16(a[rt][b16_kind(mm)], qb[j * B16_PROD + mm], acc[rt]);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+                    for (int kd = 0; kd < 3; ++kd)
+                        a[rt][kd] = *(const v4i*)(F + (16 * rt + ci) * RS + kd * DQ + 32 * j + 8 * h);
+                f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) l[rt][q] += (double)acc[rt][q];
+                for (int mm = 0; mm < B16_PROD; ++mm)
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        acc[rt] = mfma_bf16(a[rt][b16_kind(mm)], qb[jj * B16_PROD + mm], acc[rt]);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) lp[rt][q] += (double)acc[rt][q];
+            }
         }
+        // the two halves meet: l = (first half) + (second half)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xw[(16 * rt + 4 * h + q) * XS + ci] = lp[rt][q];
+        __syncthreads();
         // responsibilities of rows 16 rt + 4h + q, split into three bf16 parts
         // (element 4 rt + q of the lane's B operands)
-        uint32_t rh[8], rm[8], rl[8];
+        float rv[8];
         bool any = false;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const double tv = (l[rt][q] + cc) - ls[buf][16 * rt + 4 * h + q];
-                const float r = tv > -69.31471805599453
-                                    ? __builtin_amdgcn_exp2f((float)(tv * 1.4426950408889634074))
-                                    : 0.0f;  // below 2^-100: 0
+                const double ov = xo[(16 * rt + 4 * h + q) * XS + ci];
+                const double l = hf == 0 ? lp[rt][q] + ov : ov + lp[rt][q];
+                // the exponent in fp64, then fp32 (|t| < 70 where r is kept)
+                const float tf = (float)((l + cc) - ls[buf][16 * rt + 4 * h + q]);
+                const float r = tf > -69.3147181f ? __builtin_amdgcn_exp2f(tf * 1.44269504f)
+                                                  : 0.0f;  // below about 2^-100: 0
                 n64 += (double)r;
                 any |= r != 0.0f;
-                const int e = 4 * rt + q;
-                rh[e] = bf16_rne(r);
-                const float r1 = r - bf16_val(rh[e]);
-                rm[e] = bf16_rne(r1);
-                rl[e] = __float_as_uint(r1 - bf16_val(rm[e])) >> 16;  // exact
+                rv[4 * rt + q] = r;
             }
         v4i Rh, Rm, Rl;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            Rh[w] = (int)(rh[2 * w] | (rh[2 * w + 1] << 16));
-            Rm[w] = (int)(rm[2 * w] | (rm[2 * w + 1] << 16));
-            Rl[w] = (int)(rl[2 * w] | (rl[2 * w + 1] << 16));
+            uint32_t ph, pm, pl;
+            bf16_split3_pack(rv[2 * w], rv[2 * w + 1], ph, pm, pl);
+            Rh[w] = (int)ph;
+            Rm[w] = (int)pm;
+            Rl[w] = (int)pl;
         }
         // stage the next tile (its buffer was last read before the previous
         // iteration's closing barrier)
@@ -545,8 +602,8 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
                 return v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
             };
 #pragma unroll
-            for (int J = 0; J < NJ; ++J) {
-                const int c0 = 16 * J + ci;
+            for (int JJ = 0; JJ < NJA; ++JJ) {
+                const int c0 = 16 * (J0 + JJ) + ci;
                 const v4i fh = col(c0), fl = col(DQ + c0), fa = col(2 * DQ + c0);
                 f32x4 sa = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 sa = mfma_bf16(fa, Rl, sa);
@@ -559,35 +616,35 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
                 sb = mfma_bf16(fh, Rh, sb);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    tA[J][q] += (double)sa[q];
-                    tB[J][q] += (double)sb[q];
+                    tA[JJ][q] += (double)sa[q];
+                    tB[JJ][q] += (double)sb[q];
                 }
             }
         }
         __syncthreads();
     }
 
-    // responsibility mass: lanes ci, ci+16, ci+32, ci+48 hold disjoint rows
+    // responsibility mass (both waves of a pair hold it; the first writes):
+    // lanes ci, ci+16, ci+32, ci+48 hold disjoint rows
     n64 += shfl_xor_d(n64, 16);
     n64 += shfl_xor_d(n64, 32);
     const int64_t gbase = (int64_t)g * ntiles * 16;
-    if (h == 0) {
+    if (h == 0 && hf == 0) {
         double* np = npart + gbase + slot;
         *np = (accumulate ? *np : 0.0) + n64;
     }
     double* pp = part + (gbase + slot) * (2 * (int64_t)dp);
 #pragma unroll
-    for (int J = 0; J < NJ; ++J)
+    for (int JJ = 0; JJ < NJA; ++JJ)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int dd = 16 * J + 4 * h + q;
+            const int dd = 16 * (J0 + JJ) + 4 * h + q;
             if (dd < dp) {
-                pp[dd] = (accumulate ? pp[dd] : 0.0) + tA[J][q];
-                pp[dp + dd] = (accumulate ? pp[dp + dd] : 0.0) + tB[J][q];
+                pp[dd] = (accumulate ? pp[dd] : 0.0) + tA[JJ][q];
+                pp[dp + dd] = (accumulate ? pp[dp + dd] : 0.0) + tB[JJ][q];
             }
         }
 }
-
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -620,7 +677,7 @@ hipError_t launch_stats16(const Plan& pl, const void* x, int64_t n, int64_t ldx,
                           int acc, hipStream_t st) {
     int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
     if (rpg < STATS_ROWS) rpg = STATS_ROWS;
-    const dim3 grid(pl.ngroups * (pl.ntiles / 4)), block(256);
+    const dim3 grid(pl.ngroups * (pl.ntiles / 4)), block(512);
     const uint16_t* xb = (const uint16_t*)x;
     switch ((pl.d + 31) / 32) {
 #define CASE(DCV)                                                                              \
