@@ -375,24 +375,33 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2 on split bf16: statistics. Block = 8 waves (two per SIMD) for 4
-// K-tiles: waves 2i and 2i+1 own K-tile kg*4 + i and split its dimensions,
-// the first and the second half of the 32-dim slices, for both contractions
-// (each keeps only its half of the coefficient pieces in registers). The
-// block walks its row group in 32-row tiles. Per tile, the block builds the
-// rows' bf16 features once into LDS (double-buffered, the next tile's while
-// this one is used) in two layouts: row-major [row][a^2 hi | a^2 lo | a] for
-// the E-step's A operand and column-major [feature][row] for the M-step's.
-// E-step: each wave contracts its slices (the normaliser pass's order), the
-// two halves' fp64 sums meet through LDS and are added as the normaliser
-// pass adds them, so both waves hold the same log-densities as pass 1, bit
-// for bit. The E-step result leaves lane (h, i) with rows 16 rt + 4h + q of
-// component i, and these 8 rows are the lane's 8 positions of the M-step
-// contraction, so the responsibilities become the M-step's B operand without
-// leaving the lane (A = features of 16 columns at the same 8 rows, two
-// 8-byte column reads); each wave contracts its half of the columns. A pair
-// skips the M-step of a tile whose responsibilities are all 0.
+// Pass 2 on split bf16: statistics. Block = 8 waves for 4 K-tiles (two waves
+// per SIMD): waves 0-3 are E-waves, waves 4-7 M-waves, and the two waves of
+// a SIMD own the same K-tile kg*4 + (wave & 3). The block walks its row group
+// in 32-row tiles, one barrier per tile, as a two-stage pipeline:
+//  * every wave helps build the next tile's bf16 features into LDS, as 1 KB
+//    MFMA operand pieces: E pieces (row tile, kind, slice) for the E-step's
+//    A operand, M pieces (kind, 16-column tile) for the M-step's, in which
+//    lane (h, i) holds column i at the rows 4h .. 4h+3 and 16+4h .. 16+4h+3;
+//    a piece's 16-byte lane chunks are rotated (chunk 16h + (i + 4h + p) mod
+//    16 for piece p) so that both the builders' writes and the MFMA lanes'
+//    reads hit distinct banks;
+//  * the E-wave keeps all the K-tile's coefficient pieces in registers,
+//    contracts the tile exactly as the normaliser pass does (same order,
+//    same bits), forms r = exp(l - lse), splits it into three bf16 parts and
+//    hands them to its M-wave through LDS (the E-step result leaves lane
+//    (h, i) with rows 16 rt + 4h + q of component i, which are the lane's 8
+//    positions of the M-step contraction);
+//  * the M-wave, one tile behind, contracts those parts with the tile's M
+//    pieces into fp32 per tile and fp64 totals (skipping a tile whose
+//    responsibilities are all 0).
+// The two roles run different code on a SIMD at the same time, so one
+// wave's VALU work (exponentials, splits, fp64 folds) overlaps the other's
+// MFMAs. The features are triple-buffered for the M-waves' lag.
 // ---------------------------------------------------------------------------
+// rotated position of lane (h, i)'s 16-byte chunk in piece p
+__device__ __forceinline__ int b16_chunk(int h, int i, int p) { return 16 * h + ((i + 4 * h + p) & 15); }
+
 template <int DC>
 __global__ __launch_bounds__(512, 1)
 void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
@@ -400,26 +409,25 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
                const double* __restrict__ lse, int64_t rows_per_group, double* __restrict__ part,
                double* __restrict__ npart, int accumulate, const int* __restrict__ status) {
     constexpr int KT = 4;       // K-tiles per block
-    constexpr int NT = 512;
     constexpr int DQ = 32 * DC;
     constexpr int DCA = (DC + 1) / 2;   // slices of the first half
-    constexpr int RS = 3 * DQ + 8;      // row-major stride (bf16 values)
-    constexpr int CS = STATS_ROWS + 8;  // column-major stride: conflict-free 8-byte reads
-    constexpr int XS = 17;              // exchange row stride (doubles)
     constexpr int NJ = DQ / 16;         // 16-column M-step tiles per feature kind
-    constexpr int NJA = NJ / 2;         // ... per wave
     constexpr int TQ = DQ / 2;          // builder threads per 4-row group (2 dims each)
-    static_assert(8 * TQ <= NT, "one builder thread per 4 rows x 2 dims");
-    __shared__ __attribute__((aligned(16))) uint16_t fr[2][STATS_ROWS * RS];
-    __shared__ __attribute__((aligned(16))) uint16_t fc[2][3 * DQ * CS];
+    constexpr int NPE = 2 * 3 * DC;     // E pieces per tile: (row tile, kind, slice)
+    constexpr int NPM = 3 * NJ;         // M pieces per tile: (kind, column tile)
+    static_assert(8 * TQ <= 512, "one builder thread per 4 rows x 2 dims");
+    __shared__ __attribute__((aligned(16))) uint32_t fe[2][NPE * 256];
+    __shared__ __attribute__((aligned(16))) uint32_t fm[3][NPM * 256];
+    __shared__ __attribute__((aligned(16))) uint32_t rr[2][KT][3 * 256];  // r parts per K-tile
     __shared__ double ls[2][STATS_ROWS];
-    __shared__ double xl[KT][2][STATS_ROWS * XS];
+    __shared__ int anyr[2][KT];
     if (status[I8S_MODE2] != MODE2_B16) return;  // another statistics pass runs instead
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ci = lane & 15, h = lane >> 4;
-    const int kq = wave >> 1, hf = wave & 1;
+    const int kq = wave & 3;
+    const bool ewave = wave < 4;
     const int kgroups = ntiles / KT;
     const int nb = gridDim.x;
     // blocks of one XCD take consecutive (row group, K-group) pairs: the
@@ -428,28 +436,6 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
     const int g = o / kgroups;
     const int tile = (o % kgroups) * KT + kq;
     const int slot = tile * 16 + ci;
-    const int j0 = hf ? DCA : 0, nj = hf ? DC - DCA : DCA;  // this wave's E-step slices
-    const int J0 = hf * NJA;                                // ... and M-step column tiles
-
-    v4i qb[B16_PROD * DCA];  // this wave's coefficient pieces (B operands), resident
-    {
-        const uint16_t* cp = coef + (int64_t)tile * (B16_TILE_BYTES / 2) + lane * 8;
-#pragma unroll
-        for (int p = 0; p < B16_PROD * DCA; ++p)
-            qb[p] = p < B16_PROD * nj ? *(const v4i*)(cp + (j0 * B16_PROD + p) * 512)
-                                      : v4i{0, 0, 0, 0};
-    }
-    const double cc = cvec[slot];
-
-    double tA[NJA][4], tB[NJA][4];
-#pragma unroll
-    for (int j = 0; j < NJA; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            tA[j][q] = 0.0;
-            tB[j][q] = 0.0;
-        }
-    double n64 = 0.0;
 
     const int64_t gr0 = (int64_t)g * rows_per_group;
     int64_t gr1 = gr0 + rows_per_group;
@@ -487,10 +473,11 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
         const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
         lv = lrow < nv ? v : INFINITY;  // rows past the row group: responsibility 0
     };
-    auto store = [&](int buf) {
+    // features of the loaded tile into E buffer be and M buffer bm
+    auto store = [&](int be, int bm) {
         if (bw) {
-            uint16_t* R = fr[buf];
-            uint16_t* C = fc[buf];
+            const int rt = rq >> 2, hr = rq & 3;  // rows 16 rt + 4 hr .. +3
+            const int j = q2 >> 4, hd = (q2 >> 2) & 3, ew = q2 & 3;  // dims 32 j + 8 hd + 2 ew .. +1
             uint32_t f[3][4];  // [kind][row]: dims 2 q2 (low half) and 2 q2 + 1
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -500,150 +487,183 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
             }
 #pragma unroll
             for (int kd = 0; kd < 3; ++kd) {
+                // E piece (rt, kd, j): row 4 hr + r is lane (hd, 4 hr + r), dims 2 ew .. +1 of its 8
+                uint32_t* pe = fe[be] + ((rt * 3 + kd) * DC + j) * 256;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) *(uint32_t*)(R + (4 * rq + r) * RS + kd * DQ + 2 * q2) = f[kd][r];
-                // columns: rows 4 rq .. +3 of each dim (the low or high halves)
-                *(uint2*)(C + (kd * DQ + 2 * q2) * CS + 4 * rq) =
-                    uint2{__builtin_amdgcn_perm(f[kd][1], f[kd][0], 0x05040100u),
-                          __builtin_amdgcn_perm(f[kd][3], f[kd][2], 0x05040100u)};
-                *(uint2*)(C + (kd * DQ + 2 * q2 + 1) * CS + 4 * rq) =
-                    uint2{__builtin_amdgcn_perm(f[kd][1], f[kd][0], 0x07060302u),
-                          __builtin_amdgcn_perm(f[kd][3], f[kd][2], 0x07060302u)};
+                for (int r = 0; r < 4; ++r) pe[b16_chunk(hd, 4 * hr + r, j) * 4 + ew] = f[kd][r];
+                // M pieces (kd, J) of columns 2 q2 and 2 q2 + 1: lane (hr, column mod 16),
+                // elements 4 rt .. 4 rt + 3 (rows 16 rt + 4 hr .. +3)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int c = 2 * q2 + u, J = c >> 4;
+                    uint32_t* pm = fm[bm] + (kd * NJ + J) * 256;
+                    const uint32_t sel = u ? 0x07060302u : 0x05040100u;
+                    *(uint2*)(pm + b16_chunk(hr, c & 15, J) * 4 + 2 * rt) =
+                        uint2{__builtin_amdgcn_perm(f[kd][1], f[kd][0], sel),
+                              __builtin_amdgcn_perm(f[kd][3], f[kd][2], sel)};
+                }
             }
         }
-        if (tid < STATS_ROWS) ls[buf][tid] = lv;
+        if (tid < STATS_ROWS) ls[be][tid] = lv;
+    };
+    // the pipeline's shared step: build tile it+1, load tile it+2
+    auto build_next = [&](int64_t it) {
+        if (it + 1 < ntile_rows) {
+            store((int)((it + 1) & 1), (int)((it + 1) % 3));
+            if (it + 2 < ntile_rows) load(it + 2);
+        }
     };
 
     if (ntile_rows > 0) {
         load(0);
-        store(0);
+        store(0, 0);
         if (ntile_rows > 1) load(1);
     }
     __syncthreads();
 
-    double* xw = xl[kq][hf];
-    const double* xo = xl[kq][hf ^ 1];
-    for (int64_t it = 0; it < ntile_rows; ++it) {
-        const int buf = (int)(it & 1);
-        // E-step over this wave's slices, two 16-row tiles
-        const uint16_t* F = fr[buf];
-        double lp[2][4];
+    if (ewave) {
+        // ---- E-wave: E-step, responsibilities and their parts for tile it
+        v4i qb[B16_PROD * DC];  // the K-tile's coefficient pieces (B operands), resident
+        {
+            const uint16_t* cp = coef + (int64_t)tile * (B16_TILE_BYTES / 2) + lane * 8;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) lp[rt][q] = 0.0;
-#pragma unroll
-        for (int jj = 0; jj < DCA; ++jj) {
-            if (jj < nj) {
-                const int j = j0 + jj;
-                v4i a[2][3];
+            for (int p = 0; p < B16_PROD * DC; ++p) qb[p] = *(const v4i*)(cp + p * 512);
+        }
+        const double cc = cvec[slot];
+        double n64 = 0.0;
+        for (int64_t it = 0; it <= ntile_rows; ++it) {
+            if (it < ntile_rows) {
+                const int be = (int)(it & 1);
+                const uint32_t* F = fe[be];
+                double la[2][4], lb[2][4];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int kd = 0; kd < 3; ++kd)
-                        a[rt][kd] = *(const v4i*)(F + (16 * rt + ci) * RS + kd * DQ + 32 * j + 8 * h);
-                f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+                    for (int q = 0; q < 4; ++q) {
+                        la[rt][q] = 0.0;
+                        lb[rt][q] = 0.0;
+                    }
 #pragma unroll
-                for (int mm = 0; mm < B16_PROD; ++mm)
+                for (int j = 0; j < DC; ++j) {
+                    v4i a[2][3];
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt)
-                        acc[rt] = mfma_bf16(a[rt][b16_kind(mm)], qb[jj * B16_PROD + mm], acc[rt]);
+#pragma unroll
+                        for (int kd = 0; kd < 3; ++kd)
+                            a[rt][kd] = *(const v4i*)(F + ((rt * 3 + kd) * DC + j) * 256 +
+                                                      b16_chunk(h, ci, j) * 4);
+                    f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+                    for (int mm = 0; mm < B16_PROD; ++mm)
+#pragma unroll
+                        for (int rt = 0; rt < 2; ++rt)
+                            acc[rt] = mfma_bf16(a[rt][b16_kind(mm)], qb[j * B16_PROD + mm], acc[rt]);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            if (j < DCA) la[rt][q] += (double)acc[rt][q];
+                            else lb[rt][q] += (double)acc[rt][q];
+                        }
+                }
+                // responsibilities of rows 16 rt + 4h + q (element 4 rt + q of
+                // the M-step's B operands), split into three bf16 parts
+                float rv[8];
+                bool any = false;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) lp[rt][q] += (double)acc[rt][q];
+                    for (int q = 0; q < 4; ++q) {
+                        // the exponent in fp64, then fp32 (|t| < 70 where r is kept)
+                        const float tf = (float)(((la[rt][q] + lb[rt][q]) + cc) -
+                                                 ls[be][16 * rt + 4 * h + q]);
+                        const float r = tf > -69.3147181f ? __builtin_amdgcn_exp2f(tf * 1.44269504f)
+                                                          : 0.0f;  // below about 2^-100: 0
+                        n64 += (double)r;
+                        any |= r != 0.0f;
+                        rv[4 * rt + q] = r;
+                    }
+                uint32_t* R = rr[be][kq];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    uint32_t ph[2], pm[2], pl[2];
+#pragma unroll
+                    for (int v = 0; v < 2; ++v)
+                        bf16_split3_pack(rv[4 * w + 2 * v], rv[4 * w + 2 * v + 1], ph[v], pm[v], pl[v]);
+                    *(uint2*)(R + lane * 4 + 2 * w) = uint2{ph[0], ph[1]};
+                    *(uint2*)(R + 256 + lane * 4 + 2 * w) = uint2{pm[0], pm[1]};
+                    *(uint2*)(R + 512 + lane * 4 + 2 * w) = uint2{pl[0], pl[1]};
+                }
+                const bool wany = __builtin_amdgcn_ballot_w64(any) != 0;
+                if (lane == 0) anyr[be][kq] = wany ? 1 : 0;
             }
+            build_next(it);
+            __syncthreads();
         }
-        // the two halves meet: l = (first half) + (second half)
+        // responsibility mass: lanes ci, ci+16, ci+32, ci+48 hold disjoint rows
+        n64 += shfl_xor_d(n64, 16);
+        n64 += shfl_xor_d(n64, 32);
+        if (h == 0) {
+            double* np = npart + (int64_t)g * ntiles * 16 + slot;
+            *np = (accumulate ? *np : 0.0) + n64;
+        }
+    } else {
+        // ---- M-wave: M-step of tile it - 1
+        double tA[NJ][4], tB[NJ][4];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) xw[(16 * rt + 4 * h + q) * XS + ci] = lp[rt][q];
-        __syncthreads();
-        // responsibilities of rows 16 rt + 4h + q, split into three bf16 parts
-        // (element 4 rt + q of the lane's B operands)
-        float rv[8];
-        bool any = false;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const double ov = xo[(16 * rt + 4 * h + q) * XS + ci];
-                const double l = hf == 0 ? lp[rt][q] + ov : ov + lp[rt][q];
-                // the exponent in fp64, then fp32 (|t| < 70 where r is kept)
-                const float tf = (float)((l + cc) - ls[buf][16 * rt + 4 * h + q]);
-                const float r = tf > -69.3147181f ? __builtin_amdgcn_exp2f(tf * 1.44269504f)
-                                                  : 0.0f;  // below about 2^-100: 0
-                n64 += (double)r;
-                any |= r != 0.0f;
-                rv[4 * rt + q] = r;
+                tA[j][q] = 0.0;
+                tB[j][q] = 0.0;
             }
-        v4i Rh, Rm, Rl;
+        for (int64_t it = 0; it <= ntile_rows; ++it) {
+            if (it >= 1) {
+                const int be = (int)((it - 1) & 1), bm = (int)((it - 1) % 3);
+                if (anyr[be][kq] != 0) {
+                    const uint32_t* R = rr[be][kq];
+                    const v4i Rh = *(const v4i*)(R + lane * 4);
+                    const v4i Rm = *(const v4i*)(R + 256 + lane * 4);
+                    const v4i Rl = *(const v4i*)(R + 512 + lane * 4);
+                    const uint32_t* M = fm[bm];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            uint32_t ph, pm, pl;
-            bf16_split3_pack(rv[2 * w], rv[2 * w + 1], ph, pm, pl);
-            Rh[w] = (int)ph;
-            Rm[w] = (int)pm;
-            Rl[w] = (int)pl;
-        }
-        // stage the next tile (its buffer was last read before the previous
-        // iteration's closing barrier)
-        if (it + 1 < ntile_rows) {
-            store(buf ^ 1);
-            if (it + 2 < ntile_rows) load(it + 2);
-        }
-        // M-step: C[column 16J + 4h + q][component ci] over the tile's 32 rows
-        if (__builtin_amdgcn_ballot_w64(any) != 0) {
-            const uint16_t* C = fc[buf];
-            auto col = [&](int c) -> v4i {
-                const uint2 lo = *(const uint2*)(C + c * CS + 4 * h);
-                const uint2 hi = *(const uint2*)(C + c * CS + 16 + 4 * h);
-                return v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-            };
+                    for (int J = 0; J < NJ; ++J) {
+                        const int co = b16_chunk(h, ci, J) * 4;
+                        const v4i fh = *(const v4i*)(M + J * 256 + co);
+                        const v4i fl = *(const v4i*)(M + (NJ + J) * 256 + co);
+                        const v4i fa = *(const v4i*)(M + (2 * NJ + J) * 256 + co);
+                        f32x4 sa = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        sa = mfma_bf16(fa, Rl, sa);
+                        sa = mfma_bf16(fa, Rm, sa);
+                        sa = mfma_bf16(fa, Rh, sa);
+                        sb = mfma_bf16(fl, Rm, sb);
+                        sb = mfma_bf16(fh, Rl, sb);
+                        sb = mfma_bf16(fl, Rh, sb);
+                        sb = mfma_bf16(fh, Rm, sb);
+                        sb = mfma_bf16(fh, Rh, sb);
 #pragma unroll
-            for (int JJ = 0; JJ < NJA; ++JJ) {
-                const int c0 = 16 * (J0 + JJ) + ci;
-                const v4i fh = col(c0), fl = col(DQ + c0), fa = col(2 * DQ + c0);
-                f32x4 sa = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                sa = mfma_bf16(fa, Rl, sa);
-                sa = mfma_bf16(fa, Rm, sa);
-                sa = mfma_bf16(fa, Rh, sa);
-                sb = mfma_bf16(fl, Rm, sb);
-                sb = mfma_bf16(fh, Rl, sb);
-                sb = mfma_bf16(fl, Rh, sb);
-                sb = mfma_bf16(fh, Rm, sb);
-                sb = mfma_bf16(fh, Rh, sb);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    tA[JJ][q] += (double)sa[q];
-                    tB[JJ][q] += (double)sb[q];
+                        for (int q = 0; q < 4; ++q) {
+                            tA[J][q] += (double)sa[q];
+                            tB[J][q] += (double)sb[q];
+                        }
+                    }
                 }
             }
+            build_next(it);
+            __syncthreads();
         }
-        __syncthreads();
-    }
-
-    // responsibility mass (both waves of a pair hold it; the first writes):
-    // lanes ci, ci+16, ci+32, ci+48 hold disjoint rows
-    n64 += shfl_xor_d(n64, 16);
-    n64 += shfl_xor_d(n64, 32);
-    const int64_t gbase = (int64_t)g * ntiles * 16;
-    if (h == 0 && hf == 0) {
-        double* np = npart + gbase + slot;
-        *np = (accumulate ? *np : 0.0) + n64;
-    }
-    double* pp = part + (gbase + slot) * (2 * (int64_t)dp);
+        double* pp = part + ((int64_t)g * ntiles * 16 + slot) * (2 * (int64_t)dp);
 #pragma unroll
-    for (int JJ = 0; JJ < NJA; ++JJ)
+        for (int J = 0; J < NJ; ++J)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int dd = 16 * (J0 + JJ) + 4 * h + q;
-            if (dd < dp) {
-                pp[dd] = (accumulate ? pp[dd] : 0.0) + tA[JJ][q];
-                pp[dp + dd] = (accumulate ? pp[dp + dd] : 0.0) + tB[JJ][q];
+            for (int q = 0; q < 4; ++q) {
+                const int dd = 16 * J + 4 * h + q;
+                if (dd < dp) {
+                    pp[dd] = (accumulate ? pp[dd] : 0.0) + tA[J][q];
+                    pp[dp + dd] = (accumulate ? pp[dp + dd] : 0.0) + tB[J][q];
+                }
             }
-        }
+    }
 }
 // ---------------------------------------------------------------------------
 // Launchers
