@@ -40,16 +40,16 @@ PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (the fp64 kernels
 PEAK_INT8_MFMA_TOPS = 5000.0   # MI355X dense INT8 matrix peak (the int8-slice kernels' dtype)
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak (the split-bf16 kernels' dtype)
 
-# HBM bytes per launch of the dominant kernel on the headline workload, from
-# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of this bench (profiles/
-# int8_passes_descriptor_n10M_d96_k1024_hbm.md), each scaled by what the
-# counter reads for a plain 3.84 GB device copy (FETCH_SIZE x2.0, WRITE_SIZE
-# x1.0). Keyed by a hash of the kernel sources: a changed kernel reports null
-# until it is profiled again.
+# HBM bytes per launch of the dominant kernel, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE runs of this bench (profiles/*_hbm.md), each
+# scaled by what the counter reads for a plain 3.84 GB device copy
+# (FETCH_SIZE x2.0, WRITE_SIZE x1.0). Keyed by a hash of the kernel sources,
+# then by workload: a changed kernel reports null until it is profiled again.
 MEASURED_TRAFFIC = {
-    "54e9df864cecdd62": {"workload": "descriptor",
-                         "kernel": "k_stats8x (pass 2: int8-slice E-step and M-step)",
-                         "bytes_per_launch": 1.3963e9},
+    "595c2b490ba31b8b": {
+        "bf16_large": {"kernel": "k_stats16 (pass 2: split-bf16 E-step and M-step)",
+                       "bytes_per_launch": 2.594e9},
+    },
 }
 
 
@@ -64,8 +64,8 @@ def _kernel_hash() -> str:
 
 
 def _traffic(workload: str, kernel: str):
-    rec = MEASURED_TRAFFIC.get(_kernel_hash())
-    if rec is None or rec["workload"] != workload or rec["kernel"] != kernel:
+    rec = MEASURED_TRAFFIC.get(_kernel_hash(), {}).get(workload)
+    if rec is None or rec["kernel"] != kernel:
         return None
     return rec["bytes_per_launch"]
 
