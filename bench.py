@@ -398,21 +398,35 @@ def _other_mode(args, W, x, xt, w0, m0, v0, ws, n_rows) -> int:
         return 1
     ms_step = start.elapsed_time(stop) / args.steps
     (ms1, n1), (ms2, n2) = prof["pass1"], prof["pass2"]
-    kname, kms, kn = ("k_wide normaliser + k_wmerge (pass 1)" if W.d > 128 else "k_lse (pass 1)"), ms1, n1
+    # the distance pass runs on int8 slices where the k-means distances are
+    # exact on them (the device reports it), else in fp64
+    int8 = args.mode == "kmeans" and ops.estep_arithmetic(ws, dev) == ops.GMM_ESTEP_INT8_SLICES
+    if W.d > 128:
+        p1name = "k_wide normaliser + k_wmerge (pass 1)"
+    elif int8:
+        p1name = "k_lse8 (pass 1, k-means mode: int8-slice distances)"
+    else:
+        p1name = "k_lse (pass 1)"
+    kname, kms, kn, on_p1 = p1name, ms1, n1, True
     if ms2 > ms1:
-        kname, kms, kn = "k_stats (pass 2, one-hot)", ms2, n2
-    flops_launch = 4.0 * W.d * W.k * n_rows / (kn / args.steps) if kname.endswith("(pass 1)") else None
+        kname, kms, kn, on_p1 = "k_stats (pass 2, one-hot)", ms2, n2, False
+    flops_launch = 4.0 * W.d * W.k * n_rows / (kn / args.steps) if on_p1 else None
     avg_ms = kms / kn
     achieved = flops_launch / (avg_ms * 1e-3) / 1e12 if flops_launch else None
+    peak = PEAK_INT8_MFMA_TOPS if (int8 and on_p1) else PEAK_FP64_MFMA_TFLOPS
     out = {
         "metric": metric, "value": round(1000.0 / ms_step, 4), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8+f64" if int8 else "f64",
         "data": "synthetic", "config": cfg,
         "roofline": {"kernel": kname, "bound": "mfma",
                      "achieved": round(achieved, 2) if achieved else None,
-                     "peak": PEAK_FP64_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP64_MFMA_TFLOPS, 4) if achieved else None,
+                     "peak": peak, "unit": "TFLOP/s",
+                     "peak_dtype": "int8 (dense, TOP/s)" if peak == PEAK_INT8_MFMA_TOPS else "fp64 (dense)",
+                     "frac": round(achieved / peak, 4) if achieved else None,
+                     "frac_of_fp64_mfma_peak": (round(achieved / PEAK_FP64_MFMA_TFLOPS, 4)
+                                                if achieved else None),
                      "traffic": None, "avg_launch_ms": round(avg_ms, 4),
                      "pass1_ms_per_step": round(ms1 / args.steps, 3),
                      "pass2_ms_per_step": round(ms2 / args.steps, 3)},

@@ -387,8 +387,11 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
                           workspace_bytes, &pl);
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
-    // weights and variances null: the k-means coefficients (2c, -1, -|c|^2)
+    // weights and variances null: the k-means coefficients (2c, -1, -|c|^2);
+    // the distances on int8 slices where they are exact, as for the EM step
     hipError_t e = launch_prologue(pl, nullptr, centroids, nullptr, st);
+    if (e == hipSuccess && !pl.wide)
+        e = launch_i8_prologue(pl, nullptr, centroids, nullptr, x, n, ldx, x_dtype, st);
     const size_t esz = x_dtype == GMM_BF16 ? 2 : 4;
     for (int64_t c0 = 0, ci = 0; e == hipSuccess && c0 < n; c0 += pl.chunk, ++ci) {
         const int64_t cn = n - c0 < pl.chunk ? n - c0 : pl.chunk;
@@ -397,8 +400,15 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
         // normaliser scratch (CHUNK_ROWS doubles hold CHUNK_ROWS int32)
         int32_t* zc = assign_dev ? assign_dev + c0 : (int32_t*)pl.lse;
         prof_mark(1, true, st);
-        e = pl.wide ? launch_wide_lse(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, 1, zc, nullptr, st, 1)
-                    : launch_lse(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, 1, zc, nullptr, st, 1);
+        if (pl.wide) {
+            e = launch_wide_lse(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, 1, zc, nullptr, st, 1);
+        } else {
+            // both variants; the mode flag lets one of them work
+            e = launch_lse8_km(pl, xc, cn, ldx, x_dtype, zc, ci > 0, st);
+            if (e == hipSuccess)
+                e = launch_lse(pl, xc, cn, ldx, x_dtype, nullptr, ci > 0, 1, zc, nullptr, st, 1,
+                               pl.status + I8S_MODE);
+        }
         prof_mark(1, false, st);
         if (e != hipSuccess) break;
         prof_mark(2, true, st);

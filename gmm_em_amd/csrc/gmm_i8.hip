@@ -265,12 +265,13 @@ __global__ __launch_bounds__(256) void k_i8_coef(const float* __restrict__ w, co
     // marked the int8 path inapplicable, and nothing is written
     if (L.nc > I8_MAX_NC) return;
     const int dph = dp >> 1;
+    // k-means mode (no variances): w = 2, so l = 2 b a - a^2 - |b|^2 = -|x - c|^2
+    const bool km = var == nullptr;
     // columns: 0 .. d-1 the a^2 coefficients (-w/2), d .. 2d-1 the a coefficients (w b)
     auto coef_u = [&](int col) -> double {
         const int dd = col < d ? col : col - d;
         const double s = shift[(dd & 1) * dph + (dd >> 1)];
-        const double v = (double)var[(int64_t)slot * d + dd];
-        const double iw = 1.0 / v;
+        const double iw = km ? 2.0 : 1.0 / (double)var[(int64_t)slot * d + dd];
         if (col < d) return ldexp(-0.5 * iw, plan[I8P_GB + dd]);
         return ldexp(iw * ((double)mu[(int64_t)slot * d + dd] - s), plan[I8P_GA + dd]);
     };
@@ -410,14 +411,15 @@ constexpr int L8_WAVES = 8;
 constexpr int L8_RT = 4;  // 16-row tiles per wave
 constexpr int L8_ROWS = L8_WAVES * L8_RT * 16;
 
-template <int NC, int LV, typename XT>
+template <int NC, int LV, typename XT, bool KM = false>
 __global__ __launch_bounds__(L8_WAVES * 64, 1)
 void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             const double* __restrict__ shift, const int* __restrict__ plan,
             const int8_t* __restrict__ coef8, const int* __restrict__ ek,
             const int* __restrict__ tinfo, const double* __restrict__ cvec, int ntiles,
             double* __restrict__ lse_out, double* __restrict__ llpart, int ll_accumulate,
-            int8_t* __restrict__ drows, const int* __restrict__ status) {
+            int8_t* __restrict__ drows, const int* __restrict__ status,
+            int32_t* __restrict__ z_out = nullptr, int k = 0) {
     constexpr int FLS = NC * 64 + 16;            // LDS stride of a packed row (conflict-free b128 reads)
     constexpr int TBL = LV * NC * 1024;          // bytes of one tile's level vectors
     constexpr int STG = L8_WAVES * 16 * FLS;     // staging of 16 rows per wave
@@ -434,7 +436,7 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
     const int ci = lane & 15, h = lane >> 4;
     const int64_t wrow = (int64_t)blockIdx.x * L8_ROWS + wave * (L8_RT * 16);
     const int dph = dp >> 1;
-    const bool hand_off = status[I8S_MODE2] != 0;
+    const bool hand_off = !KM && status[I8S_MODE2] != 0;
 
     // ---- pack the wave's rows: digits of a^2 and a, through LDS. Lane l
     // handles dims l and l + 64 (d <= 128) of 16 rows at a time, with the
@@ -515,14 +517,18 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
                 cr, (__attribute__((address_space(3))) void*)(cbuf[buf] + p * 1024), 16, lane * 16,
                 p * 1024, 0, 0);
     };
+    // normaliser mode: online logsumexp (m, s); k-means mode: the best value
+    // and its component (m, bi; the first in component order on ties)
     double m[L8_RT][4];
     float s[L8_RT][4];
+    int bi[L8_RT][4];
 #pragma unroll
     for (int rt = 0; rt < L8_RT; ++rt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            m[rt][q] = -1.0e300;
+            m[rt][q] = KM ? -INFINITY : -1.0e300;
             s[rt][q] = 0.0f;
+            bi[rt][q] = 0x7fffffff;
         }
     issue_tile(0, 0);
     // per-component scale exponent and constant of the next tile, loaded one
@@ -582,7 +588,16 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
 #pragma unroll
         for (int rt = 0; rt < L8_RT; ++rt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) lse_push(m[rt][q], s[rt][q], l[rt][q] + cc);
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (KM) {
+                    const double v = l[rt][q] + cc;
+                    const bool up = v > m[rt][q];
+                    m[rt][q] = up ? v : m[rt][q];
+                    bi[rt][q] = up ? t * 16 + ci : bi[rt][q];
+                } else {
+                    lse_push(m[rt][q], s[rt][q], l[rt][q] + cc);
+                }
+            }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t+1 have landed
         __syncthreads();                // ... and every wave's; tile t's buffer is free
     }
@@ -595,8 +610,15 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
 #pragma unroll 1
             for (int off = 1; off < 16; off <<= 1) {
                 const double m2 = shfl_xor_d(m[rt][q], off);
-                const float s2 = __shfl_xor(s[rt][q], off);
-                lse_merge(m[rt][q], s[rt][q], m2, s2);
+                if constexpr (KM) {
+                    const int i2 = __shfl_xor(bi[rt][q], off);
+                    const bool take = m2 > m[rt][q] || (m2 == m[rt][q] && i2 < bi[rt][q]);
+                    m[rt][q] = take ? m2 : m[rt][q];
+                    bi[rt][q] = take ? i2 : bi[rt][q];
+                } else {
+                    const float s2 = __shfl_xor(s[rt][q], off);
+                    lse_merge(m[rt][q], s[rt][q], m2, s2);
+                }
             }
         }
     if (ci == 0) {
@@ -608,8 +630,14 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
                 const int64_t row = (int64_t)blockIdx.x * L8_ROWS + lr;
                 double v = 0.0;
                 if (row < n) {
-                    v = m[rt][q] + log((double)s[rt][q]);
-                    if (lse_out) lse_out[row] = v;
+                    if constexpr (KM) {
+                        // the row's best value -|x - c_z|^2 (its share of -inertia)
+                        v = m[rt][q];
+                        z_out[row] = bi[rt][q] < k ? bi[rt][q] : -1;
+                    } else {
+                        v = m[rt][q] + log((double)s[rt][q]);
+                        if (lse_out) lse_out[row] = v;
+                    }
                 }
                 rowll[lr] = v;
             }
@@ -1190,24 +1218,25 @@ hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, c
                        pl.i8_dbl, pl.status);
     hipLaunchKernelGGL(k_i8_coef, dim3(pl.ntiles), dim3(256), 0, st, w, mu, var, pl.k, pl.d, pl.dp,
                        pl.shift, pl.i8_plan, pl.i8_dbl, pl.i8_coef, pl.i8_ek, pl.i8_tinfo, pl.status);
-    const bool b16 = dtype != 0 && pl.b16_coef != nullptr;
+    const bool b16 = dtype != 0 && pl.b16_coef != nullptr && var != nullptr;  // not for k-means
     if (b16) {
         const hipError_t e = launch_b16_coef(pl, w, mu, var, st);
         if (e != hipSuccess) return e;
     }
+    // (k-means, var == nullptr, has its own statistics pass: no int8 one)
     hipLaunchKernelGGL(k_i8_mode, dim3(1), dim3(64), 0, st, pl.status, pl.i8_plan, pl.d, pl.dp,
-                       pl.i8_stats ? 1 : 0, b16 ? 1 : 0, pl.shift);
+                       pl.i8_stats && var != nullptr ? 1 : 0, b16 ? 1 : 0, pl.shift);
     return hipGetLastError();
 }
 
-template <int NC, int LV, typename XT>
+template <int NC, int LV, typename XT, bool KM>
 static void launch_lse8_t(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
-                          int ll_acc, hipStream_t st) {
+                          int ll_acc, int32_t* z, hipStream_t st) {
     const int64_t blocks = (n + L8_ROWS - 1) / L8_ROWS;
-    hipLaunchKernelGGL((k_lse8<NC, LV, XT>), dim3((unsigned)blocks), dim3(L8_WAVES * 64), 0, st,
+    hipLaunchKernelGGL((k_lse8<NC, LV, XT, KM>), dim3((unsigned)blocks), dim3(L8_WAVES * 64), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.dp, pl.shift, pl.i8_plan, pl.i8_coef, pl.i8_ek,
                        pl.i8_tinfo, pl.cvec, pl.ntiles, lse_out, pl.llpart, ll_acc, pl.i8_rows,
-                       pl.status);
+                       pl.status, z, pl.k);
 }
 
 // Chunk counts a packed row can have at this dimension: ceil(dq t / 64) for
@@ -1225,13 +1254,13 @@ int i8_nc_for(int d) {
 
 // Every variant whose chunk count the plan can produce, for both level
 // counts; the plan's digit counts (on the device) let exactly one work.
-template <typename XT>
+template <typename XT, bool KM>
 static hipError_t launch_lse8_all(const Plan& pl, const void* x, int64_t n, int64_t ldx,
-                                  double* lse_out, int ll_acc, hipStream_t st) {
-#define VAR(NCV)                                                                    \
-    if (pl.i8_nc & (1 << NCV)) {                                                    \
-        launch_lse8_t<NCV, S8_LV, XT>(pl, x, n, ldx, lse_out, ll_acc, st);          \
-        launch_lse8_t<NCV, I8_MAX_LEV, XT>(pl, x, n, ldx, lse_out, ll_acc, st);     \
+                                  double* lse_out, int ll_acc, int32_t* z, hipStream_t st) {
+#define VAR(NCV)                                                                       \
+    if (pl.i8_nc & (1 << NCV)) {                                                       \
+        launch_lse8_t<NCV, S8_LV, XT, KM>(pl, x, n, ldx, lse_out, ll_acc, z, st);      \
+        launch_lse8_t<NCV, I8_MAX_LEV, XT, KM>(pl, x, n, ldx, lse_out, ll_acc, z, st); \
     }
     VAR(1) VAR(2) VAR(3) VAR(4) VAR(5) VAR(6)
 #undef VAR
@@ -1241,8 +1270,15 @@ static hipError_t launch_lse8_all(const Plan& pl, const void* x, int64_t n, int6
 hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                        double* lse_out, int ll_acc, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    return dtype == 0 ? launch_lse8_all<float>(pl, x, n, ldx, lse_out, ll_acc, st)
-                      : launch_lse8_all<uint16_t>(pl, x, n, ldx, lse_out, ll_acc, st);
+    return dtype == 0 ? launch_lse8_all<float, false>(pl, x, n, ldx, lse_out, ll_acc, nullptr, st)
+                      : launch_lse8_all<uint16_t, false>(pl, x, n, ldx, lse_out, ll_acc, nullptr, st);
+}
+
+hipError_t launch_lse8_km(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                          int32_t* z, int ll_acc, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    return dtype == 0 ? launch_lse8_all<float, true>(pl, x, n, ldx, nullptr, ll_acc, z, st)
+                      : launch_lse8_all<uint16_t, true>(pl, x, n, ldx, nullptr, ll_acc, z, st);
 }
 
 template <int DP, typename XT>

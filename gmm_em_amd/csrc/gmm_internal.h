@@ -138,6 +138,11 @@ hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, c
                               const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st);
 hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                        double* lse_out, int ll_acc, hipStream_t st);
+// k-means mode of the int8-slice pass 1 (after launch_i8_prologue with null
+// weights and variances): each row's nearest centroid into z and its
+// -|x - c_z|^2 into the partials, when status[I8S_MODE] == 1
+hipError_t launch_lse8_km(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
+                          int32_t* z, int ll_acc, hipStream_t st);
 // Split-bf16 path: coefficient pieces and the applicability check (run by
 // launch_i8_prologue for bf16 data), the normaliser pass (status[I8S_MODE] ==
 // MODE1_B16) and the statistics pass (status[I8S_MODE2] == MODE2_B16).

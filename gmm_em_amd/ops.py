@@ -239,8 +239,8 @@ def device_status(ws, device="cuda") -> int:
 
 
 def estep_arithmetic(ws, device="cuda") -> int:
-    """Synchronise; the gmm_estep_kind of the last EM step / log-likelihood call
-    on ``ws``: GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES (normaliser pass on exact
+    """Synchronise; the gmm_estep_kind of the last EM step / log-likelihood /
+    k-means call on ``ws``: GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES (normaliser pass on exact
     int8 slices), GMM_ESTEP_INT8_SLICES_BOTH (both passes) or
     GMM_ESTEP_INT8_SLICES_MSTEP (both passes, and the M-step too) or
     GMM_ESTEP_BF16_SPLIT (bf16 data: both passes on split bf16)."""

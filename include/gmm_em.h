@@ -182,7 +182,9 @@ int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
  * assign_dev (device, n int32, may be NULL) receives z. inertia_dev (device,
  * 1 double, may be NULL) receives sum_n |x_n - c_z[n]|^2 for the INPUT
  * centroids. The distances use the expanded form 2 a.b - a.a - b.b about a
- * per-dimension shift (exact up to fp64 rounding), so rows whose two nearest
+ * per-dimension shift, in fp64 or, where the data and centroids allow it (as
+ * for gmm_em_step: the int8 slices' error bound holds), on exact int8 slices
+ * (exact up to fp64 rounding either way), so rows whose two nearest
  * centroids are within rounding of each other may be assigned either one.
  * The workspace is the one for (d, k). n >= 1; d <= 768 (GMM_E_UNSUPPORTED
  * otherwise). A non-finite centroid is reported by gmm_device_status and
@@ -229,9 +231,11 @@ int gmm_kmeans_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_d
 int gmm_device_status(const void* workspace, void* stream);
 
 /* Synchronises the stream and returns the gmm_estep_kind of the E-step of the
- * last gmm_em_step / gmm_fit / gmm_loglik call that used this workspace
- * (GMM_ESTEP_FP64 for the other entry points and for rows wider than 128),
- * or -1 if the workspace is NULL or the synchronisation failed. */
+ * last gmm_em_step / gmm_fit / gmm_loglik call that used this workspace, or
+ * of the distance pass of the last gmm_kmeans_step / gmm_kmeans_fit call
+ * (GMM_ESTEP_INT8_SLICES when the distances ran on int8 slices;
+ * GMM_ESTEP_FP64 for gmm_assign_topm and for rows wider than 128), or -1 if
+ * the workspace is NULL or the synchronisation failed. */
 int gmm_estep_arithmetic(const void* workspace, void* stream);
 
 /* Static description of a status code. */

@@ -1,7 +1,8 @@
 """GPU parity of the k-means (Lloyd) mode against the oracle's Lloyd step.
 
-The GPU's distances use the expanded form about a per-dimension shift, the
-oracle's the direct sum of squared differences, both in fp64. Where the two
+The GPU's distances use the expanded form about a per-dimension shift, in
+fp64 or on exact int8 slices (integer-valued data), the oracle's the direct
+sum of squared differences in fp64. Where the two
 nearest centroids of a row are within rounding of each other the two sides
 may pick different ones; such a row is accepted when the GPU's choice is
 within the fp64 rounding bound of the best distance, and the clusters it
@@ -77,7 +78,7 @@ def _check_step(x, c_in, c_gpu, z_gpu, inertia_gpu, label, tol=1e-4):
     return worst, int(bad.size)
 
 
-def _run(ops, x, c0, steps, label, tol=1e-4):
+def _run(ops, x, c0, steps, label, tol=1e-4, path=None):
     xt = _xt(x)
     c = torch.from_numpy(np.ascontiguousarray(c0, dtype=np.float32)).to(DEV)
     ws = ops.workspace(x.shape[1], len(c0), DEV)
@@ -89,6 +90,9 @@ def _run(ops, x, c0, steps, label, tol=1e-4):
         I = inertia.item()
         worst, nbad = _check_step(x, c_in, c.cpu().numpy(), z.cpu().numpy(), I, f"{label} step {t}", tol)
         print(f"{label} step {t}: centroid err {worst:.2e}, tie rows {nbad}, inertia {I:.6e}")
+        if path is not None:  # which distance arithmetic the device chose
+            got = ops.estep_arithmetic(ws, DEV)
+            assert got == path, f"{label} step {t}: distance arithmetic {got}, expected {path}"
         # Lloyd never increases the inertia (up to the fp32 rounding of c)
         assert I <= prev * (1 + 1e-7) + 1e-9
         prev = I
@@ -104,7 +108,20 @@ def test_kmeans_per_step_ragged(ops, n, d, k, seed):
     x, _, _ = dg.custom(n, d, k, seed=seed)
     rng = np.random.default_rng(seed)
     c0 = x[rng.choice(n, k, replace=False)].astype(np.float32)
-    _run(ops, x, c0, 4, f"kmeans n={n} d={d} k={k}")
+    # real-valued data: the distances run in fp64
+    _run(ops, x, c0, 4, f"kmeans n={n} d={d} k={k}", path=ops.GMM_ESTEP_FP64)
+
+
+@pytest.mark.parametrize("n,d,k,seed", [(1000, 16, 8, 11), (4999, 96, 100, 12), (3000, 37, 130, 13),
+                                         (9000, 128, 50, 14), (777, 5, 300, 15)])
+def test_kmeans_int8_integer_data(ops, n, d, k, seed):
+    # integer-valued data in [0, 120] (one digit for a, two for a^2): the
+    # distances run on exact int8 slices, the same shapes as above
+    x, _, _ = dg.custom(n, d, k, seed=seed)
+    x = np.clip(np.rint(x * 8.0 + 40.0), 0, 120).astype(np.float32)
+    rng = np.random.default_rng(seed)
+    c0 = x[rng.choice(n, k, replace=False)].astype(np.float32)
+    _run(ops, x, c0, 4, f"kmeans int8 n={n} d={d} k={k}", path=ops.GMM_ESTEP_INT8_SLICES)
 
 
 def test_kmeans_bf16_per_step(ops):
@@ -163,7 +180,7 @@ def test_kmeans_descriptor_prefix_per_step(ops):
     W = dg.WORKLOADS["descriptor"]
     x = dg.rows(W, 60_000)
     _, m0, _ = dg.init_params(W, x)
-    _run(ops, x, m0, 2, "kmeans descriptor prefix")
+    _run(ops, x, m0, 2, "kmeans descriptor prefix", path=ops.GMM_ESTEP_INT8_SLICES)
 
 
 def test_kmeans_descriptor_full_size(ops):
@@ -177,8 +194,10 @@ def test_kmeans_descriptor_full_size(ops):
     _, m0, _ = dg.init_params(W, x)
     xt = _xt(x)
     c = torch.from_numpy(m0.copy()).to(DEV)
-    inertia, z = ops.kmeans_step(xt, c)
+    ws = ops.workspace(W.d, W.k, DEV)
+    inertia, z = ops.kmeans_step(xt, c, ws=ws)
     torch.cuda.synchronize()
+    assert ops.estep_arithmetic(ws, DEV) == ops.GMM_ESTEP_INT8_SLICES
     zg, cg, I = z.cpu().numpy(), c.cpu().numpy(), inertia.item()
     del xt
     rng = np.random.default_rng(77)
