@@ -62,6 +62,7 @@ def _fit_gpu(ops, x, w0, m0, v0, floor, iters, tol=0.0):
     hist, done = ops.fit(xt, w, mu, var, floor, iters, tol, ws=ws)
     torch.cuda.synchronize()
     assert ops.device_status(ws, DEV) == ops.GMM_OK
+    _fit_gpu.last_arith = ops.estep_arithmetic(ws, DEV)  # the last iteration's arithmetic
     return hist.cpu().numpy(), done, (w, mu, var), xt
 
 
@@ -116,7 +117,7 @@ def _golden(case):
     return np.load(p, allow_pickle=False)
 
 
-def _golden_compare(ops, case, tol):
+def _golden_compare(ops, case, tol, path=None):
     g = _golden(case)
     W = dg.WORKLOADS[str(g["workload"])]
     n, iters = int(g["n"]), int(g["iters"])
@@ -125,6 +126,8 @@ def _golden_compare(ops, case, tol):
     print(f"# {case} prefix: N={n} D={W.d} K={W.k} {iters} iterations", flush=True)
     h, done, th, xt = _fit_gpu(ops, x, w0, m0, v0, W.var_floor, iters)
     assert done == iters
+    if path is not None:
+        assert _fit_gpu.last_arith == path, (case, _fit_gpu.last_arith, path)
     eh = np.abs(h - g["hist"]) / np.abs(g["hist"])
     assert np.all(eh <= 1e-5), (case, h, g["hist"])
     gw, gmu, gv = _host(*th)
@@ -144,8 +147,10 @@ def _golden_compare(ops, case, tol):
 
 
 def test_bf16_large_prefix_end_to_end(ops):
-    # bf16 data: the 5e-3 bar for the parameters, 1e-5 for the log-likelihood
-    _golden_compare(ops, "bf16_large", 5e-3)
+    # bf16 data: the 5e-3 bar for the parameters, 1e-5 for the log-likelihood;
+    # on the split-bf16 path (checked for the last iteration, whose narrower
+    # components make its selection check the strictest)
+    _golden_compare(ops, "bf16_large", 5e-3, path=ops.GMM_ESTEP_BF16_SPLIT)
 
 
 def test_wide_prefix_end_to_end_and_top2(ops):
