@@ -398,13 +398,14 @@ def _other_mode(args, W, x, xt, w0, m0, v0, ws, n_rows) -> int:
         return 1
     ms_step = start.elapsed_time(stop) / args.steps
     (ms1, n1), (ms2, n2) = prof["pass1"], prof["pass2"]
-    # the distance pass runs on int8 slices where the k-means distances are
+    # the distance / log-density pass runs on int8 slices where they are
     # exact on them (the device reports it), else in fp64
-    int8 = args.mode == "kmeans" and ops.estep_arithmetic(ws, dev) == ops.GMM_ESTEP_INT8_SLICES
+    int8 = ops.estep_arithmetic(ws, dev) == ops.GMM_ESTEP_INT8_SLICES
     if W.d > 128:
         p1name = "k_wide normaliser + k_wmerge (pass 1)"
     elif int8:
-        p1name = "k_lse8 (pass 1, k-means mode: int8-slice distances)"
+        p1name = ("k_lse8 (pass 1, k-means mode: int8-slice distances)" if args.mode == "kmeans"
+                  else "k_lse8 (pass 1, top-2 mode: int8-slice log-densities)")
     else:
         p1name = "k_lse (pass 1)"
     kname, kms, kn, on_p1 = p1name, ms1, n1, True

@@ -187,9 +187,13 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
         } else if (i8) {
             // every variant is launched; the mode flag the prologue wrote
             // lets exactly one of them do the work
-            e = launch_lse8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
-            if (e == hipSuccess && dtype == GMM_BF16)
-                e = launch_lse16(pl, xc, cn, ldx, lse, ci > 0, st);
+            if (m > 0) {  // top-m lists (fp32 rows)
+                e = launch_lse8_topm(pl, xc, cn, ldx, lse, ci > 0, m, ic, rc, st);
+            } else {
+                e = launch_lse8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
+                if (e == hipSuccess && dtype == GMM_BF16)
+                    e = launch_lse16(pl, xc, cn, ldx, lse, ci > 0, st);
+            }
             if (e == hipSuccess)
                 e = launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st, 0,
                                pl.status + I8S_MODE);
@@ -373,7 +377,13 @@ int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_prologue(pl, weights, means, variances, st);
-    if (e == hipSuccess) e = run_passes(pl, x, n, ldx, x_dtype, false, st, m, idx_dev, resp_dev);
+    // the int8-slice pass with top-m lists serves fp32 rows up to 128 dims
+    // (where its error bound holds; the fp64 pass otherwise)
+    const bool i8 = !pl.wide && x_dtype == GMM_F32;
+    if (e == hipSuccess && i8)
+        e = launch_i8_prologue(pl, weights, means, variances, x, n, ldx, x_dtype, st, false);
+    if (e == hipSuccess)
+        e = run_passes(pl, x, n, ldx, x_dtype, false, st, m, idx_dev, resp_dev, nullptr, i8);
     return hip_status(e);
 }
 
@@ -391,7 +401,7 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
     // the distances on int8 slices where they are exact, as for the EM step
     hipError_t e = launch_prologue(pl, nullptr, centroids, nullptr, st);
     if (e == hipSuccess && !pl.wide)
-        e = launch_i8_prologue(pl, nullptr, centroids, nullptr, x, n, ldx, x_dtype, st);
+        e = launch_i8_prologue(pl, nullptr, centroids, nullptr, x, n, ldx, x_dtype, st, false);
     const size_t esz = x_dtype == GMM_BF16 ? 2 : 4;
     for (int64_t c0 = 0, ci = 0; e == hipSuccess && c0 < n; c0 += pl.chunk, ++ci) {
         const int64_t cn = n - c0 < pl.chunk ? n - c0 : pl.chunk;

@@ -406,12 +406,16 @@ __device__ __forceinline__ void fold_pair(double& l, int a, int b, double sc) {
 // int32 accumulator per row tile, folded into fp64 (l += acc * 2^(E_k - 7L));
 // the finished tile's values go into the online logsumexp (fp64 running
 // maximum, fp32 scaled sum). Levels past a tile's count have zero digits.
+// MODE selects what the kernel keeps per row: 0 the normaliser; 1 (k-means)
+// the best value and its component instead; 2 or 4 the normaliser and the
+// top-2 or top-4 components (soft assignment), with 32 rows per wave (two
+// row tiles) so that the candidate lists fit the registers of two waves per
+// SIMD.
 // ---------------------------------------------------------------------------
 constexpr int L8_WAVES = 8;
 constexpr int L8_RT = 4;  // 16-row tiles per wave
-constexpr int L8_ROWS = L8_WAVES * L8_RT * 16;
 
-template <int NC, int LV, typename XT, bool KM = false>
+template <int NC, int LV, typename XT, int MODE = 0>
 __global__ __launch_bounds__(L8_WAVES * 64, 1)
 void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             const double* __restrict__ shift, const int* __restrict__ plan,
@@ -419,13 +423,20 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             const int* __restrict__ tinfo, const double* __restrict__ cvec, int ntiles,
             double* __restrict__ lse_out, double* __restrict__ llpart, int ll_accumulate,
             int8_t* __restrict__ drows, const int* __restrict__ status,
-            int32_t* __restrict__ z_out = nullptr, int k = 0) {
+            int32_t* __restrict__ z_out = nullptr, int k = 0, int m_out = 0,
+            float* __restrict__ resp_out = nullptr) {
+    constexpr bool KM = MODE == 1;
+    constexpr int TM = MODE >= 2 ? MODE : 0;  // candidates kept per row
+    constexpr int TMA = TM > 0 ? TM : 1;
+    constexpr int RT = TM > 0 ? 2 : L8_RT;   // 16-row tiles per wave
+    constexpr int ROWS = L8_WAVES * RT * 16;
+    static_assert(ROWS % LL_ROWS == 0, "whole log-likelihood partials per block");
     constexpr int FLS = NC * 64 + 16;            // LDS stride of a packed row (conflict-free b128 reads)
     constexpr int TBL = LV * NC * 1024;          // bytes of one tile's level vectors
     constexpr int STG = L8_WAVES * 16 * FLS;     // staging of 16 rows per wave
     constexpr int TB = TBL > STG ? TBL : STG;
     __shared__ __attribute__((aligned(16))) int8_t cbuf[2][TB];
-    __shared__ double rowll[L8_ROWS];
+    __shared__ double rowll[ROWS];
     if (status[I8S_MODE] != 1) return;  // the fp64 kernels run instead
     const I8Layout LY = i8_layout(plan, d);
     const int maxlev = status[I8S_MAXLEV];
@@ -434,15 +445,15 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ci = lane & 15, h = lane >> 4;
-    const int64_t wrow = (int64_t)blockIdx.x * L8_ROWS + wave * (L8_RT * 16);
+    const int64_t wrow = (int64_t)blockIdx.x * ROWS + wave * (RT * 16);
     const int dph = dp >> 1;
-    const bool hand_off = !KM && status[I8S_MODE2] != 0;
+    const bool hand_off = MODE == 0 && status[I8S_MODE2] != 0;
 
     // ---- pack the wave's rows: digits of a^2 and a, through LDS. Lane l
     // handles dims l and l + 64 (d <= 128) of 16 rows at a time, with the
     // per-dimension shift and scales loaded once and the 32 values of a
     // 16-row tile loaded together.
-    v4i A[L8_RT][NC];
+    v4i A[RT][NC];
     {
         int8_t* stg = &cbuf[1][wave * 16 * FLS];
         double sh[2], ga[2], gb[2];
@@ -455,7 +466,7 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             gb[u] = live ? ldexp(1.0, -plan[I8P_GB + dd]) : 0.0;
         }
 #pragma unroll
-        for (int rt = 0; rt < L8_RT; ++rt) {  // unrolled: A stays in registers
+        for (int rt = 0; rt < RT; ++rt) {  // unrolled: A stays in registers
             float xv[16][2];
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -519,16 +530,23 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
     };
     // normaliser mode: online logsumexp (m, s); k-means mode: the best value
     // and its component (m, bi; the first in component order on ties)
-    double m[L8_RT][4];
-    float s[L8_RT][4];
-    int bi[L8_RT][4];
+    double m[RT][4];
+    float s[RT][4];
+    int bi[RT][4];
+    double tv[RT][4][TMA];  // top-m candidates (value, component), best first
+    int ti[RT][4][TMA];
 #pragma unroll
-    for (int rt = 0; rt < L8_RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             m[rt][q] = KM ? -INFINITY : -1.0e300;
             s[rt][q] = 0.0f;
             bi[rt][q] = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < TMA; ++j) {
+                tv[rt][q][j] = -INFINITY;
+                ti[rt][q][j] = 0x7fffffff;
+            }
         }
     issue_tile(0, 0);
     // per-component scale exponent and constant of the next tile, loaded one
@@ -549,9 +567,9 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             ccn = cvec[(t + 1) * 16 + ci];
             nln = tinfo[(t + 1) * I8_TINFO];
         }
-        double l[L8_RT][4];
+        double l[RT][4];
 #pragma unroll
-        for (int rt = 0; rt < L8_RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) l[rt][q] = 0.0;
         const int8_t* cb = cbuf[buf] + lane * 16;
@@ -559,9 +577,9 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
 #pragma unroll
         for (int lev = 0; lev < LV; lev += 2) {
             if (lev >= nl) break;  // the tile's remaining levels are zero
-            v4i acc0[L8_RT], acc1[L8_RT];
+            v4i acc0[RT], acc1[RT];
 #pragma unroll
-            for (int rt = 0; rt < L8_RT; ++rt) {
+            for (int rt = 0; rt < RT; ++rt) {
                 acc0[rt] = v4i{0, 0, 0, 0};
                 acc1[rt] = v4i{0, 0, 0, 0};
             }
@@ -569,15 +587,15 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             for (int c = 0; c < NC; ++c) {
                 const v4i b0 = *(const v4i*)(cb + (lev * NC + c) * 1024);
 #pragma unroll
-                for (int rt = 0; rt < L8_RT; ++rt) acc0[rt] = mfma_i8(A[rt][c], b0, acc0[rt]);
+                for (int rt = 0; rt < RT; ++rt) acc0[rt] = mfma_i8(A[rt][c], b0, acc0[rt]);
                 if (lev + 1 < LV) {
                     const v4i b1 = *(const v4i*)(cb + ((lev + 1 < LV ? lev + 1 : lev) * NC + c) * 1024);
 #pragma unroll
-                    for (int rt = 0; rt < L8_RT; ++rt) acc1[rt] = mfma_i8(A[rt][c], b1, acc1[rt]);
+                    for (int rt = 0; rt < RT; ++rt) acc1[rt] = mfma_i8(A[rt][c], b1, acc1[rt]);
                 }
             }
 #pragma unroll
-            for (int rt = 0; rt < L8_RT; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) fold_pair(l[rt][q], acc0[rt][q], acc1[rt][q], sc);
             sc *= 1.0 / 16384.0;
@@ -586,7 +604,7 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int rt = 0; rt < L8_RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if constexpr (KM) {
@@ -596,6 +614,8 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
                     bi[rt][q] = up ? t * 16 + ci : bi[rt][q];
                 } else {
                     lse_push(m[rt][q], s[rt][q], l[rt][q] + cc);
+                    // components arrive in increasing order along the lane
+                    if constexpr (TM > 0) top_push_inc<TM>(tv[rt][q], ti[rt][q], l[rt][q] + cc, t * 16 + ci);
                 }
             }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t+1 have landed
@@ -604,7 +624,7 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
 
     // ---- merge the 16 lanes holding the same rows (fixed butterfly order)
 #pragma unroll
-    for (int rt = 0; rt < L8_RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll 1
@@ -618,16 +638,17 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
                 } else {
                     const float s2 = __shfl_xor(s[rt][q], off);
                     lse_merge(m[rt][q], s[rt][q], m2, s2);
+                    if constexpr (TM > 0) top_merge<TM>(tv[rt][q], ti[rt][q], off);
                 }
             }
         }
     if (ci == 0) {
 #pragma unroll
-        for (int rt = 0; rt < L8_RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int lr = wave * (L8_RT * 16) + rt * 16 + 4 * h + q;
-                const int64_t row = (int64_t)blockIdx.x * L8_ROWS + lr;
+                const int lr = wave * (RT * 16) + rt * 16 + 4 * h + q;
+                const int64_t row = (int64_t)blockIdx.x * ROWS + lr;
                 double v = 0.0;
                 if (row < n) {
                     if constexpr (KM) {
@@ -637,19 +658,29 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
                     } else {
                         v = m[rt][q] + log((double)s[rt][q]);
                         if (lse_out) lse_out[row] = v;
+                        if constexpr (TM > 0) {
+#pragma unroll
+                            for (int j = 0; j < TM; ++j) {  // (static indices: the lists stay in registers)
+                                if (j >= m_out) continue;
+                                const int sl = ti[rt][q][j];
+                                z_out[row * m_out + j] = sl < k ? sl : -1;
+                                if (resp_out) resp_out[row * m_out + j] = __expf((float)(tv[rt][q][j] - v));
+                            }
+                        }
                     }
                 }
                 rowll[lr] = v;
             }
     }
     __syncthreads();
-    // one partial per 64 rows: wave w sums its own rows (fixed order)
-    {
-        double tot = rowll[wave * 64 + lane];
+    // one partial per 64 rows: wave w < ROWS / 64 sums rows 64w .. 64w + 63
+    // (its own rows at 64 rows per wave; fixed order)
+    if (wave < ROWS / LL_ROWS) {
+        double tot = rowll[wave * LL_ROWS + lane];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) tot += shfl_xor_d(tot, off);
-        const int64_t pi = (int64_t)blockIdx.x * (L8_ROWS / LL_ROWS) + wave;
-        if (lane == 0 && wrow < n) llpart[pi] = (ll_accumulate ? llpart[pi] : 0.0) + tot;
+        const int64_t pi = (int64_t)blockIdx.x * (ROWS / LL_ROWS) + wave;
+        if (lane == 0 && pi * LL_ROWS < n) llpart[pi] = (ll_accumulate ? llpart[pi] : 0.0) + tot;
     }
 }
 
@@ -1199,7 +1230,8 @@ void k_stats8x(const int8_t* __restrict__ drows, int64_t n, int d,
 // Host-side launchers.
 // ---------------------------------------------------------------------------
 hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
-                              const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st) {
+                              const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st,
+                              bool em_stats) {
     hipLaunchKernelGGL(k_i8_reset, dim3(1), dim3(128), 0, st, pl.i8_amax, pl.i8_lsb, pl.b16_amax,
                        pl.b16_lsb, pl.dp);
     if (n > 0) {
@@ -1218,25 +1250,27 @@ hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, c
                        pl.i8_dbl, pl.status);
     hipLaunchKernelGGL(k_i8_coef, dim3(pl.ntiles), dim3(256), 0, st, w, mu, var, pl.k, pl.d, pl.dp,
                        pl.shift, pl.i8_plan, pl.i8_dbl, pl.i8_coef, pl.i8_ek, pl.i8_tinfo, pl.status);
-    const bool b16 = dtype != 0 && pl.b16_coef != nullptr && var != nullptr;  // not for k-means
+    const bool b16 = dtype != 0 && pl.b16_coef != nullptr && var != nullptr && em_stats;
     if (b16) {
         const hipError_t e = launch_b16_coef(pl, w, mu, var, st);
         if (e != hipSuccess) return e;
     }
-    // (k-means, var == nullptr, has its own statistics pass: no int8 one)
+    // (only an EM step runs a statistics pass on these kernels: k-means has its
+    // own, the top-m assignment none)
     hipLaunchKernelGGL(k_i8_mode, dim3(1), dim3(64), 0, st, pl.status, pl.i8_plan, pl.d, pl.dp,
-                       pl.i8_stats && var != nullptr ? 1 : 0, b16 ? 1 : 0, pl.shift);
+                       pl.i8_stats && em_stats ? 1 : 0, b16 ? 1 : 0, pl.shift);
     return hipGetLastError();
 }
 
-template <int NC, int LV, typename XT, bool KM>
+template <int NC, int LV, typename XT, int MODE>
 static void launch_lse8_t(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
-                          int ll_acc, int32_t* z, hipStream_t st) {
-    const int64_t blocks = (n + L8_ROWS - 1) / L8_ROWS;
-    hipLaunchKernelGGL((k_lse8<NC, LV, XT, KM>), dim3((unsigned)blocks), dim3(L8_WAVES * 64), 0, st,
+                          int ll_acc, int32_t* z, int m, float* resp, hipStream_t st) {
+    const int rows = L8_WAVES * (MODE >= 2 ? 2 : L8_RT) * 16;
+    const int64_t blocks = (n + rows - 1) / rows;
+    hipLaunchKernelGGL((k_lse8<NC, LV, XT, MODE>), dim3((unsigned)blocks), dim3(L8_WAVES * 64), 0, st,
                        (const XT*)x, n, pl.d, ldx, pl.dp, pl.shift, pl.i8_plan, pl.i8_coef, pl.i8_ek,
                        pl.i8_tinfo, pl.cvec, pl.ntiles, lse_out, pl.llpart, ll_acc, pl.i8_rows,
-                       pl.status, z, pl.k);
+                       pl.status, z, pl.k, m, resp);
 }
 
 // Chunk counts a packed row can have at this dimension: ceil(dq t / 64) for
@@ -1254,13 +1288,14 @@ int i8_nc_for(int d) {
 
 // Every variant whose chunk count the plan can produce, for both level
 // counts; the plan's digit counts (on the device) let exactly one work.
-template <typename XT, bool KM>
+template <typename XT, int MODE>
 static hipError_t launch_lse8_all(const Plan& pl, const void* x, int64_t n, int64_t ldx,
-                                  double* lse_out, int ll_acc, int32_t* z, hipStream_t st) {
-#define VAR(NCV)                                                                       \
-    if (pl.i8_nc & (1 << NCV)) {                                                       \
-        launch_lse8_t<NCV, S8_LV, XT, KM>(pl, x, n, ldx, lse_out, ll_acc, z, st);      \
-        launch_lse8_t<NCV, I8_MAX_LEV, XT, KM>(pl, x, n, ldx, lse_out, ll_acc, z, st); \
+                                  double* lse_out, int ll_acc, int32_t* z, int m, float* resp,
+                                  hipStream_t st) {
+#define VAR(NCV)                                                                                  \
+    if (pl.i8_nc & (1 << NCV)) {                                                                  \
+        launch_lse8_t<NCV, S8_LV, XT, MODE>(pl, x, n, ldx, lse_out, ll_acc, z, m, resp, st);      \
+        launch_lse8_t<NCV, I8_MAX_LEV, XT, MODE>(pl, x, n, ldx, lse_out, ll_acc, z, m, resp, st); \
     }
     VAR(1) VAR(2) VAR(3) VAR(4) VAR(5) VAR(6)
 #undef VAR
@@ -1270,15 +1305,23 @@ static hipError_t launch_lse8_all(const Plan& pl, const void* x, int64_t n, int6
 hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                        double* lse_out, int ll_acc, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    return dtype == 0 ? launch_lse8_all<float, false>(pl, x, n, ldx, lse_out, ll_acc, nullptr, st)
-                      : launch_lse8_all<uint16_t, false>(pl, x, n, ldx, lse_out, ll_acc, nullptr, st);
+    return dtype == 0 ? launch_lse8_all<float, 0>(pl, x, n, ldx, lse_out, ll_acc, nullptr, 0, nullptr, st)
+                      : launch_lse8_all<uint16_t, 0>(pl, x, n, ldx, lse_out, ll_acc, nullptr, 0, nullptr, st);
 }
 
 hipError_t launch_lse8_km(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                           int32_t* z, int ll_acc, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    return dtype == 0 ? launch_lse8_all<float, true>(pl, x, n, ldx, nullptr, ll_acc, z, st)
-                      : launch_lse8_all<uint16_t, true>(pl, x, n, ldx, nullptr, ll_acc, z, st);
+    return dtype == 0 ? launch_lse8_all<float, 1>(pl, x, n, ldx, nullptr, ll_acc, z, 0, nullptr, st)
+                      : launch_lse8_all<uint16_t, 1>(pl, x, n, ldx, nullptr, ll_acc, z, 0, nullptr, st);
+}
+
+// top-m mode (m <= 4): fp32 data only (the caller runs the fp64 pass for bf16)
+hipError_t launch_lse8_topm(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
+                            int ll_acc, int m, int32_t* idx, float* resp, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    return m <= 2 ? launch_lse8_all<float, 2>(pl, x, n, ldx, lse_out, ll_acc, idx, m, resp, st)
+                  : launch_lse8_all<float, 4>(pl, x, n, ldx, lse_out, ll_acc, idx, m, resp, st);
 }
 
 template <int DP, typename XT>

@@ -134,8 +134,11 @@ hipError_t launch_lse(const Plan& pl, const void* x, int64_t n, int64_t ldx, int
                       hipStream_t st, int km = 0, const int* skip = nullptr);
 // int8-slice E-step: data pass, digit plan and coefficient digits, then the
 // mode flag (status[I8S_MODE]) that selects the int8 or the fp64 pass 1.
+// em_stats: the call is an EM step or log-likelihood (the int8 and split-bf16
+// statistics / normaliser variants may be selected), not k-means or top-m.
 hipError_t launch_i8_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
-                              const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st);
+                              const void* x, int64_t n, int64_t ldx, int dtype, hipStream_t st,
+                              bool em_stats = true);
 hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                        double* lse_out, int ll_acc, hipStream_t st);
 // k-means mode of the int8-slice pass 1 (after launch_i8_prologue with null
@@ -143,6 +146,10 @@ hipError_t launch_lse8(const Plan& pl, const void* x, int64_t n, int64_t ldx, in
 // -|x - c_z|^2 into the partials, when status[I8S_MODE] == 1
 hipError_t launch_lse8_km(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                           int32_t* z, int ll_acc, hipStream_t st);
+// top-m mode of the int8-slice pass 1 for fp32 data (m <= 4): the normalisers
+// and each row's m most responsible components (idx, resp), as launch_lse
+hipError_t launch_lse8_topm(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
+                            int ll_acc, int m, int32_t* idx, float* resp, hipStream_t st);
 // Split-bf16 path: coefficient pieces and the applicability check (run by
 // launch_i8_prologue for bf16 data), the normaliser pass (status[I8S_MODE] ==
 // MODE1_B16) and the statistics pass (status[I8S_MODE2] == MODE2_B16).

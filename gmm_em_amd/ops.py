@@ -50,6 +50,7 @@ for _f in (lib.gmm_em_step, lib.gmm_fit, lib.gmm_loglik, lib.gmm_assign_topm, li
 
 (GMM_OK, GMM_E_INVALID, GMM_E_DTYPE, GMM_E_WORKSPACE, GMM_E_PARAMS, GMM_E_HIP,
  GMM_E_UNSUPPORTED) = range(7)
+GMM_F32, GMM_BF16 = 0, 1  # gmm_dtype
 
 
 class GmmError(RuntimeError):
@@ -87,9 +88,9 @@ def _data(x: torch.Tensor):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D tensor with unit stride along columns")
     if x.dtype == torch.float32:
-        dt = 0
+        dt = GMM_F32
     elif x.dtype == torch.bfloat16:
-        dt = 1
+        dt = GMM_BF16
     else:
         raise TypeError("x must be float32 or bfloat16")
     if not x.is_cuda:
@@ -240,7 +241,7 @@ def device_status(ws, device="cuda") -> int:
 
 def estep_arithmetic(ws, device="cuda") -> int:
     """Synchronise; the gmm_estep_kind of the last EM step / log-likelihood /
-    k-means call on ``ws``: GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES (normaliser pass on exact
+    k-means / top-m assignment call on ``ws``: GMM_ESTEP_FP64, GMM_ESTEP_INT8_SLICES (normaliser pass on exact
     int8 slices), GMM_ESTEP_INT8_SLICES_BOTH (both passes) or
     GMM_ESTEP_INT8_SLICES_MSTEP (both passes, and the M-step too) or
     GMM_ESTEP_BF16_SPLIT (bf16 data: both passes on split bf16)."""

@@ -164,6 +164,8 @@ int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype
  * row, most responsible first (ties: smaller component index first), with
  * their responsibilities r[n][k]. idx_dev (device, n*m int32) and resp_dev
  * (device, n*m floats) are row-major n x m. 1 <= m <= min(k, 4). n may be 0.
+ * The log-densities run on int8 slices for fp32 rows where gmm_em_step's
+ * conditions for them hold, else in fp64 (bf16 rows: fp64).
  * Parameter errors are reported by gmm_device_status; the outputs are then
  * unspecified. */
 int gmm_assign_topm(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype,
@@ -230,12 +232,13 @@ int gmm_kmeans_fit(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_d
  * GMM_E_HIP if the synchronisation failed. */
 int gmm_device_status(const void* workspace, void* stream);
 
-/* Synchronises the stream and returns the gmm_estep_kind of the E-step of the
- * last gmm_em_step / gmm_fit / gmm_loglik call that used this workspace, or
- * of the distance pass of the last gmm_kmeans_step / gmm_kmeans_fit call
- * (GMM_ESTEP_INT8_SLICES when the distances ran on int8 slices;
- * GMM_ESTEP_FP64 for gmm_assign_topm and for rows wider than 128), or -1 if
- * the workspace is NULL or the synchronisation failed. */
+/* Synchronises the stream and returns the gmm_estep_kind of the last call
+ * that used this workspace: of the E-step of gmm_em_step / gmm_fit /
+ * gmm_loglik, of the distance pass of gmm_kmeans_step / gmm_kmeans_fit, or of
+ * the log-densities of gmm_assign_topm (the last two report
+ * GMM_ESTEP_INT8_SLICES when they ran on int8 slices, else GMM_ESTEP_FP64;
+ * rows wider than 128 always run in fp64), or -1 if the workspace is NULL or
+ * the synchronisation failed. */
 int gmm_estep_arithmetic(const void* workspace, void* stream);
 
 /* Static description of a status code. */

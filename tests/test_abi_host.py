@@ -170,5 +170,6 @@ def test_binding_constants_match_header(ops):
     vals = dict((m[0], int(m[1])) for m in re.findall(r"\b(GMM_[A-Z0-9_]+)\s*=\s*(-?\d+)", src))
     for name in ("GMM_ESTEP_FP64", "GMM_ESTEP_INT8_SLICES", "GMM_ESTEP_INT8_SLICES_BOTH",
                  "GMM_ESTEP_INT8_SLICES_MSTEP", "GMM_ESTEP_BF16_SPLIT", "GMM_OK",
-                 "GMM_E_INVALID", "GMM_E_WORKSPACE", "GMM_E_UNSUPPORTED", "GMM_E_PARAMS"):
+                 "GMM_E_INVALID", "GMM_E_WORKSPACE", "GMM_E_UNSUPPORTED", "GMM_E_PARAMS",
+                 "GMM_F32", "GMM_BF16"):
         assert getattr(ops, name) == vals[name], name

@@ -173,6 +173,26 @@ def test_assign_topm(ops, wl, n, m):
     _check_topm(idx.cpu().numpy(), resp.cpu().numpy(), ridx, rresp, gap, ell_top)
 
 
+@pytest.mark.parametrize("n,d,k,m,seed", [(3001, 20, 70, 1, 61), (64 * 7 + 5, 33, 17, 2, 62),
+                                           (5000, 96, 200, 3, 63), (2500, 128, 40, 4, 64),
+                                           (700, 5, 9, 4, 65)])
+def test_assign_topm_int8(ops, n, d, k, m, seed):
+    # integer-valued fp32 rows: the top-m pass runs on exact int8 slices
+    # (32 rows per wave, top-2 or top-4 lists); ragged N, D, K and every m
+    x = _int_data(n, d, k, seed, hi=120.0)
+    w0, m0, v0 = _seed_params(x, k, seed)
+    rw, rmu, rv, *_ = oracle.em_step(x, w0, m0, v0)
+    th = [a.astype(np.float32) for a in (rw, rmu, rv)]
+    xt, w, mu, var = _to_dev(x, *th)
+    ws = ops.workspace(d, k, DEV)
+    idx, resp = ops.assign_topm(xt, w, mu, var, m, ws=ws)
+    torch.cuda.synchronize()
+    assert ops.estep_arithmetic(ws, DEV) == ops.GMM_ESTEP_INT8_SLICES
+    ridx, rresp, gap = oracle.topm(x, *th, m)
+    ell_top = np.abs(np.log(np.maximum(rresp[:, 0], 1e-300)))
+    _check_topm(idx.cpu().numpy(), resp.cpu().numpy(), ridx, rresp, gap, ell_top)
+
+
 def test_embed_prefix_per_step(ops):
     W = dg.WORKLOADS["embed"]
     x = dg.rows(W, 100_000)

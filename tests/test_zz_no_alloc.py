@@ -35,18 +35,25 @@ def ops():
 def _noalloc(ops, xt, w, mu, var, floor):
     L = torch.empty((), dtype=torch.float64, device=DEV)
     p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    rc = ops.lib.gmm_em_step_noalloc(p(xt), xt.shape[0], xt.shape[1], xt.shape[1], 0, p(w), p(mu),
+    dt = ops.GMM_BF16 if xt.dtype == torch.bfloat16 else ops.GMM_F32
+    rc = ops.lib.gmm_em_step_noalloc(p(xt), xt.shape[0], xt.shape[1], xt.shape[1], dt, p(w), p(mu),
                                      p(var), w.shape[0], floor, p(L),
                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     return rc, L
 
 
-def _compare(ops, x, w0, m0, v0, floor, label):
+def _compare(ops, x, w0, m0, v0, floor, label, path=None):
     print(f"# {label}: N={x.shape[0]} D={x.shape[1]} K={len(w0)}", flush=True)
-    xt = torch.from_numpy(x).to(DEV)
+    if x.dtype == np.uint16:  # bf16 bit patterns
+        xt = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        xt = torch.from_numpy(x).to(DEV)
     ref = [torch.from_numpy(a).to(DEV) for a in (w0, m0, v0)]
     got = [t.clone() for t in ref]
-    Lr = ops.em_step(xt, *ref, floor)
+    ws = ops.workspace(x.shape[1], len(w0), DEV)
+    Lr = ops.em_step(xt, *ref, floor, ws=ws)
+    if path is not None:
+        assert ops.estep_arithmetic(ws, DEV) == path
     rc, Lg = _noalloc(ops, xt, *got, floor)
     torch.cuda.synchronize()
     assert rc == ops.GMM_OK, rc
@@ -63,6 +70,18 @@ def test_noalloc_matches_workspace_entry_point_twice(ops):
     T = dg.WORKLOADS["tiny"]
     xs = dg.rows(T)
     _compare(ops, xs, *dg.init_params(T, xs), T.var_floor, "tiny (smaller, after the first)")
+
+
+def test_noalloc_bf16_split_path(ops):
+    # bf16 data on the split-bf16 path: the scratch also holds that path's
+    # coefficient pieces; a larger call, then a smaller one
+    B = dg.WORKLOADS["bf16_large"]
+    xb = dg.rows(B, 120_000)
+    _compare(ops, xb, *dg.init_params(B, xb), B.var_floor, "bf16_large prefix",
+             path=ops.GMM_ESTEP_BF16_SPLIT)
+    xs = xb[:5_003]
+    _compare(ops, xs, *dg.init_params(B, xs), B.var_floor, "bf16_large smaller prefix",
+             path=ops.GMM_ESTEP_BF16_SPLIT)
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch(ops):
