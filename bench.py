@@ -46,9 +46,11 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak (the split-bf16 
 # (FETCH_SIZE x2.0, WRITE_SIZE x1.0). Keyed by a hash of the kernel sources,
 # then by workload: a changed kernel reports null until it is profiled again.
 MEASURED_TRAFFIC = {
-    "595c2b490ba31b8b": {
+    "89d76aa7213ba9ad": {
+        "descriptor": {"kernel": "k_stats8x (pass 2: int8-slice E-step and M-step)",
+                       "bytes_per_launch": 1.3964e9},
         "bf16_large": {"kernel": "k_stats16 (pass 2: split-bf16 E-step and M-step)",
-                       "bytes_per_launch": 2.594e9},
+                       "bytes_per_launch": 2.5933e9},
     },
 }
 
