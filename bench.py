@@ -138,7 +138,9 @@ def main() -> int:
     torch.cuda.reset_peak_memory_stats(dev)
     free_before, total_mem = torch.cuda.mem_get_info(dev)
 
-    chunk = 4096 if W.d > 128 else (1 << 22)  # rows per launch of each pass
+    # rows per launch of each pass: the library's chunks (wide rows 4096; an EM
+    # step on bf16 rows 2^20, the split-bf16 path's operand pieces; else 2^22)
+    chunk = 4096 if W.d > 128 else ((1 << 20) if W.dtype == "bf16" else (1 << 22))
     ops.profile_begin(args.steps * (-(-n_rows // chunk)) + 8)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)

@@ -14,7 +14,7 @@ namespace gmm {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows, int max_groups) {
+bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows, int max_groups, int64_t b16_rows) {
     if (d < 1 || k < 1 || k > (1 << 22)) return false;
     Plan p;
     p.d = d;
@@ -61,7 +61,12 @@ bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows, int max_gro
     const size_t o_it = take(i8 ? (size_t)p.ntiles * I8_TINFO * sizeof(int) : 0);
     p.i8_nc = i8 ? i8_nc_for(d) : 0;
     p.i8_stats = i8 && i8_stats_for(p.dp);
-    const size_t o_ir = take(p.i8_stats ? (size_t)chunk_rows * S8_FLG : 0);
+    // one region for the int8 pass's packed digit rows and the split-bf16
+    // statistics pass's operand pieces (a call uses one of them)
+    p.b16_chunk = i8 ? (b16_rows < chunk_rows ? b16_rows : chunk_rows) : 0;
+    const size_t rows8 = p.i8_stats ? (size_t)chunk_rows * S8_FLG : 0;
+    const size_t rows16 = (size_t)p.b16_chunk * B16_PIECE_ROW_BYTES * (size_t)((d + 31) / 32);
+    const size_t o_ir = take(rows8 > rows16 ? rows8 : rows16);
     const size_t o_bc = take(i8 ? (size_t)p.ntiles * B16_TILE_BYTES : 0);
     const size_t o_bv = take(i8 ? (size_t)p.kp * sizeof(double) : 0);
     const size_t o_ba = take(i8 ? MAX_DP * sizeof(unsigned long long) : 0);
@@ -91,6 +96,7 @@ bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows, int max_gro
             p.i8_ek = (int*)(b + o_ie);
             p.i8_tinfo = (int*)(b + o_it);
             if (p.i8_stats) p.i8_rows = (int8_t*)(b + o_ir);
+            p.b16_pieces = (uint32_t*)(b + o_ir);
             p.b16_coef = (uint16_t*)(b + o_bc);
             p.b16_cvec = (double*)(b + o_bv);
             p.b16_amax = (unsigned long long*)(b + o_ba);
@@ -169,13 +175,21 @@ static void prof_mark(int pass, bool start, hipStream_t st) {
 // receives every row's normaliser instead of the chunk scratch. With i8 (the
 // int8-slice prologue has run), pass 1 is the int8-slice kernel when the
 // prologue selected it.
+// Rows per chunk of run_passes: an EM step on bf16 data on the narrow path
+// takes the split-bf16 statistics pass's chunk (its operand pieces fill the
+// workspace region for that many rows).
+static int64_t chunk_for(const Plan& pl, int dtype, bool stats) {
+    return stats && dtype == GMM_BF16 && !pl.wide ? pl.b16_chunk : pl.chunk;
+}
+
 static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t ldx, int dtype,
                              bool stats, hipStream_t st, int m = 0, int32_t* idx = nullptr,
                              float* resp = nullptr, double* lse_rows = nullptr,
                              bool i8 = false) {
     const size_t esz = dtype == GMM_BF16 ? 2 : 4;
-    for (int64_t c0 = 0, ci = 0; c0 < n; c0 += pl.chunk, ++ci) {
-        const int64_t cn = n - c0 < pl.chunk ? n - c0 : pl.chunk;
+    const int64_t chunk = chunk_for(pl, dtype, stats);
+    for (int64_t c0 = 0, ci = 0; c0 < n; c0 += chunk, ++ci) {
+        const int64_t cn = n - c0 < chunk ? n - c0 : chunk;
         const void* xc = (const char*)x + (size_t)c0 * (size_t)ldx * esz;
         double* lse = lse_rows ? lse_rows + c0 : pl.lse;
         int32_t* ic = m > 0 ? idx + c0 * m : nullptr;
@@ -192,7 +206,7 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
             } else {
                 e = launch_lse8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
                 if (e == hipSuccess && dtype == GMM_BF16)
-                    e = launch_lse16(pl, xc, cn, ldx, lse, ci > 0, st);
+                    e = launch_lse16(pl, xc, cn, ldx, lse, ci > 0, stats, st);
             }
             if (e == hipSuccess)
                 e = launch_lse(pl, xc, cn, ldx, dtype, lse, ci > 0, m, ic, rc, st, 0,
@@ -210,7 +224,7 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
                 // as for pass 1: the mode flag lets one of them work
                 if (pl.i8_stats) e = launch_stats8(pl, xc, cn, ldx, dtype, lse, ci > 0, st);
                 if (e == hipSuccess && dtype == GMM_BF16)
-                    e = launch_stats16(pl, xc, cn, ldx, lse, ci > 0, st);
+                    e = launch_stats16(pl, cn, lse, ci > 0, st);
                 if (e == hipSuccess)
                     e = launch_stats(pl, xc, cn, ldx, dtype, lse, ci > 0, st, pl.status + I8S_MODE2);
             } else {
@@ -223,8 +237,8 @@ static hipError_t run_passes(const Plan& pl, const void* x, int64_t n, int64_t l
     return hipSuccess;
 }
 
-static int ll_parts(const Plan& pl, int64_t n) {
-    const int64_t first = n < pl.chunk ? n : pl.chunk;
+static int ll_parts(const Plan& pl, int64_t n, int64_t chunk) {
+    const int64_t first = n < chunk ? n : chunk;
     return (int)((first + LL_ROWS - 1) / LL_ROWS);
 }
 
@@ -238,7 +252,7 @@ static int em_step_planned(const Plan& pl, const void* x, int64_t n, int64_t ldx
         e = launch_i8_prologue(pl, weights, means, variances, x, n, ldx, x_dtype, st);
     if (e != hipSuccess) return GMM_E_HIP;
     e = run_passes(pl, x, n, ldx, x_dtype, true, st, 0, nullptr, nullptr, nullptr, !pl.wide);
-    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), ll_out, st);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n, chunk_for(pl, x_dtype, true)), ll_out, st);
     if (e == hipSuccess) e = launch_finalize(pl, pl.ngroups, n, var_floor, weights, means, variances, st);
     return hip_status(e);
 }
@@ -299,7 +313,8 @@ int gmm_em_step_noalloc(const void* x, int64_t n, int32_t d, int64_t ldx, int32_
     Plan pl;
     int groups = 512;
     for (;;) {
-        if (!make_plan(d, k, nullptr, &pl, NOALLOC_CHUNK_ROWS, groups)) return GMM_E_UNSUPPORTED;
+        if (!make_plan(d, k, nullptr, &pl, NOALLOC_CHUNK_ROWS, groups, NOALLOC_B16_CHUNK_ROWS))
+            return GMM_E_UNSUPPORTED;
         if (pl.bytes <= NOALLOC_SCRATCH_BYTES) break;
         if (groups == 1) return GMM_E_UNSUPPORTED;  // (d, k) too large for the scratch
         groups = groups / 2 > 1 ? groups / 2 : 1;
@@ -307,7 +322,7 @@ int gmm_em_step_noalloc(const void* x, int64_t n, int32_t d, int64_t ldx, int32_
     void* scr = nullptr;
     const int rc = scratch_address(&scr);
     if (rc) return rc;
-    make_plan(d, k, scr, &pl, NOALLOC_CHUNK_ROWS, groups);
+    make_plan(d, k, scr, &pl, NOALLOC_CHUNK_ROWS, groups, NOALLOC_B16_CHUNK_ROWS);
     return em_step_planned(pl, x, n, ldx, x_dtype, weights, means, variances, var_floor, loglik_dev,
                            (hipStream_t)stream);
 }
@@ -362,7 +377,7 @@ int gmm_loglik(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_dtype
     if (e == hipSuccess)
         e = run_passes(pl, x, n, ldx, x_dtype, false, st, 0, nullptr, nullptr, per_row_dev,
                        !pl.wide);
-    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), total_dev, st);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n, pl.chunk), total_dev, st);
     return hip_status(e);
 }
 
@@ -426,7 +441,7 @@ int gmm_kmeans_step(const void* x, int64_t n, int32_t d, int64_t ldx, int32_t x_
                     : launch_km_stats(pl, xc, cn, ldx, x_dtype, zc, ci > 0, st);
         prof_mark(2, false, st);
     }
-    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n), inertia_dev ? inertia_dev : pl.ll_tmp, st, -1.0);
+    if (e == hipSuccess) e = launch_ll_final(pl, ll_parts(pl, n, pl.chunk), inertia_dev ? inertia_dev : pl.ll_tmp, st, -1.0);
     if (e == hipSuccess) e = launch_kmfinal(pl, centroids, st);
     return hip_status(e);
 }

@@ -216,16 +216,23 @@ __device__ __forceinline__ uint32_t b16_feature(float a, int kd) {
     return kd == 0 ? hb : __float_as_uint(a2 - bf16_val(hb)) >> 16;  // the rest, exact
 }
 
+// rotated position of lane (h, i)'s 16-byte chunk in piece p of a row tile's
+// operand pieces (below)
+__device__ __forceinline__ int b16_chunk(int h, int i, int p) { return 16 * h + ((i + 4 * h + p) & 15); }
+
 template <int DC>
 __global__ __launch_bounds__(L16_WAVES * 64, 1)
 void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
              const uint16_t* __restrict__ coef, const double* __restrict__ cvec, int ntiles,
              double* __restrict__ lse_out, double* __restrict__ llpart, int ll_accumulate,
-             const int* __restrict__ status) {
+             uint32_t* __restrict__ pieces, const int* __restrict__ status) {
     constexpr int DQ = 32 * DC;
     constexpr int DCA = (DC + 1) / 2;  // slices of the first half
     constexpr int KS = DQ + 8;         // staged stride of one kind (bf16 values): conflict-free reads
     constexpr int NP = B16_PROD * DC;
+    constexpr int NPE = 2 * 3 * DC;    // E pieces of a 32-row tile: (row tile, kind, slice)
+    constexpr int NJ = DQ / 16;        // M pieces per kind: 16-column tiles
+    constexpr int NPT = NPE + 3 * NJ;  // pieces of a 32-row tile
     constexpr int TBL = NP * 1024;
     constexpr int STG = L16_WAVES * 16 * KS * 2;
     constexpr int TB = TBL > STG ? TBL : STG;
@@ -238,10 +245,18 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int ci = lane & 15, h = lane >> 4;
     const int64_t wrow = (int64_t)blockIdx.x * L16_ROWS + wave * (L16_RT * 16);
 
-    // ---- features of the wave's rows; lane l handles dims l and l + 64
+    // ---- features of the wave's rows; lane l handles dims l and l + 64.
+    // With `pieces`, the wave's 32 rows (one row tile of the statistics pass)
+    // also go out as that pass's MFMA operand pieces, 1 KB each, at
+    // pieces[tile][piece]: E pieces (row tile rt, kind, slice j) as the A
+    // operands below, and M pieces (kind, column tile J), in which lane (h, i)
+    // holds column 16 J + i at rows 4h + q (elements q) and 16 + 4h + q
+    // (elements 4 + q); each lane's 16-byte chunk at its rotated position.
     v4i A[L16_RT][3 * DC];
     {
         uint16_t* stg = (uint16_t*)&cbuf[1][wave * 16 * KS * 2];
+        const int64_t ptile = wrow / (L16_RT * 16);
+        uint32_t* pt = (pieces && wrow < n) ? pieces + ptile * (NPT * 256) : nullptr;
 #pragma unroll
         for (int rt = 0; rt < L16_RT; ++rt) {  // unrolled: A stays in registers
             float xv[16][2];
@@ -267,6 +282,19 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
 #pragma unroll
                 for (int j = 0; j < DC; ++j)
                     A[rt][kd * DC + j] = *(const v4i*)(stg + ci * KS + 32 * j + 8 * h);
+                if (pt) {
+#pragma unroll
+                    for (int j = 0; j < DC; ++j)
+                        *(v4i*)(pt + ((rt * 3 + kd) * DC + j) * 256 + b16_chunk(h, ci, j) * 4) =
+                            A[rt][kd * DC + j];
+#pragma unroll
+                    for (int J = 0; J < NJ; ++J) {
+                        const uint16_t* col = stg + 4 * h * KS + 16 * J + ci;
+                        *(uint2*)(pt + (NPE + kd * NJ + J) * 256 + b16_chunk(h, ci, J) * 4 + 2 * rt) =
+                            uint2{(uint32_t)col[0] | ((uint32_t)col[KS] << 16),
+                                  (uint32_t)col[2 * KS] | ((uint32_t)col[3 * KS] << 16)};
+                    }
+                }
                 __syncthreads();
             }
         }
@@ -379,13 +407,13 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
 // per SIMD): waves 0-3 are E-waves, waves 4-7 M-waves, and the two waves of
 // a SIMD own the same K-tile kg*4 + (wave & 3). The block walks its row group
 // in 32-row tiles, one barrier per tile, as a two-stage pipeline:
-//  * every wave helps build the next tile's bf16 features into LDS, as 1 KB
-//    MFMA operand pieces: E pieces (row tile, kind, slice) for the E-step's
-//    A operand, M pieces (kind, 16-column tile) for the M-step's, in which
+//  * the next tile's bf16 features arrive in LDS by buffer-to-LDS copies of
+//    the 1 KB MFMA operand pieces the normaliser pass wrote for it (every
+//    wave copies some): E pieces (row tile, kind, slice) for the E-step's A
+//    operand, M pieces (kind, 16-column tile) for the M-step's, in which
 //    lane (h, i) holds column i at the rows 4h .. 4h+3 and 16+4h .. 16+4h+3;
 //    a piece's 16-byte lane chunks are rotated (chunk 16h + (i + 4h + p) mod
-//    16 for piece p) so that both the builders' writes and the MFMA lanes'
-//    reads hit distinct banks;
+//    16 for piece p) so that the MFMA lanes' reads hit distinct banks;
 //  * the E-wave keeps all the K-tile's coefficient pieces in registers,
 //    contracts the tile exactly as the normaliser pass does (same order,
 //    same bits), forms r = exp(l - lse), splits it into three bf16 parts and
@@ -399,12 +427,9 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
 // wave's VALU work (exponentials, splits, fp64 folds) overlaps the other's
 // MFMAs. The features are triple-buffered for the M-waves' lag.
 // ---------------------------------------------------------------------------
-// rotated position of lane (h, i)'s 16-byte chunk in piece p
-__device__ __forceinline__ int b16_chunk(int h, int i, int p) { return 16 * h + ((i + 4 * h + p) & 15); }
-
 template <int DC>
 __global__ __launch_bounds__(512, 1)
-void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
+void k_stats16(int64_t n, int dp, const uint32_t* __restrict__ pieces,
                const uint16_t* __restrict__ coef, const double* __restrict__ cvec, int ntiles,
                const double* __restrict__ lse, int64_t rows_per_group, double* __restrict__ part,
                double* __restrict__ npart, int accumulate, const int* __restrict__ status) {
@@ -412,10 +437,9 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
     constexpr int DQ = 32 * DC;
     constexpr int DCA = (DC + 1) / 2;   // slices of the first half
     constexpr int NJ = DQ / 16;         // 16-column M-step tiles per feature kind
-    constexpr int TQ = DQ / 2;          // builder threads per 4-row group (2 dims each)
     constexpr int NPE = 2 * 3 * DC;     // E pieces per tile: (row tile, kind, slice)
     constexpr int NPM = 3 * NJ;         // M pieces per tile: (kind, column tile)
-    static_assert(8 * TQ <= 512, "one builder thread per 4 rows x 2 dims");
+    constexpr int NPT = NPE + NPM;
     __shared__ __attribute__((aligned(16))) uint32_t fe[2][NPE * 256];
     __shared__ __attribute__((aligned(16))) uint32_t fm[3][NPM * 256];
     __shared__ __attribute__((aligned(16))) uint32_t rr[2][KT][3 * 256];  // r parts per K-tile
@@ -442,83 +466,41 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
     if (gr1 > n) gr1 = n;
     const int64_t ntile_rows = gr1 > gr0 ? (gr1 - gr0 + STATS_ROWS - 1) / STATS_ROWS : 0;
 
-    // builder: thread (rq, q2) handles rows 4 rq .. +3, dims 2 q2 .. +1
-    const bool bw = tid < 8 * TQ;
-    const int rq = tid / TQ, q2 = tid % TQ;
-    float xv[4][2];
-    int nvl = 0;  // valid rows of the loaded tile
-    double lv = 0.0;
-    auto load = [&](int64_t it) {
+    // tile it's pieces into E buffer be and M buffer bm (every wave copies
+    // some), and the normaliser of row tid (+inf past the row group: r = 0)
+    auto issue = [&](int64_t it, int be, int bm) {
+        const int64_t tile_g = (gr0 + it * STATS_ROWS) / STATS_ROWS;
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(pieces + tile_g * (NPT * 256)), (short)0, NPT * 1024, BUF_RSRC_WORD3);
+        for (int p = wave; p < NPT; p += 8) {
+            uint32_t* dst = p < NPE ? fe[be] + p * 256 : fm[bm] + (p - NPE) * 256;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (__attribute__((address_space(3))) void*)dst, 16,
+                                                     lane * 16, p * 1024, 0, 0);
+        }
+    };
+    auto load_ls = [&](int64_t it) -> double {
         const int64_t rbase = gr0 + it * STATS_ROWS;
-        int64_t nv = gr1 - rbase;
-        nv = nv < 0 ? 0 : (nv > STATS_ROWS ? STATS_ROWS : nv);
-        nvl = (int)nv;
-        const int xbytes = nv > 0 ? (int)(((nv - 1) * ldx + d) * 2) : 0;
-        const __amdgpu_buffer_rsrc_t xr =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(x + rbase * ldx), (short)0, xbytes, BUF_RSRC_WORD3);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int dd = 2 * q2 + u;
-                // dims past d read past the buffer (0); rows past nv likewise
-                const uint32_t off = (bw && dd < d)
-                                         ? (uint32_t)((((int64_t)(4 * rq + r)) * ldx + dd) * 2)
-                                         : 0xFFFFFFF0u;
-                xv[r][u] = buf_load_x<uint16_t>(xr, off);
-            }
-        const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(lse + rbase), (short)0, (int)(nv * (int64_t)sizeof(double)), BUF_RSRC_WORD3);
-        const int lrow = tid & (STATS_ROWS - 1);
-        const double v = buf_load_f64(lr, (uint32_t)lrow * 8u);
-        lv = lrow < nv ? v : INFINITY;  // rows past the row group: responsibility 0
+        const int64_t nv = gr1 - rbase;
+        return tid < nv ? lse[rbase + tid] : INFINITY;
     };
-    // features of the loaded tile into E buffer be and M buffer bm
-    auto store = [&](int be, int bm) {
-        if (bw) {
-            const int rt = rq >> 2, hr = rq & 3;  // rows 16 rt + 4 hr .. +3
-            const int j = q2 >> 4, hd = (q2 >> 2) & 3, ew = q2 & 3;  // dims 32 j + 8 hd + 2 ew .. +1
-            uint32_t f[3][4];  // [kind][row]: dims 2 q2 (low half) and 2 q2 + 1
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool live = 4 * rq + r < nvl;  // rows past the group hold zeros
-                b16_features_pack(live ? xv[r][0] : 0.0f, live ? xv[r][1] : 0.0f, f[0][r], f[1][r],
-                                  f[2][r]);
-            }
-#pragma unroll
-            for (int kd = 0; kd < 3; ++kd) {
-                // E piece (rt, kd, j): row 4 hr + r is lane (hd, 4 hr + r), dims 2 ew .. +1 of its 8
-                uint32_t* pe = fe[be] + ((rt * 3 + kd) * DC + j) * 256;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pe[b16_chunk(hd, 4 * hr + r, j) * 4 + ew] = f[kd][r];
-                // M pieces (kd, J) of columns 2 q2 and 2 q2 + 1: lane (hr, column mod 16),
-                // elements 4 rt .. 4 rt + 3 (rows 16 rt + 4 hr .. +3)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int c = 2 * q2 + u, J = c >> 4;
-                    uint32_t* pm = fm[bm] + (kd * NJ + J) * 256;
-                    const uint32_t sel = u ? 0x07060302u : 0x05040100u;
-                    *(uint2*)(pm + b16_chunk(hr, c & 15, J) * 4 + 2 * rt) =
-                        uint2{__builtin_amdgcn_perm(f[kd][1], f[kd][0], sel),
-                              __builtin_amdgcn_perm(f[kd][3], f[kd][2], sel)};
-                }
-            }
-        }
-        if (tid < STATS_ROWS) ls[be][tid] = lv;
-    };
-    // the pipeline's shared step: build tile it+1, load tile it+2
-    auto build_next = [&](int64_t it) {
+    // the pipeline's shared step: copy tile it+1 (it lands before the barrier)
+    double lsn = 0.0;
+    auto next_issue = [&](int64_t it) {
         if (it + 1 < ntile_rows) {
-            store((int)((it + 1) & 1), (int)((it + 1) % 3));
-            if (it + 2 < ntile_rows) load(it + 2);
+            issue(it + 1, (int)((it + 1) & 1), (int)((it + 1) % 3));
+            if (tid < STATS_ROWS) lsn = load_ls(it + 1);
         }
+    };
+    auto next_finish = [&](int64_t it) {
+        if (it + 1 < ntile_rows && tid < STATS_ROWS) ls[(it + 1) & 1][tid] = lsn;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
     };
 
     if (ntile_rows > 0) {
-        load(0);
-        store(0, 0);
-        if (ntile_rows > 1) load(1);
+        issue(0, 0, 0);
+        if (tid < STATS_ROWS) ls[0][tid] = load_ls(0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     if (ewave) {
@@ -532,6 +514,7 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
         const double cc = cvec[slot];
         double n64 = 0.0;
         for (int64_t it = 0; it <= ntile_rows; ++it) {
+            next_issue(it);
             if (it < ntile_rows) {
                 const int be = (int)(it & 1);
                 const uint32_t* F = fe[be];
@@ -597,7 +580,7 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
                 const bool wany = __builtin_amdgcn_ballot_w64(any) != 0;
                 if (lane == 0) anyr[be][kq] = wany ? 1 : 0;
             }
-            build_next(it);
+            next_finish(it);
             __syncthreads();
         }
         // responsibility mass: lanes ci, ci+16, ci+32, ci+48 hold disjoint rows
@@ -618,6 +601,7 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
                 tB[j][q] = 0.0;
             }
         for (int64_t it = 0; it <= ntile_rows; ++it) {
+            next_issue(it);
             if (it >= 1) {
                 const int be = (int)((it - 1) & 1), bm = (int)((it - 1) % 3);
                 if (anyr[be][kq] != 0) {
@@ -649,7 +633,7 @@ void k_stats16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx, in
                     }
                 }
             }
-            build_next(it);
+            next_finish(it);
             __syncthreads();
         }
         double* pp = part + ((int64_t)g * ntiles * 16 + slot) * (2 * (int64_t)dp);
@@ -676,7 +660,8 @@ hipError_t launch_b16_coef(const Plan& pl, const float* w, const float* mu, cons
 }
 
 hipError_t launch_lse16(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
-                        int ll_acc, hipStream_t st) {
+                        int ll_acc, bool pieces, hipStream_t st) {
+    if (pieces && n > pl.b16_chunk) return hipErrorInvalidValue;  // the pieces buffer's rows
     if (n <= 0) return hipSuccess;
     const dim3 grid((unsigned)((n + L16_ROWS - 1) / L16_ROWS)), block(L16_WAVES * 64);
     const uint16_t* xb = (const uint16_t*)x;
@@ -684,7 +669,8 @@ hipError_t launch_lse16(const Plan& pl, const void* x, int64_t n, int64_t ldx, d
 #define CASE(DCV)                                                                               \
     case DCV:                                                                                   \
         hipLaunchKernelGGL((k_lse16<DCV>), grid, block, 0, st, xb, n, pl.d, ldx, pl.b16_coef,   \
-                           pl.b16_cvec, pl.ntiles, lse_out, pl.llpart, ll_acc, pl.status);     \
+                           pl.b16_cvec, pl.ntiles, lse_out, pl.llpart, ll_acc,                  \
+                           pieces ? pl.b16_pieces : nullptr, pl.status);                        \
         break;
         CASE(1) CASE(2) CASE(3) CASE(4)
 #undef CASE
@@ -693,16 +679,15 @@ hipError_t launch_lse16(const Plan& pl, const void* x, int64_t n, int64_t ldx, d
     return hipGetLastError();
 }
 
-hipError_t launch_stats16(const Plan& pl, const void* x, int64_t n, int64_t ldx, const double* lse,
-                          int acc, hipStream_t st) {
+hipError_t launch_stats16(const Plan& pl, int64_t n, const double* lse, int acc, hipStream_t st) {
+    if (n > pl.b16_chunk) return hipErrorInvalidValue;  // the pieces the normaliser pass wrote
     int64_t rpg = ((n + pl.ngroups - 1) / pl.ngroups + STATS_ROWS - 1) / STATS_ROWS * STATS_ROWS;
     if (rpg < STATS_ROWS) rpg = STATS_ROWS;
     const dim3 grid(pl.ngroups * (pl.ntiles / 4)), block(512);
-    const uint16_t* xb = (const uint16_t*)x;
     switch ((pl.d + 31) / 32) {
 #define CASE(DCV)                                                                              \
     case DCV:                                                                                  \
-        hipLaunchKernelGGL((k_stats16<DCV>), grid, block, 0, st, xb, n, pl.d, ldx, pl.dp,      \
+        hipLaunchKernelGGL((k_stats16<DCV>), grid, block, 0, st, n, pl.dp, pl.b16_pieces,      \
                            pl.b16_coef, pl.b16_cvec, pl.ntiles, lse, rpg, pl.part, pl.npart,   \
                            acc, pl.status);                                                    \
         break;

@@ -65,6 +65,13 @@ constexpr int I8S_B16FAIL = 9;
 constexpr int B16_MAX_DC = 4;
 constexpr int B16_PROD = 8;
 constexpr int B16_TILE_BYTES = B16_MAX_DC * B16_PROD * 1024;
+// The statistics pass's operand pieces of one row: 12 dc pieces of 1 KB per
+// 32-row tile (E and M layouts of the three feature kinds), written by the
+// normaliser pass for chunks of B16_CHUNK_ROWS rows (the allocation-free
+// entry point: NOALLOC_B16_CHUNK_ROWS).
+constexpr int B16_PIECE_ROW_BYTES = 12 * 1024 / 32;  // per row and 32-dim slice
+constexpr int64_t B16_CHUNK_ROWS = (int64_t)1 << 20;
+constexpr int64_t NOALLOC_B16_CHUNK_ROWS = (int64_t)1 << 14;
 // accepted estimate of the fp32 rounding of a log-density (nats): 2^-7
 constexpr double B16_DELTA = 0.0078125;
 // The statistics pass keeps a K-tile's digit levels in registers: at most
@@ -104,6 +111,11 @@ struct Plan {
     int* i8_ek = nullptr;      // [kp] per-component scale exponent
     int* i8_tinfo = nullptr;   // [ntiles][I8_TINFO] levels per tile
     int8_t* i8_rows = nullptr; // [CHUNK_ROWS][S8_FLG] packed digit rows of the current chunk
+    // [b16_chunk / STATS_ROWS][12 dc][1024 B] the split-bf16 statistics pass's
+    // operand pieces of the current chunk (the same memory as i8_rows: one
+    // call uses one of them)
+    uint32_t* b16_pieces = nullptr;
+    int64_t b16_chunk = 0;     // rows per chunk of an EM step on bf16 data
     uint16_t* b16_coef = nullptr;  // [ntiles][B16_TILE_BYTES / 2] split-bf16 coefficient pieces
     double* b16_cvec = nullptr;    // [kp] per-component constants of the split-bf16 path (shift 0)
     unsigned long long* b16_amax = nullptr;  // [MAX_DP] largest |x| per dim (fp64 bits), bf16 data
@@ -117,9 +129,11 @@ struct Plan {
 
 // Workspace layout for (d, k). chunk_rows: rows per launch of the narrow
 // passes (sizes the per-row scratch); max_groups: cap on the statistics
-// pass's row groups (sizes the partials).
+// pass's row groups (sizes the partials); b16_rows: rows per launch of an EM
+// step on bf16 data (sizes the split-bf16 operand pieces; at most chunk_rows,
+// a multiple of 256).
 bool make_plan(int d, int k, void* ws, Plan* pl, int64_t chunk_rows = CHUNK_ROWS,
-               int max_groups = 512);
+               int max_groups = 512, int64_t b16_rows = B16_CHUNK_ROWS);
 
 hipError_t launch_prologue(const Plan& pl, const float* w, const float* mu, const float* var,
                            hipStream_t st);
@@ -152,13 +166,14 @@ hipError_t launch_lse8_topm(const Plan& pl, const void* x, int64_t n, int64_t ld
                             int ll_acc, int m, int32_t* idx, float* resp, hipStream_t st);
 // Split-bf16 path: coefficient pieces and the applicability check (run by
 // launch_i8_prologue for bf16 data), the normaliser pass (status[I8S_MODE] ==
-// MODE1_B16) and the statistics pass (status[I8S_MODE2] == MODE2_B16).
+// MODE1_B16; with `pieces` it also writes the chunk's operand pieces for the
+// statistics pass, n <= b16_chunk) and the statistics pass (status[I8S_MODE2]
+// == MODE2_B16), which reads those pieces instead of the rows.
 hipError_t launch_b16_coef(const Plan& pl, const float* w, const float* mu, const float* var,
                            hipStream_t st);
 hipError_t launch_lse16(const Plan& pl, const void* x, int64_t n, int64_t ldx, double* lse_out,
-                        int ll_acc, hipStream_t st);
-hipError_t launch_stats16(const Plan& pl, const void* x, int64_t n, int64_t ldx, const double* lse,
-                          int acc, hipStream_t st);
+                        int ll_acc, bool pieces, hipStream_t st);
+hipError_t launch_stats16(const Plan& pl, int64_t n, const double* lse, int acc, hipStream_t st);
 // int8-slice statistics passes (status[I8S_MODE2] == 1: int8 E-step with the
 // fp64 M-step; == 2: the M-step on int8 slices too; the fp64 statistics
 // kernel is told to skip through the same flag when it is nonzero)
