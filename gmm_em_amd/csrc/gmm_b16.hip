@@ -24,12 +24,13 @@
 //    below B16_DELTA (2^-7 nats) for every component; otherwise the fp64
 //    kernels run. The path has its own constants c_k (b = mu), and selecting
 //    it sets the shift to 0 for the finalisation of the statistics.
-//  * M-step: r in fp32 (below about 2^-100 it is taken as 0) is exactly rh + rm +
-//    rl in bf16 (24 significant bits in three 8-bit parts), and
-//    sum r a = sum (rl + rm + rh) a, sum r a^2 = sum (rm a2lo + rl a2hi +
-//    rh a2lo + rm a2hi + rh a2hi) (the product rl a2lo, below 2^-25 of the
-//    total, is left out), in fp32 per 32-row tile and in fp64 across tiles.
-//    The mass sum r is taken from the same fp32 values.
+//  * M-step: r in fp32 (below about 2^-100 it is taken as 0) is rounded to
+//    r' = rh + rm, two bf16 parts each rounded to nearest (within 2^-18 of r,
+//    relative; exact in fp32), and sum r' a = sum (rm + rh) a, sum r' a^2 =
+//    sum (rm a2lo + rh a2lo + rm a2hi + rh a2hi), all products exact, in fp32
+//    per 32-row tile and in fp64 across tiles. The mass sum r' is taken from
+//    the same values, so the three sums are the statistics of one set of
+//    weights r'.
 // Both passes contract the E-step in the same order, so they compute the
 // same log-densities bit for bit.
 //
@@ -70,16 +71,6 @@ __device__ __forceinline__ uint32_t bf16_pack(float x, float y) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
-
-// v = hi + mid + lo exactly for two fp32 values (24 significant bits in three
-// 8-bit parts; the last part is exact, so its rounding is too), packed in pairs
-__device__ __forceinline__ void bf16_split3_pack(float x, float y, uint32_t& ph, uint32_t& pm,
-                                                 uint32_t& pl) {
-    ph = bf16_pack(x, y);
-    const float x1 = x - bf16_lo(ph), y1 = y - bf16_hi(ph);  // exact
-    pm = bf16_pack(x1, y1);
-    pl = bf16_pack(x1 - bf16_lo(pm), y1 - bf16_hi(pm));      // exact
-}
 
 // The three feature kinds of two bf16 values a, b, packed in pairs:
 // a^2 hi, a^2 lo (a^2 = hi + lo exactly: at most 16 significant bits) and a
@@ -416,7 +407,7 @@ void k_lse16(const uint16_t* __restrict__ x, int64_t n, int d, int64_t ldx,
 //    16 for piece p) so that the MFMA lanes' reads hit distinct banks;
 //  * the E-wave keeps all the K-tile's coefficient pieces in registers,
 //    contracts the tile exactly as the normaliser pass does (same order,
-//    same bits), forms r = exp(l - lse), splits it into three bf16 parts and
+//    same bits), forms r = exp(l - lse), rounds it to two bf16 parts and
 //    hands them to its M-wave through LDS (the E-step result leaves lane
 //    (h, i) with rows 16 rt + 4h + q of component i, which are the lane's 8
 //    positions of the M-step contraction);
@@ -442,7 +433,7 @@ void k_stats16(int64_t n, int dp, const uint32_t* __restrict__ pieces,
     constexpr int NPT = NPE + NPM;
     __shared__ __attribute__((aligned(16))) uint32_t fe[2][NPE * 256];
     __shared__ __attribute__((aligned(16))) uint32_t fm[3][NPM * 256];
-    __shared__ __attribute__((aligned(16))) uint32_t rr[2][KT][3 * 256];  // r parts per K-tile
+    __shared__ __attribute__((aligned(16))) uint32_t rr[2][KT][2 * 256];  // r parts per K-tile
     __shared__ double ls[2][STATS_ROWS];
     __shared__ int anyr[2][KT];
     if (status[I8S_MODE2] != MODE2_B16) return;  // another statistics pass runs instead
@@ -550,7 +541,7 @@ void k_stats16(int64_t n, int dp, const uint32_t* __restrict__ pieces,
                         }
                 }
                 // responsibilities of rows 16 rt + 4h + q (element 4 rt + q of
-                // the M-step's B operands), split into three bf16 parts
+                // the M-step's B operands), rounded to two bf16 parts below
                 float rv[8];
                 bool any = false;
 #pragma unroll
@@ -562,20 +553,25 @@ void k_stats16(int64_t n, int dp, const uint32_t* __restrict__ pieces,
                                                  ls[be][16 * rt + 4 * h + q]);
                         const float r = tf > -69.3147181f ? __builtin_amdgcn_exp2f(tf * 1.44269504f)
                                                           : 0.0f;  // below about 2^-100: 0
-                        n64 += (double)r;
                         any |= r != 0.0f;
                         rv[4 * rt + q] = r;
                     }
                 uint32_t* R = rr[be][kq];
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
-                    uint32_t ph[2], pm[2], pl[2];
+                    uint32_t ph[2], pm[2];
 #pragma unroll
-                    for (int v = 0; v < 2; ++v)
-                        bf16_split3_pack(rv[4 * w + 2 * v], rv[4 * w + 2 * v + 1], ph[v], pm[v], pl[v]);
+                    for (int v = 0; v < 2; ++v) {
+                        // r' = rh + rm (each rounded to nearest), exact in fp32;
+                        // the mass takes the same r' as the moments
+                        const float x = rv[4 * w + 2 * v], y = rv[4 * w + 2 * v + 1];
+                        ph[v] = bf16_pack(x, y);
+                        pm[v] = bf16_pack(x - bf16_lo(ph[v]), y - bf16_hi(ph[v]));
+                        n64 += (double)(bf16_lo(ph[v]) + bf16_lo(pm[v]));
+                        n64 += (double)(bf16_hi(ph[v]) + bf16_hi(pm[v]));
+                    }
                     *(uint2*)(R + lane * 4 + 2 * w) = uint2{ph[0], ph[1]};
                     *(uint2*)(R + 256 + lane * 4 + 2 * w) = uint2{pm[0], pm[1]};
-                    *(uint2*)(R + 512 + lane * 4 + 2 * w) = uint2{pl[0], pl[1]};
                 }
                 const bool wany = __builtin_amdgcn_ballot_w64(any) != 0;
                 if (lane == 0) anyr[be][kq] = wany ? 1 : 0;
@@ -608,7 +604,6 @@ void k_stats16(int64_t n, int dp, const uint32_t* __restrict__ pieces,
                     const uint32_t* R = rr[be][kq];
                     const v4i Rh = *(const v4i*)(R + lane * 4);
                     const v4i Rm = *(const v4i*)(R + 256 + lane * 4);
-                    const v4i Rl = *(const v4i*)(R + 512 + lane * 4);
                     const uint32_t* M = fm[bm];
 #pragma unroll
                     for (int J = 0; J < NJ; ++J) {
@@ -617,11 +612,9 @@ void k_stats16(int64_t n, int dp, const uint32_t* __restrict__ pieces,
                         const v4i fl = *(const v4i*)(M + (NJ + J) * 256 + co);
                         const v4i fa = *(const v4i*)(M + (2 * NJ + J) * 256 + co);
                         f32x4 sa = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sb = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                        sa = mfma_bf16(fa, Rl, sa);
                         sa = mfma_bf16(fa, Rm, sa);
                         sa = mfma_bf16(fa, Rh, sa);
                         sb = mfma_bf16(fl, Rm, sb);
-                        sb = mfma_bf16(fh, Rl, sb);
                         sb = mfma_bf16(fl, Rh, sb);
                         sb = mfma_bf16(fh, Rm, sb);
                         sb = mfma_bf16(fh, Rh, sb);
