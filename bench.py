@@ -43,31 +43,36 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak (the split-bf16 
 # HBM bytes per launch of the dominant kernel, from rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE runs of this bench (profiles/*_hbm.md), each
 # scaled by what the counter reads for a plain 3.84 GB device copy
-# (FETCH_SIZE x2.0, WRITE_SIZE x1.0). Keyed by a hash of the kernel sources,
-# then by workload: a changed kernel reports null until it is profiled again.
+# (FETCH_SIZE x2.0, WRITE_SIZE x1.0). Each record holds a hash of the sources
+# that kernel is compiled from: a changed kernel reports null until it is
+# profiled again.
+TRAFFIC_SOURCES = {
+    "descriptor": ("gmm_i8.hip", "gmm_device.h", "gmm_internal.h"),
+    "bf16_large": ("gmm_b16.hip", "gmm_device.h", "gmm_internal.h"),
+}
 MEASURED_TRAFFIC = {
-    "89d76aa7213ba9ad": {
-        "descriptor": {"kernel": "k_stats8x (pass 2: int8-slice E-step and M-step)",
-                       "bytes_per_launch": 1.3964e9},
-        "bf16_large": {"kernel": "k_stats16 (pass 2: split-bf16 E-step and M-step)",
-                       "bytes_per_launch": 2.5933e9},
-    },
+    "descriptor": {"sources": "40ff8624ebc27a7e",
+                   "kernel": "k_stats8x (pass 2: int8-slice E-step and M-step)",
+                   "bytes_per_launch": 1.3960e9},
+    "bf16_large": {"sources": "52e992bdd72b5e14",
+                   "kernel": "k_stats16 (pass 2: split-bf16 E-step and M-step)",
+                   "bytes_per_launch": 3.6186e9},
 }
 
 
-def _kernel_hash() -> str:
+def _kernel_hash(workload: str) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("gmm_kernels.hip", "gmm_i8.hip", "gmm_b16.hip", "gmm_device.h", "gmm_internal.h"):
+    for name in TRAFFIC_SOURCES.get(workload, ()):
         with open(os.path.join(ROOT, "gmm_em_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def _traffic(workload: str, kernel: str):
-    rec = MEASURED_TRAFFIC.get(_kernel_hash(), {}).get(workload)
-    if rec is None or rec["kernel"] != kernel:
+    rec = MEASURED_TRAFFIC.get(workload)
+    if rec is None or rec["kernel"] != kernel or rec["sources"] != _kernel_hash(workload):
         return None
     return rec["bytes_per_launch"]
 
@@ -79,7 +84,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="descriptor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3_000_000)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the oracle's timed sample (default: sized for about 15 s of host work)")
     ap.add_argument("--rows", type=int, default=0,
                     help="time a prefix of this many rows instead of the workload's N (the "
                          "JSON line then reports the prefix; EM cost is linear in N)")
@@ -244,7 +250,17 @@ def main() -> int:
 
         # The oracle's step from the parameters that entered the timed steps
         # (a dense iteration), on a bounded row prefix, scaled to all rows.
-        nr = min(args.cpu_rows, n_rows)
+        # The sample is sized for about 15 s of host work from a timed
+        # calibration step on a small prefix (the oracle's rate per row
+        # depends on D, K and how much of the parameters the caches hold).
+        if args.cpu_rows:
+            nr = min(args.cpu_rows, n_rows)
+        else:
+            n0 = min(n_rows, max(2_000, int(2.0e10 / (W.d * W.k))))
+            t0 = time.perf_counter()
+            oracle.em_step(x[:n0], *theta_w, W.var_floor)
+            dt0 = time.perf_counter() - t0
+            nr = min(n_rows, max(n0, int(n0 * 15.0 / max(dt0, 1e-6))))
         xs = x[:nr]
         t1 = time.perf_counter()
         rw, rmu, rv, rL, rnk = oracle.em_step(xs, *theta_w, W.var_floor)
