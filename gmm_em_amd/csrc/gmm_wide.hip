@@ -518,6 +518,219 @@ void k_wstats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     }
 }
 
+// Statistics pass for fp32 rows: the same roles, arithmetic and order as
+// k_wstats, run as a two-stage pipeline so that the roles overlap. In phase p
+// the E waves contract tile p while the M waves run the M-step of tile p - 1
+// on the same SIMDs, so the matrix units see both roles' MFMAs back to back.
+// Rows stay fp32 in LDS, in three tile buffers (tile t in buffer t % 3): the
+// copies of tile p + 1 are issued at the start of phase p by all 8 waves
+// (buffer-to-LDS, two rows per wave, each row through its own buffer range:
+// rows past the group and dims past d read as 0) and have landed by the end
+// of phase p. Each wave forms a = x - s in fp64 for the values it reads (the
+// expression the staged kernels store), so the results equal k_wstats's bit
+// for bit. Per phase two barriers: after A the E waves publish their partial
+// l of tile p; after B the M waves read them at the start of phase p + 1.
+// Every wave runs the same ntr + 1 phases.
+// ---------------------------------------------------------------------------
+template <int DS>
+__device__ __forceinline__ f64x4 wide_estep_raw(const float* px, const double* psh,
+                                                const double (&pr)[DS / 2]) {
+    constexpr int T1 = DS / 4, EB = 4;
+    static_assert(T1 % EB == 0, "whole E batches");
+    f64x4 e = {0.0, 0.0, 0.0, 0.0};
+    float rx[2][EB];
+    double rs[2][EB];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+        rx[0][u] = px[4 * u];
+        rs[0][u] = psh[4 * u];
+    }
+#pragma unroll
+    for (int bt = 0; bt < T1 / EB; ++bt) {
+        const int cur = bt & 1;
+        if (bt + 1 < T1 / EB) {
+#pragma unroll
+            for (int u = 0; u < EB; ++u) {
+                rx[cur ^ 1][u] = px[4 * ((bt + 1) * EB + u)];
+                rs[cur ^ 1][u] = psh[4 * ((bt + 1) * EB + u)];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < EB; ++u) {
+            const int j = bt * EB + u;
+            const double v = (double)rx[cur][u] - rs[cur][u];
+            e = mfma4d(v, pr[2 * j], e);
+            e = mfma4d(v * v, pr[2 * j + 1], e);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return e;
+}
+
+template <int DP>
+__global__ __launch_bounds__(512, 1)
+void k_wstats_p(const float* __restrict__ x, int64_t n, int d, int64_t ldx,
+                const double* __restrict__ Pg, const double* __restrict__ cvec,
+                const double* __restrict__ shift, int ntiles, int64_t rows_per_group,
+                const double* __restrict__ lse, double* __restrict__ part,
+                double* __restrict__ npart, int accumulate) {
+    // RSF = DP + 2 floats: the E-step's reads (16 rows at one dim, 4 dims)
+    // hit distinct banks within each half-wave
+    constexpr int NT = 512, NS = 4, DS = DP / NS, NJ = DS / 16, NB = 3;
+    constexpr int RSF = DP + 2, SEGR = DP / 64;
+    static_assert(DP % 64 == 0, "whole 64-value segments per row");
+    __shared__ __attribute__((aligned(16))) float xr[NB][WROWS * RSF];
+    __shared__ double shl[DP];
+    __shared__ __attribute__((aligned(16))) f64x4 xb[NS][64];
+    __shared__ double ls[NB][WROWS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ci = lane & 15, h = lane >> 4;
+    const int s = w & 3;  // slice
+    const int o = wide_block_order();
+    const int g = o / ntiles;
+    const int kt = o % ntiles;
+    const int slot = kt * 16 + ci;
+    for (int i = tid; i < DP; i += NT) shl[i] = shift[(i & 1) * (DP / 2) + (i >> 1)];
+
+    const int64_t gr0 = (int64_t)g * rows_per_group;
+    int64_t gr1 = gr0 + rows_per_group;
+    if (gr1 > n) gr1 = n;
+    const int64_t ntr = gr1 > gr0 ? (gr1 - gr0 + WROWS - 1) / WROWS : 0;
+
+    // copies of tile `it` into its buffer: wave w moves rows 2w and 2w + 1
+    auto issue = [&](int64_t it) {
+        float* dst = xr[(int)(it % NB)];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int row = 2 * w + rr;
+            const int64_t grow = gr0 + it * WROWS + row;
+            const int nbytes = grow < gr1 ? d * (int)sizeof(float) : 0;
+            const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(x + (grow < gr1 ? grow : gr0) * ldx), (short)0, nbytes, BUF_RSRC_WORD3);
+#pragma unroll
+            for (int c = 0; c < SEGR; ++c)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xrs, (__attribute__((address_space(3))) void*)(dst + row * RSF + 64 * c), 4,
+                    lane * 4, c * 64 * (int)sizeof(float), 0, 0);
+        }
+    };
+    // normaliser of row tid of tile it (+inf past the group: r = 0)
+    auto load_ls = [&](int64_t it) -> double {
+        const int64_t row = gr0 + it * WROWS + tid;
+        return row < gr1 ? lse[row] : INFINITY;
+    };
+
+    if (ntr > 0) {
+        issue(0);
+        if (tid < WROWS) ls[0][tid] = load_ls(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    if (w < NS) {
+        // E role
+        double pr[DS / 2];
+        wide_coefs<DP, DS>(pr, Pg, slot, s, h);
+        const double* psh = shl + s * DS + h;
+        for (int64_t p = 0; p <= ntr; ++p) {
+            double lsn = INFINITY;
+            if (p + 1 < ntr) {
+                issue(p + 1);
+                if (tid < WROWS) lsn = load_ls(p + 1);
+            }
+            f64x4 e = {0.0, 0.0, 0.0, 0.0};
+            if (p < ntr) e = wide_estep_raw<DS>(xr[(int)(p % NB)] + ci * RSF + s * DS + h, psh, pr);
+            if (p + 1 < ntr && tid < WROWS) ls[(int)((p + 1) % NB)][tid] = lsn;
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile p + 1 have landed
+            __syncthreads();                // A
+            if (p < ntr) xb[s][lane] = e;
+            __syncthreads();                // B
+        }
+    } else {
+        // M role
+        const double cc = cvec[slot];
+        f64x4 acc[2 * NJ];
+#pragma unroll
+        for (int j = 0; j < 2 * NJ; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
+        double n64 = 0.0;
+        const double* psm = shl + s * DS + ci;
+        for (int64_t p = 0; p <= ntr; ++p) {
+            if (p + 1 < ntr) issue(p + 1);
+            if (p >= 1) {
+                const int bm = (int)((p - 1) % NB);
+                // fixed-order sum of the slices' partial l, one slice at a time
+                f64x4 l = xb[0][lane];
+#pragma unroll
+                for (int v = 1; v < NS; ++v) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    l += xb[v][lane];
+                }
+                double r[4];
+                bool any = false;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    r[q] = exp_f64range(l[q] + cc - ls[bm][4 * q + h]);
+                    n64 += r[q];
+                    any = any || r[q] != 0.0;
+                }
+                // a tile whose 256 responsibilities are all exactly zero adds
+                // nothing. B = a (then a^2) of row 4q + h, dim s*DS + 16J + ci;
+                // the reads of block J+1 are issued with block J's MFMAs.
+                if (__builtin_amdgcn_ballot_w64(any) != 0) {
+                    const float* pm = xr[bm] + h * RSF + s * DS + ci;
+                    float xv[2][4];
+                    double sv[2];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) xv[0][q] = pm[4 * q * RSF];
+                    sv[0] = psm[0];
+#pragma unroll
+                    for (int J = 0; J < NJ; ++J) {
+                        const int cur = J & 1;
+                        if (J + 1 < NJ) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) xv[cur ^ 1][q] = pm[4 * q * RSF + 16 * (J + 1)];
+                            sv[cur ^ 1] = psm[16 * (J + 1)];
+                        }
+                        double av[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) av[q] = (double)xv[cur][q] - sv[cur];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[J] = mfma4d(r[q], av[q], acc[J]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[NJ + J] = mfma4d(r[q], av[q] * av[q], acc[NJ + J]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile p + 1 have landed
+            __syncthreads();                // A
+            __syncthreads();                // B
+        }
+        const int64_t gbase = (int64_t)g * ntiles * 16;
+        if (s == 0) {
+            n64 += shfl_xor_d(n64, 16);
+            n64 += shfl_xor_d(n64, 32);
+            if (h == 0) {
+                double* np = npart + gbase + slot;
+                *np = (accumulate ? *np : 0.0) + n64;
+            }
+        }
+        // register q of lane (h, ci) of block J: component 4q + h, column
+        // s*DS + 16J + ci (first moment) or DP + that (second moment)
+#pragma unroll
+        for (int J = 0; J < 2 * NJ; ++J)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int comp = kt * 16 + 4 * q + h;
+                const int col = (J < NJ ? 0 : DP) + s * DS + 16 * (J % NJ) + ci;
+                double* pp = part + (gbase + comp) * (2 * DP) + col;
+                *pp = (accumulate ? *pp : 0.0) + acc[J][q];
+            }
+    }
+}
+
 // Merge of the normaliser partials of each row over its K-tiles (fixed
 // order: lane l takes tiles l, l+64, ..., then a butterfly over the wave),
 // giving lse, the block's log-likelihood partial and the top-m components.
@@ -715,9 +928,14 @@ static hipError_t launch_wstats_t(const Plan& pl, const void* x, int64_t n, int6
                                   const double* lse, int acc, hipStream_t st) {
     const int64_t rpg = wide_rows_per_group(pl, n);
     // every row group gets a block per K-tile (empty groups write zeros)
-    hipLaunchKernelGGL((k_wstats<DP, XT>), dim3(pl.ngroups * pl.ntiles), dim3(512), 0, st,
-                       (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, rpg, lse,
-                       pl.part, pl.npart, acc);
+    if constexpr (sizeof(XT) == 4)
+        hipLaunchKernelGGL((k_wstats_p<DP>), dim3(pl.ngroups * pl.ntiles), dim3(512), 0, st,
+                           (const float*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles,
+                           rpg, lse, pl.part, pl.npart, acc);
+    else
+        hipLaunchKernelGGL((k_wstats<DP, XT>), dim3(pl.ngroups * pl.ntiles), dim3(512), 0, st,
+                           (const XT*)x, n, pl.d, ldx, pl.Pg, pl.cvec, pl.shift, pl.ntiles, rpg,
+                           lse, pl.part, pl.npart, acc);
     return hipGetLastError();
 }
 
