@@ -327,6 +327,8 @@ def main() -> int:
         "loglik_first_last": [float(hist[0]), float(hist[-1])],
         "wall_s": round(wall, 3),
         "git_revision": _git_revision(),
+        # identifies the measured code where no git checkout is present
+        "source_hash": _source_hash(),
         "roofline": roofline,
         "parity_sample": parity,
         "cpu_baseline": cpu,
@@ -344,6 +346,20 @@ def _cpu_model():
     except OSError:
         pass
     return None
+
+
+def _source_hash():
+    """First 16 hex digits of a SHA-256 over the library's sources, the header and this file."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "gmm_em_amd", "csrc", "*")))
+    files += [os.path.join(ROOT, "include", "gmm_em.h"), os.path.abspath(__file__)]
+    for p in files:
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def _git_revision():
