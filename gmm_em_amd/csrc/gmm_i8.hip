@@ -574,6 +574,10 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             for (int q = 0; q < 4; ++q) l[rt][q] = 0.0;
         const int8_t* cb = cbuf[buf] + lane * 16;
         double sc = scale * (1.0 / 128.0);  // a pair starting at level 2
+        // the wave issuing its matrix block goes first on the SIMD; its
+        // logsumexp below runs at normal priority under the other wave's
+        // matrix block
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int lev = 0; lev < LV; lev += 2) {
             if (lev >= nl) break;  // the tile's remaining levels are zero
@@ -603,6 +607,7 @@ void k_lse8(const XT* __restrict__ x, int64_t n, int d, int64_t ldx, int dp,
             // accumulators (the register budget of two waves per SIMD)
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
