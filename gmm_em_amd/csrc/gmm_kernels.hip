@@ -785,16 +785,18 @@ __global__ void k_ll_final(const double* __restrict__ llpart, int nparts, double
 // row group g and K-tile t (16 centroids), the sum of a = x - s over the rows
 // assigned to each centroid of the tile, and their count, in the layout of
 // the statistics pass's partials. The 8 waves of a block take consecutive
-// eighths of the row group; a wave walks its rows 64 at a time (the
-// assignments of KMS_ZB such chunks loaded together), selects the rows
-// assigned to the tile with a ballot, loads up to KMS_BATCH of them at once
-// and adds them, in row order, into its own LDS accumulator (each lane
-// owns two dims, so no two lanes touch one element). The eight accumulators
-// are summed in a fixed order at the end. Every row is read by exactly one
-// block; no MFMA work is needed.
+// eighths of the row group; a wave reads the assignments of 64 * KMS_ZB
+// rows at a time, writes the rows assigned to the tile (row offset and
+// centroid, in row order) to a list of its own in LDS, then loads the
+// listed rows KMS_BATCH at a time and adds them, in row order, into its own
+// LDS accumulator (each lane owns two dims, so no two lanes touch one
+// element). With 16 of K centroids a tile matches about 16/K of the rows:
+// the list keeps the load batches full. The eight accumulators are summed
+// in a fixed order at the end. Every row is read by exactly one block; no
+// MFMA work is needed.
 constexpr int KMS_WAVES = 8;
 constexpr int KMS_BATCH = 16;  // matched rows loaded at once
-constexpr int KMS_ZB = 8;      // 64-row chunks of assignments loaded at once
+constexpr int KMS_ZB = 8;      // 64-row chunks of assignments listed at once
 
 template <int DP, typename XT>
 __global__ __launch_bounds__(KMS_WAVES * 64)
@@ -806,11 +808,14 @@ void k_km_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     constexpr int KS = 128;  // accumulator row stride: every lane's two dims fit
     __shared__ double kacc[KMS_WAVES][16 * KS];
     __shared__ int kcnt[KMS_WAVES][16];
+    // per wave: the matched rows of 64 * KMS_ZB rows, (offset << 4) | centroid
+    __shared__ int klist[KMS_WAVES][64 * KMS_ZB];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = blockIdx.x / ntiles, tile = blockIdx.x - g * ntiles;
     const int kp = ntiles * 16, c0 = tile * 16;
     double* my = kacc[wave];
+    int* lst = klist[wave];
     for (int i = lane; i < 16 * KS; i += 64) my[i] = 0.0;
     if (lane < 16) kcnt[wave][lane] = 0;
     constexpr int DPH = DP / 2;
@@ -828,7 +833,6 @@ void k_km_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
     const int64_t wa = per * wave < span ? per * wave : span;
     const int64_t wb = per * (wave + 1) < span ? per * (wave + 1) : span;
     const int64_t w0 = r0 + wa, w1 = r0 + wb;
-    // the assignments of KMS_ZB chunks of 64 rows are loaded at once
     for (int64_t rz = w0; rz < w1; rz += 64 * KMS_ZB) {
         int zc[KMS_ZB];
 #pragma unroll
@@ -836,39 +840,43 @@ void k_km_stats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
             const int64_t r = rz + 64 * u + lane;
             zc[u] = (r < w1 ? z[r] : -1) - c0;
         }
+        // list the matched rows in row order (chunk u, then lane)
+        int nl = 0;  // uniform
 #pragma unroll
         for (int u = 0; u < KMS_ZB; ++u) {
-            const int64_t rb = rz + 64 * u;
-            uint64_t mask = __builtin_amdgcn_ballot_w64((unsigned)zc[u] < 16u);
-            while (mask) {
-                int cb[KMS_BATCH];
-                float xa[KMS_BATCH], xb[KMS_BATCH];
-                int nb = 0;
+            const bool hit = (unsigned)zc[u] < 16u;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+            const int pos = nl + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (hit) lst[pos] = ((64 * u + lane) << 4) | zc[u];
+            nl += __builtin_popcountll(m);
+        }
+        __builtin_amdgcn_wave_barrier();
+        for (int b0 = 0; b0 < nl; b0 += KMS_BATCH) {
+            int cb[KMS_BATCH];
+            float xa[KMS_BATCH], xb[KMS_BATCH];
 #pragma unroll
-                for (int i = 0; i < KMS_BATCH; ++i) {
-                    // past the last selected row: row rb again (its values
-                    // are loaded but not added)
-                    const bool v = mask != 0;  // uniform
-                    const int b = v ? __builtin_ctzll(mask) : 0;
-                    mask = v ? mask & (mask - 1) : mask;
-                    nb += v ? 1 : 0;
-                    cb[i] = __builtin_amdgcn_readlane(zc[u], b);
-                    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-                        (void*)(x + (rb + b) * ldx), (short)0, rbytes, BUF_RSRC_WORD3);
-                    xa[i] = buf_load_x<XT>(xr, oA);
-                    xb[i] = buf_load_x<XT>(xr, oB);
-                }
+            for (int i = 0; i < KMS_BATCH; ++i) {
+                // past the list's end: its first entry of the batch again
+                // (loaded but not added)
+                const int e = __builtin_amdgcn_readfirstlane(lst[b0 + i < nl ? b0 + i : b0]);
+                cb[i] = e & 15;
+                const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(x + (rz + (e >> 4)) * ldx), (short)0, rbytes, BUF_RSRC_WORD3);
+                xa[i] = buf_load_x<XT>(xr, oA);
+                xb[i] = buf_load_x<XT>(xr, oB);
+            }
 #pragma unroll
-                for (int i = 0; i < KMS_BATCH; ++i) {
-                    if (i < nb) {
-                        double* ar = my + cb[i] * KS;
-                        ar[dA] += (double)xa[i] - sA;
-                        ar[dB] += (double)xb[i] - sB;
-                        if (lane == 0) kcnt[wave][cb[i]] += 1;
-                    }
+            for (int i = 0; i < KMS_BATCH; ++i) {
+                if (b0 + i < nl) {
+                    double* ar = my + cb[i] * KS;
+                    ar[dA] += (double)xa[i] - sA;
+                    ar[dB] += (double)xb[i] - sB;
+                    if (lane == 0) kcnt[wave][cb[i]] += 1;
                 }
             }
         }
+        __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
     for (int i = tid; i < 16 * KS; i += KMS_WAVES * 64) {
