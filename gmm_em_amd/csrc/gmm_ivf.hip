@@ -15,8 +15,9 @@
 //                     tiles (in place) and its total;
 //   3. k_ivf_offsets: exclusive prefix of the totals -> list offsets;
 //   4. k_ivf_scatter: per tile, one wave walks its entries in order, 64 at a
-//                     time; lanes holding the same list id are ranked by lane
-//                     order with a ballot, so each row lands at
+//                     time; each lane finds the lanes holding its list id
+//                     with one ballot per id bit and is ranked among them by
+//                     lane order, so each row lands at
 //                     offset[list] + (kept entries of that list before it).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -82,14 +83,39 @@ __global__ __launch_bounds__(256) void k_ivf_hist(const int32_t* __restrict__ id
     for (int c = threadIdx.x; c < k; c += blockDim.x) row[c] = h[c];
 }
 
-__global__ __launch_bounds__(256) void k_ivf_colscan(int32_t* __restrict__ mat, int64_t ntiles,
-                                                     int k, int32_t* __restrict__ count) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+// 64 lists per block, their tiles split into 16 segments (one wave each):
+// each wave sums its segment, then rewrites it as exclusive prefixes from
+// the sum of the segments before it.
+constexpr int IVF_SEGS = 16;
+__global__ __launch_bounds__(64 * IVF_SEGS) void k_ivf_colscan(int32_t* __restrict__ mat,
+                                                              int64_t ntiles, int k,
+                                                              int32_t* __restrict__ count) {
+    __shared__ int32_t seg[IVF_SEGS][64];
+    const int col = threadIdx.x & 63, sg = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + col;
+    const int64_t per = (ntiles + IVF_SEGS - 1) / IVF_SEGS;
+    const int64_t t0 = (int64_t)sg * per < ntiles ? (int64_t)sg * per : ntiles;
+    const int64_t t1 = t0 + per < ntiles ? t0 + per : ntiles;
+    int32_t sum = 0;
+    if (c < k) {
+        int64_t t = t0;
+        // eight tiles' counts in flight at a time
+        for (; t + 8 <= t1; t += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = mat[(t + u) * k + c];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        for (; t < t1; ++t) sum += mat[t * k + c];
+    }
+    seg[sg][col] = sum;
+    __syncthreads();
     if (c >= k) return;
     int32_t run = 0;
-    int64_t t = 0;
-    // eight tiles' counts in flight at a time
-    for (; t + 8 <= ntiles; t += 8) {
+    for (int q = 0; q < sg; ++q) run += seg[q][col];
+    int64_t t = t0;
+    for (; t + 8 <= t1; t += 8) {
         int32_t v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = mat[(t + u) * k + c];
@@ -99,15 +125,14 @@ __global__ __launch_bounds__(256) void k_ivf_colscan(int32_t* __restrict__ mat, 
             run += v[u];
         }
     }
-    for (; t < ntiles; ++t) {
+    for (; t < t1; ++t) {
         const int32_t v = mat[t * k + c];
         mat[t * k + c] = run;
         run += v;
     }
-    count[c] = run;
+    if (sg == IVF_SEGS - 1) count[c] = run;
 }
 
-// One workgroup of 1024 threads; thread i sums a contiguous run of lists.
 __global__ __launch_bounds__(1024) void k_ivf_offsets(const int32_t* __restrict__ count, int k,
                                                       int64_t* __restrict__ offsets) {
     __shared__ int64_t part[1024];
@@ -148,29 +173,45 @@ __global__ __launch_bounds__(64) void k_ivf_scatter(const int32_t* __restrict__ 
     for (int c = lane; c < k; c += 64) base[c] = row[c];
     __syncthreads();
     const uint64_t below = (uint64_t(1) << lane) - 1;  // lanes before this one
+    const int nbits = k > 1 ? 32 - __builtin_clz((unsigned)(k - 1)) : 0;  // bits of a list id
     const int64_t e0 = (int64_t)blockIdx.x * tile;
     const int64_t e1 = e0 + tile < entries ? e0 + tile : entries;
-    for (int64_t eb = e0; eb < e1; eb += 64) {
-        const int64_t e = eb + lane;
-        int32_t c = -1;
-        const bool keep = e < e1 && ivf_keep(idx, resp, e, m, k, min_resp, &c);
-        uint64_t active = __builtin_amdgcn_ballot_w64(keep);
-        // each round places every lane of one list id (at most 64 rounds)
-        while (active) {
-            const int lead = __builtin_ctzll(active);
-            const int32_t c0 = __builtin_amdgcn_readlane(c, lead);
-            const bool mine = keep && c == c0;
-            const uint64_t same = __builtin_amdgcn_ballot_w64(mine);
-            const int32_t b = base[c0];
-            if (mine) {
-                const int64_t pos = offsets[c0] + b + __popcll(same & below);
-                rows_out[pos] = (int32_t)(e / m);
-                if (vals_out) vals_out[pos] = resp ? resp[e] : 1.0f;
+    constexpr int U = 4;  // 64-entry chunks whose ids and values are loaded at once
+    for (int64_t eb = e0; eb < e1; eb += 64 * U) {
+        int32_t cu[U];
+        float ru[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = eb + 64 * u + lane;
+            cu[u] = e < e1 ? idx[e] : -1;
+            ru[u] = (resp && e < e1) ? resp[e] : 1.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = eb + 64 * u + lane;
+            const int32_t c = cu[u];
+            // the rule of ivf_keep: a valid list id, and the row's first
+            // entry or a responsibility at or above the threshold
+            const bool keep = e < e1 && c >= 0 && c < k &&
+                              (e % m == 0 || !resp || ru[u] >= min_resp);
+            // the kept lanes whose list id equals this lane's, one id bit at
+            // a time (meaningful for kept lanes only)
+            uint64_t same = __builtin_amdgcn_ballot_w64(keep);
+            for (int bit = 0; bit < nbits; ++bit) {
+                const bool set = ((c >> bit) & 1) != 0;
+                const uint64_t v = __builtin_amdgcn_ballot_w64(keep && set);
+                same &= set ? v : ~v;
             }
-            // (one wave: its LDS accesses complete in program order, so every
-            // lane's read of base[c0] above precedes this update)
-            if (lane == lead) base[c0] = b + __popcll(same);
-            active &= ~same;
+            if (keep) {
+                const int32_t b = base[c];
+                const int64_t pos = offsets[c] + b + __popcll(same & below);
+                rows_out[pos] = (int32_t)(e / m);
+                if (vals_out) vals_out[pos] = ru[u];
+                // the first lane of each id advances its counter (one wave:
+                // its LDS accesses complete in program order, so every
+                // lane's read of base[c] above precedes this update)
+                if ((same & below) == 0) base[c] = b + __popcll(same);
+            }
         }
     }
 }
@@ -204,8 +245,8 @@ int gmm_ivf_build(const int32_t* idx_dev, const float* resp_dev, int64_t n, int3
         hipLaunchKernelGGL(k_ivf_hist, dim3((unsigned)p.ntiles), dim3(256), lds, st, idx_dev,
                            resp_dev, p.entries, m, k, min_resp, p.tile, mat);
     }
-    hipLaunchKernelGGL(k_ivf_colscan, dim3((k + 255) / 256), dim3(256), 0, st, mat, p.ntiles, k,
-                       count);
+    hipLaunchKernelGGL(k_ivf_colscan, dim3((k + 63) / 64), dim3(64 * IVF_SEGS), 0, st, mat,
+                       p.ntiles, k, count);
     hipLaunchKernelGGL(k_ivf_offsets, dim3(1), dim3(1024), 0, st, count, k, offsets_dev);
     if (p.ntiles > 0) {
         hipLaunchKernelGGL(k_ivf_scatter, dim3((unsigned)p.ntiles), dim3(64), lds, st, idx_dev,
