@@ -56,6 +56,8 @@ def _synthetic(n, m, k, seed, bad=0.01):
     (5001, 3, 300, 0.1, 4),      # several tiles with a ragged tail
     (70_000, 4, 1024, 0.05, 5),  # many tiles, headline list count
     (9000, 2, 16384, 0.0, 6),    # the largest list count
+    (4000, 2, 2, 0.0, 9),        # two lists: a chunk's lanes share an id, ranks up to 63
+    (3000, 3, 1025, 0.0, 10),    # one list past a power of two (11 id bits)
 ])
 def test_ivf_synthetic(ops, n, m, k, tau, seed):
     idx, resp = _synthetic(n, m, k, seed)
