@@ -14,7 +14,9 @@
 // * Rows are processed in 16-row tiles. The tile's shifted values a = x - s
 //   are staged once in LDS in fp64, natural dim order (a^2 is formed by one
 //   multiply where an operand needs it: 16 rows of both powers would not
-//   fit in LDS).
+//   fit in LDS). The statistics pass for fp32 rows (k_wstats_p) instead
+//   keeps three fp32 tiles in LDS and forms a where it is read, so that its
+//   two wave roles can work on consecutive tiles at once.
 // * Each wave contracts its slice; the partial log-densities are summed
 //   through LDS in a fixed order, so every wave sees the same l.
 // * Normaliser pass: per (row, K-tile) a (max, scaled sum) partial and the
