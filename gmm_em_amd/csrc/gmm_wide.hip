@@ -30,6 +30,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gmm_device.h"
 #include "gmm_internal.h"
 
@@ -534,7 +536,9 @@ void k_wstats(const XT* __restrict__ x, int64_t n, int d, int64_t ldx,
 // l of tile p; after B the M waves read them at the start of phase p + 1.
 // Every wave runs the same ntr + 1 phases.
 // ---------------------------------------------------------------------------
-template <int DS>
+// ZS: every shift is 0, so a = x (x - 0.0 is x exactly, -0 included) and
+// neither the shifts nor the subtraction are needed.
+template <int DS, bool ZS = false>
 __device__ __forceinline__ f64x4 wide_estep_raw(const float* px, const double* psh,
                                                 const double (&pr)[DS / 2]) {
     constexpr int T1 = DS / 4, EB = 4;
@@ -545,7 +549,7 @@ __device__ __forceinline__ f64x4 wide_estep_raw(const float* px, const double* p
 #pragma unroll
     for (int u = 0; u < EB; ++u) {
         rx[0][u] = px[4 * u];
-        rs[0][u] = psh[4 * u];
+        rs[0][u] = ZS ? 0.0 : psh[4 * u];
     }
 #pragma unroll
     for (int bt = 0; bt < T1 / EB; ++bt) {
@@ -554,13 +558,13 @@ __device__ __forceinline__ f64x4 wide_estep_raw(const float* px, const double* p
 #pragma unroll
             for (int u = 0; u < EB; ++u) {
                 rx[cur ^ 1][u] = px[4 * ((bt + 1) * EB + u)];
-                rs[cur ^ 1][u] = psh[4 * ((bt + 1) * EB + u)];
+                rs[cur ^ 1][u] = ZS ? 0.0 : psh[4 * ((bt + 1) * EB + u)];
             }
         }
 #pragma unroll
         for (int u = 0; u < EB; ++u) {
             const int j = bt * EB + u;
-            const double v = (double)rx[cur][u] - rs[cur][u];
+            const double v = ZS ? (double)rx[cur][u] : (double)rx[cur][u] - rs[cur][u];
             e = mfma4d(v, pr[2 * j], e);
             e = mfma4d(v * v, pr[2 * j + 1], e);
         }
@@ -629,8 +633,13 @@ void k_wstats_p(const float* __restrict__ x, int64_t n, int d, int64_t ldx,
         if (tid < WROWS) ls[0][tid] = load_ls(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
+    // every shift 0 (uniform over the block): the roles skip the subtraction;
+    // the vote is also the barrier after the first copies
+    bool zl = true;
+    for (int i = tid; i < DP; i += NT) zl = zl && shl[i] == 0.0;
+    const bool zs = __syncthreads_and(zl) != 0;
+    auto roles = [&](auto zsc) {
+    constexpr bool ZS = decltype(zsc)::value;
     if (w < NS) {
         // E role
         double pr[DS / 2];
@@ -643,7 +652,7 @@ void k_wstats_p(const float* __restrict__ x, int64_t n, int d, int64_t ldx,
                 if (tid < WROWS) lsn = load_ls(p + 1);
             }
             f64x4 e = {0.0, 0.0, 0.0, 0.0};
-            if (p < ntr) e = wide_estep_raw<DS>(xr[(int)(p % NB)] + ci * RSF + s * DS + h, psh, pr);
+            if (p < ntr) e = wide_estep_raw<DS, ZS>(xr[(int)(p % NB)] + ci * RSF + s * DS + h, psh, pr);
             if (p + 1 < ntr && tid < WROWS) ls[(int)((p + 1) % NB)][tid] = lsn;
             __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile p + 1 have landed
             __syncthreads();                // A
@@ -686,18 +695,19 @@ void k_wstats_p(const float* __restrict__ x, int64_t n, int d, int64_t ldx,
                     double sv[2];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) xv[0][q] = pm[4 * q * RSF];
-                    sv[0] = psm[0];
+                    sv[0] = ZS ? 0.0 : psm[0];
 #pragma unroll
                     for (int J = 0; J < NJ; ++J) {
                         const int cur = J & 1;
                         if (J + 1 < NJ) {
 #pragma unroll
                             for (int q = 0; q < 4; ++q) xv[cur ^ 1][q] = pm[4 * q * RSF + 16 * (J + 1)];
-                            sv[cur ^ 1] = psm[16 * (J + 1)];
+                            sv[cur ^ 1] = ZS ? 0.0 : psm[16 * (J + 1)];
                         }
                         double av[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) av[q] = (double)xv[cur][q] - sv[cur];
+                        for (int q = 0; q < 4; ++q)
+                            av[q] = ZS ? (double)xv[cur][q] : (double)xv[cur][q] - sv[cur];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) acc[J] = mfma4d(r[q], av[q], acc[J]);
 #pragma unroll
@@ -731,6 +741,9 @@ void k_wstats_p(const float* __restrict__ x, int64_t n, int d, int64_t ldx,
                 *pp = (accumulate ? *pp : 0.0) + acc[J][q];
             }
     }
+    };
+    if (zs) roles(std::true_type{});
+    else roles(std::false_type{});
 }
 
 // Merge of the normaliser partials of each row over its K-tiles (fixed
